@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized lightning indexer on one MI355X.
+
+One step = one full indexer call (every kernel of the op) on the decode
+candidate-source workload: 64 requests x 1 query token, 32768 compressed
+positions each (ratio 1, 128-row pages at a 147712-byte stride, shuffled
+block table), 64 index heads, position top-k 2048, 512 candidate blocks.
+Inputs are resident in HBM before timing starts; four copies of the paged
+cache are rotated so that no step re-reads the previous step's K from the
+256 MB last-level cache.
+
+Prints one JSON line: compressed keys scored per second, the dominant
+kernel against its roofline (algorithmic bytes per launch over its average
+duration, measured with HIP events on the launch stream), and the oracle
+timed on the host cores on a bounded sample.  Secondary workloads (the
+8192-token prefill chunk against the INT8 MFMA peak, the 1M-context
+consumer against HBM) are reported under "other_workloads".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, published (5.0 POP/s)
+KEY_BYTES = 130                # one 128-byte index-K row + its 2-byte FP16 scale
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic(pb, cand_in=None):
+    """Keys scored, algorithmic HBM bytes and INT8 ops of one call:
+    each request's eligible K rows (+scale) once, queries/scales/weights,
+    block-table entries needed, metadata, incoming candidates and outputs;
+    ops = eligible (token, position) pairs x heads x 2 x 128."""
+    import numpy as np
+    cand = cand_in if cand_in is not None else pb.cand_in
+    T, N = pb.num_tokens, pb.num_heads
+    keys = 0
+    rows = 0
+    pages = 0
+    qsl = pb.query_start_loc
+    for b in range(pb.batch):
+        q0, q1 = int(qsl[b]), int(qsl[b + 1])
+        if q1 == q0:
+            continue
+        n, S = q1 - q0, int(pb.raw_lens[b])
+        vis = (S - n + np.arange(n) + 1) // pb.ratio
+        if pb.mode == 3:
+            union = set()
+            for i, t in enumerate(range(q0, q1)):
+                nb = -(-int(vis[i]) // 8)
+                c = np.unique(cand[t, 0])
+                c = c[(c >= 0) & (c < nb)].astype(np.int64)
+                e = np.minimum(8, vis[i] - 8 * c)
+                keys += int(e.sum())
+                union |= set(c.tolist())
+            touched = sorted(union)
+            rows += sum(min(8, int(vis.max()) - 8 * c) for c in touched)
+            pages += len({(8 * c) // pb.page_rows for c in touched})
+        else:
+            keys += int(vis.sum())
+            rows += int(vis.max())
+            pages += -(-int(vis.max()) // pb.page_rows)
+    nbytes = rows * KEY_BYTES + T * N * (128 + 2 + 2) + pages * 4 + (pb.batch * 3 + 1) * 4
+    nbytes += T * pb.topk * 4
+    if pb.mode == 2:
+        nbytes += T * pb.cand_blocks * 4
+    if pb.mode == 3:
+        nbytes += T * pb.cand_in_blocks * 4
+    ops = keys * N * 256
+    return keys, nbytes, ops
+
+
+class Runner:
+    """Device inputs (several rotated copies), outputs and workspace of one
+    workload, plus prepared qli_params per copy."""
+
+    def __init__(self, pb, copies=1, cand_sets=None):
+        import torch
+
+        import quantized_top_indexer_amd as Q
+        from qli_workloads.device import to_device
+        self.pb = pb
+        self.Q = Q
+        dev0 = to_device(pb, "cuda", cand_in=cand_sets[0] if cand_sets else None)
+        self.devs = [dev0]
+        for c in range(1, copies):
+            d = dict(dev0)
+            if cand_sets:
+                d["cand_in"] = torch.from_numpy(cand_sets[c]).to("cuda")
+            else:
+                from qli_workloads.device import device_pool
+                d["pool"], d["k_cache"], d["k_scale"] = device_pool(pb, "cuda")
+            self.devs.append(d)
+        T = pb.num_tokens
+        shp_i, shp_c = Q.output_shapes(T, pb.topk, pb.cand_blocks, pb.mode)
+        self.topk_out = torch.empty(shp_i, dtype=torch.int32, device="cuda")
+        self.cand_out = torch.empty(shp_c, dtype=torch.int32, device="cuda") if shp_c else None
+        self.params = []
+        for d in self.devs:
+            p = Q.make_params(q=d["q"], q_scale=d["q_scale"], weights=d["weights"],
+                              k_cache=d["k_cache"], k_scale=d["k_scale"],
+                              block_table=d["block_table"], query_start_loc=d["query_start_loc"],
+                              k_lens=d["k_lens"], seq_mod=d["seq_mod"], cand_in=d["cand_in"],
+                              ratio=pb.ratio, mode=pb.mode, topk=pb.topk,
+                              cand_blocks=pb.cand_blocks, max_k_len=pb.max_k_len,
+                              topk_out=self.topk_out, cand_out=self.cand_out)
+            self.params.append(p)
+        need = Q.qli_workspace_bytes(self.params[0])
+        self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        for p in self.params:
+            p.workspace, p.workspace_bytes = self.ws.data_ptr(), self.ws.numel()
+        self.stream = torch.cuda.current_stream().cuda_stream
+
+    def step(self, i):
+        rc = self.Q.qli_score_topk(self.params[i % len(self.params)], self.stream)
+        if rc != self.Q.QLI_OK:
+            raise RuntimeError(self.Q.qli_status_string(rc))
+
+    def timed(self, steps, warmup):
+        import torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(steps):
+            self.step(i)
+        stop.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return start.elapsed_time(stop) / steps, wall
+
+    def kernel_ms(self, steps):
+        """Average duration per launch of each kernel (HIP events recorded by
+        the library around each launch, on the launch stream)."""
+        Q = self.Q
+        Q.qli_timing_read(reset=True)
+        Q.qli_timing_enable(True)
+        try:
+            for i in range(steps):
+                self.step(i)
+            ms, cnt = Q.qli_timing_read(reset=True)
+        finally:
+            Q.qli_timing_enable(False)
+        return {Q.KERNEL_NAMES[k]: ms[k] / cnt[k] for k in range(len(ms)) if cnt[k]}
+
+
+def measure(pb, steps, warmup, copies=1, cand_sets=None, bound="hbm"):
+    run = Runner(pb, copies=copies, cand_sets=cand_sets)
+    ms, wall = run.timed(steps, warmup)
+    kms = run.kernel_ms(steps)
+    keys, nbytes, ops = algorithmic(pb, cand_sets[0] if cand_sets else None)
+    kern = max(kms, key=kms.get)
+    kt = kms[kern] * 1e-3
+    if bound == "hbm":
+        achieved = nbytes / kt / 1e9
+        roof = {"bound": "hbm", "kernel": kern, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None, "alg_bytes_per_launch": nbytes,
+                "kernel_ms": round(kms[kern], 5)}
+    else:
+        achieved = ops / kt / 1e12
+        roof = {"bound": "mfma", "kernel": kern, "achieved": round(achieved, 1),
+                "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": None,
+                "alg_ops_per_launch": ops, "kernel_ms": round(kms[kern], 5)}
+    del run
+    import torch
+    torch.cuda.empty_cache()
+    return {"keys": keys, "ms_per_step": ms, "wall_s": wall, "kernels_ms": kms, "roofline": roof,
+            "keys_per_s": keys / (ms * 1e-3)}
+
+
+def cpu_baseline(pb, budget_tokens=None):
+    """The oracle as it stands, on the host cores, on a bounded sample of the
+    workload's tokens."""
+    import numpy as np
+
+    import oracle
+    nthreads = max(1, min(16, os.cpu_count() or 1))
+    toks = np.arange(pb.num_tokens if budget_tokens is None else min(budget_tokens,
+                                                                     pb.num_tokens))
+    o = oracle.OracleProblem(pb)
+    t0 = time.perf_counter()
+    o.run(tokens=toks, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    vis = []
+    for b in range(pb.batch):
+        n = int(pb.query_start_loc[b + 1] - pb.query_start_loc[b])
+        vis += [(int(pb.raw_lens[b]) - n + i + 1) // pb.ratio for i in range(n)]
+    assert pb.mode != 3, "the CPU baseline runs on a source or plain workload"
+    keys = int(sum(vis[int(t)] for t in toks))
+    return {"value": round(keys / dt, 1), "unit": "keys/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{len(toks)} of {pb.num_tokens} query tokens of {pb.name} "
+                      f"({keys} keys, {dt:.2f} s wall on {nthreads} threads)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--others", default="prefill_chunk,decode_consumer_1m",
+                    help="comma list of secondary workloads ('' for none)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the indexer has no multi-GPU path in this build "
+              "(requests or positions would shard with no exchange / one top-k merge; "
+              "see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import qli_workloads as W
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import quantized_top_indexer_amd as Q
+    Q.load_library()
+
+    log("decode_source: generating")
+    pb = W.decode_source()
+    main_m = measure(pb, args.steps, args.warmup, copies=args.copies, bound="hbm")
+    log(f"decode_source: {main_m['ms_per_step']:.4f} ms/step kernels {main_m['kernels_ms']}")
+
+    others = {}
+    for name in [s for s in args.others.split(",") if s]:
+        log(f"{name}: generating")
+        opb = W.WORKLOADS[name]()
+        if name == "decode_consumer_1m":
+            import numpy as np
+            from qli_workloads import make_candidates, visible_counts, Requests
+            vis = visible_counts(Requests(n=np.ones(opb.batch, np.int64), S=opb.raw_lens),
+                                 opb.ratio)
+            sets = [opb.cand_in] + [make_candidates(opb.seed + 100 * c, 1, vis, 2048)
+                                    for c in range(1, 8)]
+            m = measure(opb, args.steps, args.warmup, cand_sets=sets, copies=8, bound="hbm")
+        else:
+            m = measure(opb, max(10, args.steps // 5), args.warmup, bound="mfma")
+        others[name] = {"keys_per_s": round(m["keys_per_s"], 1),
+                        "ms_per_call": round(m["ms_per_step"], 5), "kernels_ms": m["kernels_ms"],
+                        "roofline": m["roofline"]}
+        log(f"{name}: {m['ms_per_step']:.4f} ms/call kernels {m['kernels_ms']}")
+        del opb
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on the host")
+        cpu = cpu_baseline(pb)
+
+    line = {
+        "metric": "compressed keys scored/s",
+        "value": round(main_m["keys_per_s"], 1),
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_m["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": "decode_source", "requests": 64, "query_tokens": 64,
+                   "compressed_len": 32768, "ratio": 1, "heads": 64, "head_dim": 128,
+                   "topk": 2048, "cand_blocks": 512, "page_rows": 128,
+                   "page_stride_bytes": 147712, "rotated_cache_copies": args.copies,
+                   "parallelism": "single GPU"},
+        "roofline": main_m["roofline"],
+        "cpu_baseline": cpu,
+        "kernels_ms": main_m["kernels_ms"],
+        "other_workloads": others,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,200 @@
+/*
+ * qli.h - C ABI of the MI355X (gfx950) quantized lightning indexer (QLI)
+ * with hierarchical candidate blocks.
+ *
+ * What one call computes (DeepSeek V4.1 QLI developer guide, "数据流" and
+ * "当前 A3 契约" sections):
+ *
+ *   For every query token t of a TND batch and every compressed position j
+ *   of its request that t may see (causal mask mode 3) and that is eligible:
+ *     qk   = sum_d q[t,h,d] * k[j,d]                 (exact INT32)
+ *     x    = fp16(qk / 1024); x = max(x, +0)        (FP16 ReLU)
+ *     m    = fp16(weights[t,h] * q_scale[t,h])       (FP16)
+ *     p    = fp16(x * m)                             (FP16)
+ *     sum  = p_0 + p_1 + ... + p_{N-1}               (FP32, from +0, ascending h)
+ *     score[t,j] = fp32(sum * k_scale[j])            (FP32 K scaling)
+ *   Every rounding is IEEE round-to-nearest-even; FP16 subnormals are kept.
+ *   The head-sum order is fixed (ascending head), so scores are exactly
+ *   reproducible, not merely within a tolerance.
+ *
+ *   Visibility: the queries of request b are its last n_b raw positions;
+ *   the query at raw position p sees compressed entries j < floor((p+1)/r),
+ *   where the raw length is S_b = k_lens[b] * r + seq_mod[b].
+ *
+ *   Outputs (ties: higher score first, then lower position / block id):
+ *     topk_out[t, 0, :]  the top min(topk, |E_t|) eligible positions in
+ *                        ascending (chronological) order, -1 padding at
+ *                        the tail;
+ *     cand_out[t, 0, :]  (source mode) candidate block ids: a block is 8
+ *                        consecutive compressed positions [8c, 8c+8), its
+ *                        score the maximum visible position score; the
+ *                        last visible block ceil(V/8)-1 is always kept and
+ *                        the best cand_blocks-1 other visible blocks join
+ *                        it; ascending ids, -1 tail.  An empty compressed
+ *                        context gives all -1.
+ *   Modes (runtime parameter, one operator):
+ *     QLI_MODE_PLAIN    positions over the whole visible context;
+ *     QLI_MODE_SOURCE   positions over the whole visible context, plus the
+ *                       candidate blocks;
+ *     QLI_MODE_CONSUMER positions restricted to the incoming candidate
+ *                       blocks cand_in[t, 0, :] (negative ids ignored,
+ *                       duplicates collapse, ids past the visible range add
+ *                       nothing).  A consumer without candidates is an
+ *                       error (QLI_ERR_NO_SOURCE).
+ *
+ * Memory: every pointer in qli_params is DEVICE memory owned by the caller
+ * (typically torch tensors); the library allocates nothing.  Integer
+ * metadata is read on the device only, so a call never synchronises with
+ * the host.
+ */
+#ifndef QLI_H
+#define QLI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QLI_ABI_VERSION 1
+
+/* Status codes returned by the host entry points. */
+enum qli_status {
+  QLI_OK = 0,
+  QLI_ERR_INVALID_ARG = 1, /* null pointer, value out of range, bad stride or
+                              alignment, residual present at ratio 1 or
+                              missing at ratio 2, page_rows != 128/ratio */
+  QLI_ERR_UNSUPPORTED = 2, /* num_heads not 32/64, head_dim not 128, quant
+                              mode not INT8, sizes past the documented caps */
+  QLI_ERR_NO_SOURCE = 3,   /* consumer mode without incoming candidates */
+  QLI_ERR_WORKSPACE = 4,   /* workspace missing or smaller than
+                              qli_workspace_bytes() */
+  QLI_ERR_HIP = 5          /* a kernel launch failed */
+};
+
+/* Candidate modes ("三种候选模式共享同一个原生算子": three modes, one op). */
+enum qli_mode { QLI_MODE_PLAIN = 1, QLI_MODE_SOURCE = 2, QLI_MODE_CONSUMER = 3 };
+
+/* INT8 is quantisation mode 2 in the guide's numbering ("量化模式 2"). */
+#define QLI_QUANT_INT8 2
+
+/* Bits the kernels OR into *status_out when a device-side metadata value is
+ * out of contract.  The affected positions are treated as not eligible, so
+ * every memory access stays inside the buffers described here. */
+#define QLI_DEV_BAD_PAGE 1u     /* block-table entry < 0 or >= num_pages, or a
+                                   page index past bt_stride */
+#define QLI_DEV_BAD_LENGTH 2u   /* k_lens[b] < 0 or > max_k_len */
+#define QLI_DEV_BAD_METADATA 4u /* seq_mod outside [0, ratio), or a request
+                                   with more queries than raw tokens */
+
+/* Documented caps (QLI_ERR_UNSUPPORTED beyond them). */
+#define QLI_MAX_TOPK 2048
+#define QLI_MAX_CAND_BLOCKS 2048
+#define QLI_MAX_K_LEN (1 << 24)
+
+typedef struct qli_params {
+  uint32_t struct_size; /* = sizeof(qli_params) */
+  int32_t mode;         /* enum qli_mode */
+  int32_t ratio;        /* compress ratio r: 1 or 2 */
+  int32_t num_heads;    /* N index heads: 32 or 64 */
+  int32_t head_dim;     /* must be 128 */
+  int32_t quant_mode;   /* must be QLI_QUANT_INT8 */
+  int32_t batch;        /* B requests */
+  int32_t num_tokens;   /* T query tokens (TND rows) */
+  int32_t topk;         /* position top-k, 1..2048 */
+  int32_t cand_blocks;  /* source mode: output candidate width, a multiple
+                           of 64 in [64, 2048]; ignored otherwise */
+  int32_t cand_in_blocks; /* consumer mode: incoming candidate width, a
+                             multiple of 64 in [64, 2048]; ignored otherwise */
+  int32_t page_rows;    /* rows per page view: 128 / ratio */
+  int32_t bt_stride;    /* entries per block-table row (>= 1) */
+  int32_t num_pages;    /* pages addressable through k_cache / k_scale */
+  int32_t max_k_len;    /* host-side upper bound of k_lens[] (sizes the
+                           grid and the workspace without a sync) */
+  int32_t reserved0;    /* must be 0 */
+  int64_t k_page_stride; /* bytes between page p and p+1 of the K view;
+                            multiple of 16, >= page_rows * 128 */
+  int64_t s_page_stride; /* bytes between page p and p+1 of the scale
+                            view; even, >= page_rows * 2 */
+
+  /* inputs (device) */
+  const int8_t* q;          /* [T, N, 128] int8, contiguous TND, 16-B aligned */
+  const uint16_t* q_scale;  /* [T, N] fp16 bits, per token and head */
+  const uint16_t* weights;  /* [T, N] fp16 bits, head weights */
+  const int8_t* k_cache;    /* row 0 of page 0 of the index-K view: row j of
+                               page p at k_cache + p*k_page_stride + j*128;
+                               16-B aligned */
+  const void* k_scale;      /* row 0 of page 0 of the fp16 scale view: row j
+                               of page p at (char*)k_scale + p*s_page_stride
+                               + j*2; 2-B aligned */
+  const int32_t* block_table;     /* [B, bt_stride] page ids: compressed
+                                     position j of request b lives in page
+                                     block_table[b][j / page_rows], row
+                                     j % page_rows */
+  const int32_t* query_start_loc; /* [B+1] raw query boundaries in TND
+                                     order; [0] = 0, non-decreasing,
+                                     [B] = T */
+  const int32_t* k_lens;          /* [B] compressed K lengths */
+  const int32_t* seq_mod;         /* [B] raw length mod ratio; must be NULL
+                                     at ratio 1 and non-NULL at ratio 2 */
+  const int32_t* cand_in;         /* consumer: [T, 1, cand_in_blocks] block
+                                     ids, -1 padded */
+
+  /* outputs (device) */
+  int32_t* topk_out;    /* [T, 1, topk] */
+  int32_t* cand_out;    /* source: [T, 1, cand_blocks]; else may be NULL */
+  float* dbg_scores;    /* optional (NULL in production): [T, max_k_len]
+                           FP32 scores by position, written only where a
+                           position is eligible */
+  uint32_t* status_out; /* optional device word receiving QLI_DEV_* bits
+                           (never cleared by the library) */
+
+  /* scratch (device), caller-allocated, >= qli_workspace_bytes(p) bytes,
+     256-B aligned */
+  void* workspace;
+  size_t workspace_bytes;
+} qli_params;
+
+/* ABI version of the loaded library (QLI_ABI_VERSION at build time). */
+int qli_abi_version(void);
+
+/* Host-only argument check, exactly the one qli_score_topk() performs
+ * before launching anything.  Reads no device memory. Returns a qli_status. */
+int qli_validate(const qli_params* p);
+
+/* Workspace bytes a call with these scalars needs (host-only; depends on
+ * mode, ratio, num_tokens, max_k_len and cand_in_blocks).  0 when p is NULL
+ * or when the scalars are invalid. */
+size_t qli_workspace_bytes(const qli_params* p);
+
+/* Enqueue the whole indexer on `stream` (a hipStream_t; NULL = the null
+ * stream) and return at once: no host-device synchronisation, no
+ * allocation.  Validation runs before any launch; num_tokens == 0 is a
+ * valid no-op.  Kernel faults surface at the caller's next synchronisation.
+ * Re-entrant for calls with distinct workspaces and outputs; calls that
+ * share a workspace must be ordered on one stream. Returns a qli_status. */
+int qli_score_topk(const qli_params* p, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* qli_status_string(int status);
+
+/* Kernels of one call, in launch order (for the timing facility below). */
+enum qli_kernel { QLI_KERNEL_CONSUMER_PREP = 0, QLI_KERNEL_SCORE = 1, QLI_KERNEL_SELECT = 2,
+                  QLI_NUM_KERNELS = 3 };
+
+/* Optional per-kernel timing (off by default; process-wide, not thread
+ * safe).  While enabled, every qli_score_topk() call records a HIP event
+ * before and after each kernel it launches, on the call's stream.
+ * qli_timing_read() waits for the recorded events, adds each kernel's
+ * elapsed milliseconds to ms[kernel] and its launch count to count[kernel]
+ * (arrays of QLI_NUM_KERNELS entries, accumulated since the last reset),
+ * and clears the totals when `reset` is non-zero.  Returns a qli_status. */
+int qli_timing_enable(int on);
+int qli_timing_read(double* ms, int64_t* count, int reset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLI_H */

@@ -1,0 +1,208 @@
+"""Python binding of the MI355X quantized lightning indexer (QLI) library.
+
+Thin ctypes layer over ``libqli.so`` (C ABI in ``include/qli.h``): it only
+marshals torch tensors into ``qli_params`` and calls the library; every step
+of the indexer runs in the HIP kernels.  There is no fallback: if the
+library is not built, importing the entry points raises.
+
+Entry points (same names as the C ABI): ``qli_score_topk``,
+``qli_workspace_bytes``, ``qli_validate``, ``qli_status_string``,
+``qli_abi_version``; plus ``score_topk``, a convenience wrapper that
+allocates the outputs and the workspace with torch and runs one call on the
+current stream, and ``output_shapes`` (shapes of a call's outputs).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqli.so")
+
+QLI_OK, QLI_ERR_INVALID_ARG, QLI_ERR_UNSUPPORTED, QLI_ERR_NO_SOURCE, QLI_ERR_WORKSPACE, \
+    QLI_ERR_HIP = range(6)
+QLI_MODE_PLAIN, QLI_MODE_SOURCE, QLI_MODE_CONSUMER = 1, 2, 3
+QLI_QUANT_INT8 = 2
+QLI_DEV_BAD_PAGE, QLI_DEV_BAD_LENGTH, QLI_DEV_BAD_METADATA = 1, 2, 4
+
+
+class qli_params(C.Structure):
+    """Mirror of ``struct qli_params`` in include/qli.h."""
+    _fields_ = [
+        ("struct_size", C.c_uint32), ("mode", C.c_int32), ("ratio", C.c_int32),
+        ("num_heads", C.c_int32), ("head_dim", C.c_int32), ("quant_mode", C.c_int32),
+        ("batch", C.c_int32), ("num_tokens", C.c_int32), ("topk", C.c_int32),
+        ("cand_blocks", C.c_int32), ("cand_in_blocks", C.c_int32), ("page_rows", C.c_int32),
+        ("bt_stride", C.c_int32), ("num_pages", C.c_int32), ("max_k_len", C.c_int32),
+        ("reserved0", C.c_int32),
+        ("k_page_stride", C.c_int64), ("s_page_stride", C.c_int64),
+        ("q", C.c_void_p), ("q_scale", C.c_void_p), ("weights", C.c_void_p),
+        ("k_cache", C.c_void_p), ("k_scale", C.c_void_p), ("block_table", C.c_void_p),
+        ("query_start_loc", C.c_void_p), ("k_lens", C.c_void_p), ("seq_mod", C.c_void_p),
+        ("cand_in", C.c_void_p),
+        ("topk_out", C.c_void_p), ("cand_out", C.c_void_p), ("dbg_scores", C.c_void_p),
+        ("status_out", C.c_void_p),
+        ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
+    ]
+
+
+EXPORTS = ("qli_abi_version", "qli_validate", "qli_workspace_bytes", "qli_score_topk",
+           "qli_status_string", "qli_timing_enable", "qli_timing_read")
+QLI_KERNEL_CONSUMER_PREP, QLI_KERNEL_SCORE, QLI_KERNEL_SELECT, QLI_NUM_KERNELS = 0, 1, 2, 3
+KERNEL_NAMES = ("consumer_prep_kernel", "score_kernel", "select_kernel")
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libqli.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"QLI HIP library not built ({path}); run __graft_entry__.build()")
+    L = C.CDLL(path)
+    L.qli_abi_version.restype = C.c_int
+    L.qli_validate.restype = C.c_int
+    L.qli_validate.argtypes = [C.POINTER(qli_params)]
+    L.qli_workspace_bytes.restype = C.c_size_t
+    L.qli_workspace_bytes.argtypes = [C.POINTER(qli_params)]
+    L.qli_score_topk.restype = C.c_int
+    L.qli_score_topk.argtypes = [C.POINTER(qli_params), C.c_void_p]
+    L.qli_status_string.restype = C.c_char_p
+    L.qli_status_string.argtypes = [C.c_int]
+    L.qli_timing_enable.restype = C.c_int
+    L.qli_timing_enable.argtypes = [C.c_int]
+    L.qli_timing_read.restype = C.c_int
+    L.qli_timing_read.argtypes = [C.c_void_p, C.c_void_p, C.c_int]
+    if path == LIB_PATH:
+        _lib = L
+    return L
+
+
+def qli_abi_version() -> int:
+    return load_library().qli_abi_version()
+
+
+def qli_validate(p: qli_params) -> int:
+    return load_library().qli_validate(C.byref(p))
+
+
+def qli_workspace_bytes(p: qli_params) -> int:
+    return load_library().qli_workspace_bytes(C.byref(p))
+
+
+def qli_score_topk(p: qli_params, stream=None) -> int:
+    """Enqueue one call on ``stream`` (a raw hipStream_t handle as int, or
+    None for torch's current stream)."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    return load_library().qli_score_topk(C.byref(p), C.c_void_p(stream))
+
+
+def qli_status_string(code: int) -> str:
+    return load_library().qli_status_string(code).decode()
+
+
+def qli_timing_enable(on: bool) -> int:
+    return load_library().qli_timing_enable(1 if on else 0)
+
+
+def qli_timing_read(reset: bool = True):
+    """(ms per kernel, launches per kernel) accumulated by the timing facility."""
+    ms = (C.c_double * QLI_NUM_KERNELS)()
+    cnt = (C.c_int64 * QLI_NUM_KERNELS)()
+    rc = load_library().qli_timing_read(ms, cnt, 1 if reset else 0)
+    if rc != QLI_OK:
+        raise RuntimeError(qli_status_string(rc))
+    return list(ms), list(cnt)
+
+
+def new_params() -> qli_params:
+    p = qli_params()
+    p.struct_size = C.sizeof(qli_params)
+    p.head_dim = 128
+    p.quant_mode = QLI_QUANT_INT8
+    return p
+
+
+def output_shapes(num_tokens: int, topk: int, cand_blocks: int, mode: int):
+    """Shapes of (indices, candidates) for a call; candidates only in source mode."""
+    return (num_tokens, 1, topk), ((num_tokens, 1, cand_blocks) if mode == QLI_MODE_SOURCE
+                                   else None)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def make_params(*, q, q_scale, weights, k_cache, k_scale, block_table, query_start_loc, k_lens,
+                seq_mod=None, cand_in=None, ratio, mode, topk, cand_blocks=0, max_k_len,
+                topk_out=None, cand_out=None, dbg_scores=None, status_out=None, workspace=None):
+    """Fill qli_params from torch tensors.
+
+    k_cache: int8 view [num_pages, page_rows, 128] of the paged index K (row
+    stride 128 bytes, any page stride); k_scale: fp16/int16 view
+    [num_pages, page_rows] (row stride 2 bytes, any page stride).  The page
+    strides are taken from the views, as given.
+    """
+    p = new_params()
+    T, N, D = q.shape
+    p.mode, p.ratio, p.num_heads, p.head_dim = mode, ratio, N, D
+    p.batch = k_lens.shape[0]
+    p.num_tokens = T
+    p.topk = topk
+    p.cand_blocks = cand_blocks
+    p.cand_in_blocks = cand_in.shape[-1] if cand_in is not None else 0
+    p.page_rows = k_cache.shape[1]
+    p.bt_stride = block_table.shape[1]
+    p.num_pages = k_cache.shape[0]
+    p.max_k_len = max_k_len
+    if k_cache.stride(1) != 128 or k_cache.stride(2) != 1 or k_scale.stride(1) != 1:
+        raise ValueError("k_cache rows must be 128 contiguous bytes, k_scale rows 2 bytes")
+    p.k_page_stride = k_cache.stride(0) * k_cache.element_size()
+    p.s_page_stride = k_scale.stride(0) * k_scale.element_size()
+    p.q, p.q_scale, p.weights = _ptr(q), _ptr(q_scale), _ptr(weights)
+    p.k_cache, p.k_scale = _ptr(k_cache), _ptr(k_scale)
+    p.block_table, p.query_start_loc, p.k_lens = _ptr(block_table), _ptr(query_start_loc), \
+        _ptr(k_lens)
+    p.seq_mod, p.cand_in = _ptr(seq_mod), _ptr(cand_in)
+    p.topk_out, p.cand_out = _ptr(topk_out), _ptr(cand_out)
+    p.dbg_scores, p.status_out = _ptr(dbg_scores), _ptr(status_out)
+    if workspace is not None:
+        p.workspace, p.workspace_bytes = _ptr(workspace), workspace.numel()
+    return p
+
+
+def score_topk(*, q, q_scale, weights, k_cache, k_scale, block_table, query_start_loc, k_lens,
+               seq_mod=None, cand_in=None, ratio, mode, topk, cand_blocks=0, max_k_len,
+               debug_scores=False, status_out=None, workspace=None, stream=None):
+    """One indexer call on torch device tensors.
+
+    Returns ``(indices [T,1,topk] int32, candidates [T,1,cb] int32 or None,
+    dbg_scores [T, max_k_len] float32 or None)``.  Raises RuntimeError with
+    the library's status string on a rejected call.
+    """
+    import torch
+    dev = q.device
+    T = q.shape[0]
+    shp_i, shp_c = output_shapes(T, topk, cand_blocks, mode)
+    topk_out = torch.empty(shp_i, dtype=torch.int32, device=dev)
+    cand_out = torch.empty(shp_c, dtype=torch.int32, device=dev) if shp_c else None
+    dbg = None
+    if debug_scores:
+        dbg = torch.full((T, max(max_k_len, 1)), float("nan"), dtype=torch.float32, device=dev)
+    p = make_params(q=q, q_scale=q_scale, weights=weights, k_cache=k_cache, k_scale=k_scale,
+                    block_table=block_table, query_start_loc=query_start_loc, k_lens=k_lens,
+                    seq_mod=seq_mod, cand_in=cand_in, ratio=ratio, mode=mode, topk=topk,
+                    cand_blocks=cand_blocks, max_k_len=max_k_len, topk_out=topk_out,
+                    cand_out=cand_out, dbg_scores=dbg, status_out=status_out)
+    need = qli_workspace_bytes(p)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    p.workspace, p.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    rc = qli_score_topk(p, stream)
+    if rc != QLI_OK:
+        raise RuntimeError(qli_status_string(rc))
+    return topk_out, cand_out, dbg

@@ -1,0 +1,105 @@
+// Host entry points of the QLI library: argument validation, workspace
+// sizing and status strings.  Validation mirrors the host-side checks the
+// QLI developer guide describes ("数据流": unsupported layouts are rejected
+// on the host before any kernel runs; the residual tensor must be absent at
+// ratio 1) and the contract limits of its "当前 A3 契约" section.
+#include <stdint.h>
+
+#include "qli.h"
+#include "qli_internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool cand_width_ok(int32_t w) { return w >= 64 && w <= QLI_MAX_CAND_BLOCKS && w % 64 == 0; }
+
+// Checks that need no pointer; shared by qli_validate and qli_workspace_bytes.
+int check_scalars(const qli_params* p) {
+  if (!p || p->struct_size != sizeof(qli_params)) return QLI_ERR_INVALID_ARG;
+  if (p->head_dim != 128) return QLI_ERR_UNSUPPORTED;
+  if (p->quant_mode != QLI_QUANT_INT8) return QLI_ERR_UNSUPPORTED;
+  if (p->num_heads != 32 && p->num_heads != 64) return QLI_ERR_UNSUPPORTED;
+  if (p->mode < QLI_MODE_PLAIN || p->mode > QLI_MODE_CONSUMER) return QLI_ERR_INVALID_ARG;
+  if (p->ratio != 1 && p->ratio != 2) return QLI_ERR_INVALID_ARG;
+  if (p->page_rows != 128 / p->ratio) return QLI_ERR_INVALID_ARG;
+  if (p->batch < 0 || p->num_tokens < 0 || p->reserved0 != 0) return QLI_ERR_INVALID_ARG;
+  if (p->num_tokens > 0 && p->batch < 1) return QLI_ERR_INVALID_ARG;
+  if (p->topk < 1 || p->topk > QLI_MAX_TOPK) return QLI_ERR_INVALID_ARG;
+  if (p->mode == QLI_MODE_SOURCE && !cand_width_ok(p->cand_blocks)) return QLI_ERR_INVALID_ARG;
+  if (p->mode == QLI_MODE_CONSUMER && !cand_width_ok(p->cand_in_blocks))
+    return QLI_ERR_INVALID_ARG;
+  if (p->max_k_len < 0) return QLI_ERR_INVALID_ARG;
+  if (p->max_k_len > QLI_MAX_K_LEN) return QLI_ERR_UNSUPPORTED;
+  if (p->bt_stride < 1 || p->num_pages < 1) return QLI_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(p->bt_stride) * p->page_rows < p->max_k_len) return QLI_ERR_INVALID_ARG;
+  if (p->k_page_stride < static_cast<int64_t>(p->page_rows) * 128 || p->k_page_stride % 16)
+    return QLI_ERR_INVALID_ARG;
+  if (p->s_page_stride < static_cast<int64_t>(p->page_rows) * 2 || p->s_page_stride % 2)
+    return QLI_ERR_INVALID_ARG;
+  // one workgroup per (token, 256-slot chunk) must fit a 31-bit grid
+  const qli::WsLayout w = qli::ws_layout(p);
+  if (static_cast<int64_t>(p->num_tokens) * (w.ncap / qli::kChunk) >= (int64_t(1) << 31))
+    return QLI_ERR_UNSUPPORTED;
+  return QLI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qli_abi_version(void) { return QLI_ABI_VERSION; }
+
+int qli_validate(const qli_params* p) {
+  int rc = check_scalars(p);
+  if (rc != QLI_OK) return rc;
+  // residual: absent at ratio 1 ("残差张量必须不存在"), needed at ratio 2
+  if (p->ratio == 1 && p->seq_mod) return QLI_ERR_INVALID_ARG;
+  if (p->mode == QLI_MODE_CONSUMER && !p->cand_in) return QLI_ERR_NO_SOURCE;
+  if (p->num_tokens == 0) return QLI_OK;
+  if (p->ratio == 2 && !p->seq_mod) return QLI_ERR_INVALID_ARG;
+  if (!p->q || !p->q_scale || !p->weights || !p->k_cache || !p->k_scale || !p->block_table ||
+      !p->query_start_loc || !p->k_lens || !p->topk_out)
+    return QLI_ERR_INVALID_ARG;
+  if (p->mode == QLI_MODE_SOURCE && !p->cand_out) return QLI_ERR_INVALID_ARG;
+  if (!aligned(p->q, 16) || !aligned(p->k_cache, 16) || !aligned(p->k_scale, 2) ||
+      !aligned(p->q_scale, 2) || !aligned(p->weights, 2) || !aligned(p->block_table, 4) ||
+      !aligned(p->query_start_loc, 4) || !aligned(p->k_lens, 4) || !aligned(p->topk_out, 4))
+    return QLI_ERR_INVALID_ARG;
+  const qli::WsLayout w = qli::ws_layout(p);
+  if (w.total > 0 && (!p->workspace || !aligned(p->workspace, 256))) return QLI_ERR_WORKSPACE;
+  if (p->workspace_bytes < w.total) return QLI_ERR_WORKSPACE;
+  return QLI_OK;
+}
+
+size_t qli_workspace_bytes(const qli_params* p) {
+  if (check_scalars(p) != QLI_OK) return 0;
+  return qli::ws_layout(p).total;
+}
+
+int qli_score_topk(const qli_params* p, void* stream) {
+  int rc = qli_validate(p);
+  if (rc != QLI_OK) return rc;
+  if (p->num_tokens == 0) return QLI_OK;
+  return qli::launch(p, qli::ws_layout(p), stream);
+}
+
+int qli_timing_enable(int on) { return qli::timing_enable(on); }
+
+int qli_timing_read(double* ms, int64_t* count, int reset) {
+  return qli::timing_read(ms, count, reset);
+}
+
+const char* qli_status_string(int status) {
+  switch (status) {
+    case QLI_OK: return "QLI_OK";
+    case QLI_ERR_INVALID_ARG: return "QLI_ERR_INVALID_ARG: argument out of contract";
+    case QLI_ERR_UNSUPPORTED: return "QLI_ERR_UNSUPPORTED: heads/dim/quant mode/size not supported";
+    case QLI_ERR_NO_SOURCE: return "QLI_ERR_NO_SOURCE: consumer mode needs incoming candidates";
+    case QLI_ERR_WORKSPACE: return "QLI_ERR_WORKSPACE: workspace missing or too small";
+    case QLI_ERR_HIP: return "QLI_ERR_HIP: kernel launch failed";
+    default: return "QLI: unknown status";
+  }
+}
+
+}  // extern "C"

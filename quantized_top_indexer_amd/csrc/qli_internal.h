@@ -1,0 +1,61 @@
+// Internal declarations shared by the host API and the kernel launcher.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qli.h"
+
+namespace qli {
+
+// Carve-up of the caller's workspace.
+//   keys   [T, ncap]  u32 order-preserving score keys by slot (0 = not eligible)
+//   bkeys  [T, nbcap] u32 block-max keys (source mode)
+//   slots  [T, cand_in_blocks] sorted unique visible incoming block ids (consumer)
+//   nslots [T]        number of valid entries in slots (consumer)
+struct WsLayout {
+  int64_t ncap = 0;
+  int64_t nbcap = 0;
+  size_t keys_off = 0;
+  size_t bkeys_off = 0;
+  size_t slots_off = 0;
+  size_t nslots_off = 0;
+  size_t total = 0;
+};
+
+constexpr int kChunk = 256;  // score slots per workgroup
+
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+inline WsLayout ws_layout(const qli_params* p) {
+  WsLayout w;
+  const int64_t T = p->num_tokens;
+  if (p->mode == QLI_MODE_CONSUMER)
+    w.ncap = static_cast<int64_t>(p->cand_in_blocks) * 8;
+  else
+    w.ncap = (static_cast<int64_t>(p->max_k_len) + kChunk - 1) / kChunk * kChunk;
+  size_t off = 0;
+  w.keys_off = off;
+  off = align256(off + static_cast<size_t>(T) * w.ncap * 4);
+  if (p->mode == QLI_MODE_SOURCE) {
+    w.nbcap = ((static_cast<int64_t>(p->max_k_len) + 7) / 8 + 63) / 64 * 64;
+    w.bkeys_off = off;
+    off = align256(off + static_cast<size_t>(T) * w.nbcap * 4);
+  }
+  if (p->mode == QLI_MODE_CONSUMER) {
+    w.slots_off = off;
+    off = align256(off + static_cast<size_t>(T) * p->cand_in_blocks * 4);
+    w.nslots_off = off;
+    off = align256(off + static_cast<size_t>(T) * 4);
+  }
+  w.total = off;
+  return w;
+}
+
+// Enqueue the kernels (arguments already validated).
+int launch(const qli_params* p, const WsLayout& w, void* stream);
+
+int timing_enable(int on);
+int timing_read(double* ms, int64_t* count, int reset);
+
+}  // namespace qli

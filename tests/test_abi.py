@@ -1,0 +1,175 @@
+"""The C ABI on the CPU: the library loads, exports every declared entry
+point, its struct layout matches the header, and every host-side rejection
+path returns the documented status without touching a GPU (validation runs
+before any launch, and a call with no tokens launches nothing)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+import quantized_top_indexer_amd as Q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qli.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(Q.LIB_PATH):
+        from quantized_top_indexer_amd import build
+        build.build()
+    return Q.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(qli_\w+)\s*\(", src, flags=re.M)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(Q.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", Q.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (qli_\w+)$", out, flags=re.M))
+    assert set(names) <= exported
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_abi_version(lib):
+    assert Q.qli_abi_version() == 1
+
+
+def test_struct_layout_matches_header(tmp_path):
+    fields = [f[0] for f in Q.qli_params._fields_]
+    prog = tmp_path / "layout.c"
+    body = "\n".join(f'  printf("{f} %zu\\n", offsetof(qli_params, {f}));' for f in fields)
+    prog.write_text(f'#include <stdio.h>\n#include <stddef.h>\n#include "qli.h"\n'
+                    f'int main(void) {{\n{body}\n  printf("sizeof %zu\\n", sizeof(qli_params));\n'
+                    f'  return 0;\n}}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), str(prog), "-o", str(exe)],
+                   check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                       check=True).stdout.splitlines())
+    for f in fields:
+        assert int(got[f]) == getattr(Q.qli_params, f).offset, f
+    assert int(got["sizeof"]) == C.sizeof(Q.qli_params)
+
+
+def base_params(mode=2, ratio=2, T=4):
+    """Scalars of a valid call with fake (never dereferenced) device pointers."""
+    p = Q.new_params()
+    p.mode, p.ratio, p.num_heads = mode, ratio, 32
+    p.batch, p.num_tokens, p.topk = 1, T, 16
+    p.cand_blocks, p.cand_in_blocks = 64, 64
+    p.page_rows = 128 // ratio
+    p.bt_stride, p.num_pages, p.max_k_len = 4, 8, 128
+    p.k_page_stride = 131072 if ratio == 2 else 147712
+    p.s_page_stride = p.k_page_stride
+    fake = 0x7F0000000000
+    for i, f in enumerate(("q", "q_scale", "weights", "k_cache", "k_scale", "block_table",
+                           "query_start_loc", "k_lens", "topk_out", "cand_out")):
+        setattr(p, f, fake + 4096 * i)
+    p.seq_mod = fake + 4096 * 20 if ratio == 2 else None
+    p.cand_in = fake + 4096 * 21 if mode == 3 else None
+    p.workspace = fake + (1 << 30)
+    p.workspace_bytes = 1 << 30
+    return p
+
+
+def test_valid_params_pass(lib):
+    for mode in (1, 2, 3):
+        for ratio in (1, 2):
+            assert Q.qli_validate(base_params(mode, ratio)) == Q.QLI_OK
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("struct_size", 8, Q.QLI_ERR_INVALID_ARG),
+    ("head_dim", 64, Q.QLI_ERR_UNSUPPORTED),
+    ("quant_mode", 1, Q.QLI_ERR_UNSUPPORTED),
+    ("num_heads", 16, Q.QLI_ERR_UNSUPPORTED),
+    ("num_heads", 128, Q.QLI_ERR_UNSUPPORTED),
+    ("mode", 0, Q.QLI_ERR_INVALID_ARG),
+    ("mode", 4, Q.QLI_ERR_INVALID_ARG),
+    ("ratio", 4, Q.QLI_ERR_INVALID_ARG),
+    ("page_rows", 128, Q.QLI_ERR_INVALID_ARG),
+    ("topk", 0, Q.QLI_ERR_INVALID_ARG),
+    ("topk", 2049, Q.QLI_ERR_INVALID_ARG),
+    ("cand_blocks", 32, Q.QLI_ERR_INVALID_ARG),
+    ("cand_blocks", 100, Q.QLI_ERR_INVALID_ARG),
+    ("cand_blocks", 2112, Q.QLI_ERR_INVALID_ARG),
+    ("batch", 0, Q.QLI_ERR_INVALID_ARG),
+    ("num_tokens", -1, Q.QLI_ERR_INVALID_ARG),
+    ("max_k_len", -1, Q.QLI_ERR_INVALID_ARG),
+    ("max_k_len", (1 << 24) + 1, Q.QLI_ERR_UNSUPPORTED),
+    ("bt_stride", 1, Q.QLI_ERR_INVALID_ARG),   # 1 page * 64 rows < max_k_len 128
+    ("num_pages", 0, Q.QLI_ERR_INVALID_ARG),
+    ("k_page_stride", 131072 + 8, Q.QLI_ERR_INVALID_ARG),
+    ("k_page_stride", 64 * 128 - 16, Q.QLI_ERR_INVALID_ARG),
+    ("s_page_stride", 131073, Q.QLI_ERR_INVALID_ARG),
+    ("reserved0", 1, Q.QLI_ERR_INVALID_ARG),
+    ("q", None, Q.QLI_ERR_INVALID_ARG),
+    ("k_cache", None, Q.QLI_ERR_INVALID_ARG),
+    ("topk_out", None, Q.QLI_ERR_INVALID_ARG),
+    ("cand_out", None, Q.QLI_ERR_INVALID_ARG),
+    ("seq_mod", None, Q.QLI_ERR_INVALID_ARG),           # ratio 2 needs the residual
+    ("q", 0x7F0000000000 + 8, Q.QLI_ERR_INVALID_ARG),   # not 16-B aligned
+    ("workspace", None, Q.QLI_ERR_WORKSPACE),
+    ("workspace_bytes", 1024, Q.QLI_ERR_WORKSPACE),
+])
+def test_rejections(lib, field, value, code):
+    p = base_params(mode=2, ratio=2)
+    setattr(p, field, value)
+    assert Q.qli_validate(p) == code
+    # the enqueue entry point rejects identically, before any launch
+    assert lib.qli_score_topk(C.byref(p), None) == code
+
+
+def test_residual_must_be_absent_at_ratio_1(lib):
+    p = base_params(mode=2, ratio=1)
+    p.seq_mod = 0x7F0000100000
+    assert Q.qli_validate(p) == Q.QLI_ERR_INVALID_ARG
+
+
+def test_consumer_without_source(lib):
+    p = base_params(mode=3)
+    p.cand_in = None
+    assert Q.qli_validate(p) == Q.QLI_ERR_NO_SOURCE
+    p = base_params(mode=3)
+    p.cand_in_blocks = 65
+    assert Q.qli_validate(p) == Q.QLI_ERR_INVALID_ARG
+
+
+def test_zero_tokens_is_a_noop(lib):
+    p = base_params(mode=2, T=0)
+    for f in ("q", "k_cache", "topk_out", "workspace"):
+        setattr(p, f, None)
+    p.workspace_bytes = 0
+    assert lib.qli_score_topk(C.byref(p), None) == Q.QLI_OK
+
+
+def test_workspace_bytes(lib):
+    p = base_params(mode=2, ratio=2, T=4)
+    # keys: 4 tokens * roundup(128, 256) slots * 4 B; block keys: 4 * 64 * 4 B
+    assert Q.qli_workspace_bytes(p) == 4 * 256 * 4 + 4 * 64 * 4
+    p = base_params(mode=3, ratio=2, T=4)
+    # keys: 4 * 64*8 * 4; slots: 4 * 64 * 4; nslots: 4 * 4 -> 256-B aligned
+    assert Q.qli_workspace_bytes(p) == 4 * 512 * 4 + 4 * 64 * 4 + 256
+    p.head_dim = 3
+    assert Q.qli_workspace_bytes(p) == 0
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert Q.qli_status_string(code).startswith("QLI_")
+    assert "unknown" in Q.qli_status_string(99)
+
+
+def test_output_shapes():
+    assert Q.output_shapes(7, 16, 64, Q.QLI_MODE_SOURCE) == ((7, 1, 16), (7, 1, 64))
+    assert Q.output_shapes(7, 16, 64, Q.QLI_MODE_CONSUMER) == ((7, 1, 16), None)

@@ -1,0 +1,156 @@
+"""GPU parity at sizes the oracle finishes in seconds: every output of every
+token compared with the oracle, bit for bit (indices, candidate ids, FP32
+scores), across ratios, head counts, modes, several 256-slot tiles and
+ragged tails, plus the edge cases of the method."""
+import numpy as np
+import pytest
+
+from gpu_check import (check_invariants, compare, oracle_rows, run_gpu, say, small_problem)
+
+pytestmark = pytest.mark.gpu
+
+MEDIUM = [
+    # (ratio, heads, mode, topk, cb, requests)
+    (2, 32, 2, 16, 64, ((4, 256),)),                                   # the tiny shape
+    (1, 64, 2, 100, 64, ((3, 1500), (1, 777), (2, 130))),
+    (2, 64, 2, 300, 128, ((5, 4001), (1, 999))),
+    (1, 32, 1, 7, 64, ((6, 2500), (1, 1), (2, 65))),
+    (2, 32, 1, 2048, 64, ((2, 3000), (1, 513))),
+    (1, 64, 3, 64, 64, ((3, 3333), (2, 700))),
+    (2, 32, 3, 500, 128, ((4, 5000), (1, 20))),
+    (1, 32, 2, 2048, 2048, ((2, 2600),)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(MEDIUM)))
+def test_medium_all_tokens(case):
+    ratio, N, mode, topk, cb, req = MEDIUM[case]
+    pb = small_problem(100 + case, ratio=ratio, N=N, mode=mode, topk=topk, cb=cb, cb_in=cb,
+                       requests=req)
+    say(f"case {pb.name}: T={pb.num_tokens} L={pb.max_k_len}")
+    gpu = run_gpu(pb, debug=True)
+    orc = oracle_rows(pb, scores=True)
+    compare(pb, gpu, orc)
+    check_invariants(pb, gpu)
+    # the production launch (no debug scores) gives the same outputs
+    prod = run_gpu(pb, debug=False)
+    assert np.array_equal(prod["topk"], gpu["topk"])
+    if mode == 2:
+        assert np.array_equal(prod["cand"], gpu["cand"])
+
+
+def test_tiny_workload():
+    import qli_workloads as W
+    pb = W.tiny()
+    gpu = run_gpu(pb, debug=True)
+    orc = oracle_rows(pb, scores=True)
+    compare(pb, gpu, orc)
+    check_invariants(pb, gpu)
+    assert np.all(gpu["cand"][:, 16:] == -1) and np.all(gpu["cand"][:, :16] == np.arange(16))
+
+
+EDGES = {
+    # empty compressed contexts at ratio 2 (raw length 1), a request whose
+    # queries cover its whole raw length (first query sees nothing), a
+    # request with no queries, lengths off every tile boundary
+    "empty_and_ragged": dict(ratio=2, N=32, mode=2, topk=33, cb=64,
+                             requests=((1, 1), (3, 3), (0, 500), (2, 17), (1, 1), (4, 1027))),
+    "ratio1_single_positions": dict(ratio=1, N=64, mode=2, topk=5, cb=64,
+                                    requests=((1, 1), (2, 2), (1, 9), (1, 257))),
+    "topk_exceeds_eligible": dict(ratio=2, N=32, mode=1, topk=2048, cb=64,
+                                  requests=((3, 600), (1, 4095))),
+    "cand_exceeds_blocks": dict(ratio=1, N=32, mode=2, topk=64, cb=2048,
+                                requests=((2, 1000), (1, 8), (1, 9))),
+    "topk_one": dict(ratio=2, N=64, mode=2, topk=1, cb=64, requests=((3, 2000),)),
+    "consumer_messy": dict(ratio=2, N=32, mode=3, topk=100, cb_in=128,
+                           requests=((3, 3000), (1, 1), (2, 15), (1, 4096)),
+                           cand_policy="messy"),
+    "consumer_ratio1_full": dict(ratio=1, N=64, mode=3, topk=2048, cb_in=64,
+                                 requests=((2, 600), (1, 1))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGES))
+def test_edges(name):
+    pb = small_problem(200 + sorted(EDGES).index(name), **EDGES[name])
+    say(f"edge {name}: T={pb.num_tokens} L={pb.max_k_len}")
+    gpu = run_gpu(pb, debug=True)
+    orc = oracle_rows(pb, scores=True)
+    compare(pb, gpu, orc)
+    check_invariants(pb, gpu)
+
+
+def test_layout_invariance():
+    """A larger page stride with K and scales moved inside the page gives
+    identical outputs (the kernels only follow the strides)."""
+    pb = small_problem(300, ratio=2, N=64, mode=2, topk=200, cb=64, requests=((3, 3000), (1, 50)))
+    a = run_gpu(pb, debug=True)
+    b = run_gpu(pb, debug=True, layout=dict(page_stride=131072 + 4096, k_offset=1024,
+                                            s_offset=1024 + 64 * 128 + 256))
+    assert np.array_equal(a["topk"], b["topk"]) and np.array_equal(a["cand"], b["cand"])
+    assert np.array_equal(a["scores"], b["scores"], equal_nan=True)
+
+
+def test_batching_invariance():
+    """A TND batch of requests equals one call per request."""
+    reqs = ((3, 1200), (1, 1), (2, 333), (1, 2048))
+    pb = small_problem(301, ratio=2, N=32, mode=2, topk=50, cb=64, requests=reqs)
+    whole = run_gpu(pb)
+    for b, r in enumerate(reqs):
+        one = small_problem(301, ratio=2, N=32, mode=2, topk=50, cb=64, requests=(r,))
+        # same request content: copy this request's queries and pages
+        q0, q1 = pb.query_start_loc[b], pb.query_start_loc[b + 1]
+        one.q, one.q_scale, one.weights = pb.q[q0:q1], pb.q_scale[q0:q1], pb.weights[q0:q1]
+        one.k_pages, one.s_pages = pb.k_pages, pb.s_pages
+        one.block_table = pb.block_table[b:b + 1]
+        res = run_gpu(one)
+        assert np.array_equal(res["topk"], whole["topk"][q0:q1])
+        assert np.array_equal(res["cand"], whole["cand"][q0:q1])
+
+
+def test_determinism():
+    pb = small_problem(302, ratio=1, N=64, mode=2, topk=256, cb=128, requests=((4, 3000),))
+    a, b = run_gpu(pb, debug=True), run_gpu(pb, debug=True)
+    for k in ("topk", "cand"):
+        assert np.array_equal(a[k], b[k])
+    assert np.array_equal(a["scores"], b["scores"], equal_nan=True)
+
+
+def test_device_status_flags():
+    """Out-of-contract device metadata is flagged and never dereferenced: a
+    block-table entry past the pool and a k_len above max_k_len."""
+    import torch
+
+    import quantized_top_indexer_amd as Q
+    pb = small_problem(303, ratio=2, N=32, mode=2, topk=40, cb=64, requests=((2, 2000), (1, 900)))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pb.block_table = pb.block_table.copy()
+    pb.block_table[0, 3] = pb.num_pages + 1000
+    res = run_gpu(pb, status=status)
+    assert int(status.item()) & Q.QLI_DEV_BAD_PAGE
+    row = res["topk"][:2]
+    assert not np.any((row >= 3 * 64) & (row < 4 * 64))  # nothing from the bad page
+    status.zero_()
+    pb2 = small_problem(304, ratio=2, N=32, mode=1, topk=40, requests=((1, 2000),))
+    pb2.k_lens = pb2.k_lens.copy()
+    pb2.k_lens[0] = pb2.max_k_len + 5  # call still declares the old bound
+    from qli_workloads.device import call_kwargs, to_device
+    dev = to_device(pb2, "cuda")
+    kw = call_kwargs(pb2, dev)
+    kw["max_k_len"] = 1000
+    idx, _, _ = Q.score_topk(**kw, status_out=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & Q.QLI_DEV_BAD_LENGTH
+    assert torch.all(idx == -1)
+
+
+def test_zero_tokens():
+    import torch
+
+    import quantized_top_indexer_amd as Q
+    pb = small_problem(305, ratio=1, N=32, mode=2, topk=8, requests=((0, 100),))
+    from qli_workloads.device import call_kwargs, to_device
+    dev = to_device(pb, "cuda")
+    idx, cand, _ = Q.score_topk(**call_kwargs(pb, dev))
+    torch.cuda.synchronize()
+    assert idx.shape == (0, 1, 8) and cand.shape == (0, 1, 64)
