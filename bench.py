@@ -36,6 +36,25 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def recorded_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (profiles/traffic.json), or None when the kernel source changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    src = os.path.join(ROOT, "quantized_top_indexer_amd", "csrc", "qli_kernels.hip")
+    if not os.path.exists(path):
+        return None, None
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    entry = json.load(open(path)).get(workload)
+    if not entry or entry.get("source_hash") != h:
+        return None, None
+    for k, v in entry["hbm_bytes_per_launch"].items():
+        if k.split("<")[0] == kernel:
+            return v, entry.get("summary")
+    return None, None
+
+
 def algorithmic(pb, cand_in=None):
     """Keys scored, algorithmic HBM bytes and INT8 ops of one call:
     each request's eligible K rows (+scale) once, queries/scales/weights,
@@ -164,17 +183,19 @@ def measure(pb, steps, warmup, copies=1, cand_sets=None, bound="hbm"):
     keys, nbytes, ops = algorithmic(pb, cand_sets[0] if cand_sets else None)
     kern = max(kms, key=kms.get)
     kt = kms[kern] * 1e-3
+    traffic, summary = recorded_traffic(pb.name, kern)
     if bound == "hbm":
         achieved = nbytes / kt / 1e9
         roof = {"bound": "hbm", "kernel": kern, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None, "alg_bytes_per_launch": nbytes,
+                "traffic": traffic, "traffic_summary": summary, "alg_bytes_per_launch": nbytes,
                 "kernel_ms": round(kms[kern], 5)}
     else:
         achieved = ops / kt / 1e12
         roof = {"bound": "mfma", "kernel": kern, "achieved": round(achieved, 1),
                 "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
-                "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": None,
+                "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic,
+                "traffic_summary": summary,
                 "alg_ops_per_launch": ops, "kernel_ms": round(kms[kern], 5)}
     del run
     import torch
@@ -213,9 +234,14 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--workload", default="decode_source",
+                    help="main workload (decode_source is the headline configuration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--others", default="prefill_chunk,decode_consumer_1m",
                     help="comma list of secondary workloads ('' for none)")
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MIB",
+                    help="only run a plain device copy kernel of this many MiB (5 launches), "
+                         "to scale HBM byte counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -227,36 +253,50 @@ def main():
     import torch
     import qli_workloads as W
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        n = int(args.copy_calibration * (1 << 20)) // 4
+        src = torch.ones(n, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.mul(src, 1, out=dst)  # one elementwise kernel: reads n*4 B, writes n*4 B
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_kernel_bytes_read": n * 4, "copy_kernel_bytes_written": n * 4,
+                          "launches": 5}), flush=True)
+        return
     import quantized_top_indexer_amd as Q
     Q.load_library()
 
-    log("decode_source: generating")
-    pb = W.decode_source()
-    main_m = measure(pb, args.steps, args.warmup, copies=args.copies, bound="hbm")
-    log(f"decode_source: {main_m['ms_per_step']:.4f} ms/step kernels {main_m['kernels_ms']}")
-
-    others = {}
-    for name in [s for s in args.others.split(",") if s]:
+    def run_workload(name, steps, copies):
         log(f"{name}: generating")
-        opb = W.WORKLOADS[name]()
+        wpb = W.WORKLOADS[name]()
         if name == "decode_consumer_1m":
             import numpy as np
             from qli_workloads import make_candidates, visible_counts, Requests
-            vis = visible_counts(Requests(n=np.ones(opb.batch, np.int64), S=opb.raw_lens),
-                                 opb.ratio)
-            sets = [opb.cand_in] + [make_candidates(opb.seed + 100 * c, 1, vis, 2048)
+            vis = visible_counts(Requests(n=np.ones(wpb.batch, np.int64), S=wpb.raw_lens),
+                                 wpb.ratio)
+            # eight candidate sets: the touched K rows of successive calls differ
+            sets = [wpb.cand_in] + [make_candidates(wpb.seed + 100 * c, 1, vis, 2048)
                                     for c in range(1, 8)]
-            m = measure(opb, args.steps, args.warmup, cand_sets=sets, copies=8, bound="hbm")
+            m = measure(wpb, steps, args.warmup, cand_sets=sets, copies=8, bound="hbm")
+        elif name == "prefill_chunk":
+            m = measure(wpb, steps, args.warmup, bound="mfma")
         else:
-            m = measure(opb, max(10, args.steps // 5), args.warmup, bound="mfma")
+            m = measure(wpb, steps, args.warmup, copies=copies, bound="hbm")
+        log(f"{name}: {m['ms_per_step']:.4f} ms/call kernels {m['kernels_ms']}")
+        return wpb, m
+
+    pb, main_m = run_workload(args.workload, args.steps, args.copies)
+    others = {}
+    for name in [s for s in args.others.split(",") if s and s != args.workload]:
+        opb, m = run_workload(name, max(10, args.steps // 5) if name == "prefill_chunk"
+                              else args.steps, args.copies)
         others[name] = {"keys_per_s": round(m["keys_per_s"], 1),
                         "ms_per_call": round(m["ms_per_step"], 5), "kernels_ms": m["kernels_ms"],
                         "roofline": m["roofline"]}
-        log(f"{name}: {m['ms_per_step']:.4f} ms/call kernels {m['kernels_ms']}")
         del opb
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and pb.mode != 3:
         log("cpu baseline: oracle on the host")
         cpu = cpu_baseline(pb)
 
@@ -273,10 +313,12 @@ def main():
         "vs_baseline": None,
         "dtype": "i8",
         "data": "synthetic",
-        "config": {"workload": "decode_source", "requests": 64, "query_tokens": 64,
-                   "compressed_len": 32768, "ratio": 1, "heads": 64, "head_dim": 128,
-                   "topk": 2048, "cand_blocks": 512, "page_rows": 128,
-                   "page_stride_bytes": 147712, "rotated_cache_copies": args.copies,
+        "config": {"workload": pb.name, "requests": pb.batch, "query_tokens": pb.num_tokens,
+                   "compressed_len": pb.max_k_len, "ratio": pb.ratio, "heads": pb.num_heads,
+                   "head_dim": 128, "mode": {1: "plain", 2: "source", 3: "consumer"}[pb.mode],
+                   "topk": pb.topk, "cand_blocks": pb.cand_blocks or pb.cand_in_blocks,
+                   "page_rows": pb.page_rows, "page_stride_bytes": pb.layout()[1],
+                   "rotated_cache_copies": args.copies if pb.mode != 3 else 8,
                    "parallelism": "single GPU"},
         "roofline": main_m["roofline"],
         "cpu_baseline": cpu,
