@@ -116,7 +116,7 @@ typedef struct qli_params {
   int64_t k_page_stride; /* bytes between page p and p+1 of the K view;
                             multiple of 16, >= page_rows * 128 */
   int64_t s_page_stride; /* bytes between page p and p+1 of the scale
-                            view; even, >= page_rows * 2 */
+                            view; multiple of 16, >= page_rows * 2 */
 
   /* inputs (device) */
   const int8_t* q;          /* [T, N, 128] int8, contiguous TND, 16-B aligned */
@@ -127,7 +127,8 @@ typedef struct qli_params {
                                16-B aligned */
   const void* k_scale;      /* row 0 of page 0 of the fp16 scale view: row j
                                of page p at (char*)k_scale + p*s_page_stride
-                               + j*2; 2-B aligned */
+                               + j*2; 16-B aligned (8 rows are read as one
+                               16-byte run) */
   const int32_t* block_table;     /* [B, bt_stride] page ids: compressed
                                      position j of request b lives in page
                                      block_table[b][j / page_rows], row
@@ -180,8 +181,8 @@ int qli_score_topk(const qli_params* p, void* stream);
 const char* qli_status_string(int status);
 
 /* Kernels of one call, in launch order (for the timing facility below). */
-enum qli_kernel { QLI_KERNEL_CONSUMER_PREP = 0, QLI_KERNEL_SCORE = 1, QLI_KERNEL_SELECT = 2,
-                  QLI_NUM_KERNELS = 3 };
+enum qli_kernel { QLI_KERNEL_CONSUMER_PREP = 0, QLI_KERNEL_PLAN = 1, QLI_KERNEL_SCORE = 2,
+                  QLI_KERNEL_SELECT = 3, QLI_NUM_KERNELS = 4 };
 
 /* Optional per-kernel timing (off by default; process-wide, not thread
  * safe).  While enabled, every qli_score_topk() call records a HIP event

@@ -48,8 +48,9 @@ class qli_params(C.Structure):
 
 EXPORTS = ("qli_abi_version", "qli_validate", "qli_workspace_bytes", "qli_score_topk",
            "qli_status_string", "qli_timing_enable", "qli_timing_read")
-QLI_KERNEL_CONSUMER_PREP, QLI_KERNEL_SCORE, QLI_KERNEL_SELECT, QLI_NUM_KERNELS = 0, 1, 2, 3
-KERNEL_NAMES = ("consumer_prep_kernel", "score_kernel", "select_kernel")
+QLI_KERNEL_CONSUMER_PREP, QLI_KERNEL_PLAN, QLI_KERNEL_SCORE, QLI_KERNEL_SELECT, \
+    QLI_NUM_KERNELS = 0, 1, 2, 3, 4
+KERNEL_NAMES = ("consumer_prep_kernel", "plan_kernel", "score_kernel", "select_kernel")
 
 _lib = None
 

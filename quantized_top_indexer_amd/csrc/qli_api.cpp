@@ -35,7 +35,7 @@ int check_scalars(const qli_params* p) {
   if (static_cast<int64_t>(p->bt_stride) * p->page_rows < p->max_k_len) return QLI_ERR_INVALID_ARG;
   if (p->k_page_stride < static_cast<int64_t>(p->page_rows) * 128 || p->k_page_stride % 16)
     return QLI_ERR_INVALID_ARG;
-  if (p->s_page_stride < static_cast<int64_t>(p->page_rows) * 2 || p->s_page_stride % 2)
+  if (p->s_page_stride < static_cast<int64_t>(p->page_rows) * 2 || p->s_page_stride % 16)
     return QLI_ERR_INVALID_ARG;
   // one workgroup per (token, 256-slot chunk) must fit a 31-bit grid
   const qli::WsLayout w = qli::ws_layout(p);
@@ -62,7 +62,7 @@ int qli_validate(const qli_params* p) {
       !p->query_start_loc || !p->k_lens || !p->topk_out)
     return QLI_ERR_INVALID_ARG;
   if (p->mode == QLI_MODE_SOURCE && !p->cand_out) return QLI_ERR_INVALID_ARG;
-  if (!aligned(p->q, 16) || !aligned(p->k_cache, 16) || !aligned(p->k_scale, 2) ||
+  if (!aligned(p->q, 16) || !aligned(p->k_cache, 16) || !aligned(p->k_scale, 16) ||
       !aligned(p->q_scale, 2) || !aligned(p->weights, 2) || !aligned(p->block_table, 4) ||
       !aligned(p->query_start_loc, 4) || !aligned(p->k_lens, 4) || !aligned(p->topk_out, 4))
     return QLI_ERR_INVALID_ARG;

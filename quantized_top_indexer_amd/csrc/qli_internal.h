@@ -9,44 +9,61 @@
 namespace qli {
 
 // Carve-up of the caller's workspace.
-//   keys   [T, ncap]  u32 order-preserving score keys by slot (0 = not eligible)
-//   bkeys  [T, nbcap] u32 block-max keys (source mode)
+//   keys   [T, ncap]    u32 order-preserving score keys by slot (0 = not eligible)
+//   bkeys  [T, nbcap]   u32 block-max keys (source mode)
+//   plan   header (group count, work units), groups [T] x 32 B, ustart [T+1]:
+//          the work list the plan kernel builds for the persistent score kernel
 //   slots  [T, cand_in_blocks] sorted unique visible incoming block ids (consumer)
-//   nslots [T]        number of valid entries in slots (consumer)
+//   srow   [T, cand_in_blocks] page*page_rows + row of each slot block (consumer)
+//   ncount [T]          eligible positions per token (consumer)
 struct WsLayout {
   int64_t ncap = 0;
   int64_t nbcap = 0;
   size_t keys_off = 0;
   size_t bkeys_off = 0;
+  size_t plan_off = 0;
+  size_t groups_off = 0;
+  size_t ustart_off = 0;
   size_t slots_off = 0;
-  size_t nslots_off = 0;
+  size_t srow_off = 0;
+  size_t ncount_off = 0;
   size_t total = 0;
 };
 
-constexpr int kChunk = 256;  // score slots per workgroup
+constexpr int kChunk = 256;       // score slots per work item
+constexpr int kGroupTokens = 4;   // tokens of one request sharing a K tile (plain/source)
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 inline WsLayout ws_layout(const qli_params* p) {
   WsLayout w;
-  const int64_t T = p->num_tokens;
+  const size_t T = static_cast<size_t>(p->num_tokens);
   if (p->mode == QLI_MODE_CONSUMER)
     w.ncap = static_cast<int64_t>(p->cand_in_blocks) * 8;
   else
     w.ncap = (static_cast<int64_t>(p->max_k_len) + kChunk - 1) / kChunk * kChunk;
   size_t off = 0;
   w.keys_off = off;
-  off = align256(off + static_cast<size_t>(T) * w.ncap * 4);
+  off = align256(off + T * static_cast<size_t>(w.ncap) * 4);
   if (p->mode == QLI_MODE_SOURCE) {
     w.nbcap = ((static_cast<int64_t>(p->max_k_len) + 7) / 8 + 63) / 64 * 64;
     w.bkeys_off = off;
-    off = align256(off + static_cast<size_t>(T) * w.nbcap * 4);
+    off = align256(off + T * static_cast<size_t>(w.nbcap) * 4);
   }
+  w.plan_off = off;
+  off = align256(off + 256);
+  w.groups_off = off;
+  off = align256(off + T * 32);
+  w.ustart_off = off;
+  off = align256(off + (T + 1) * 4);
   if (p->mode == QLI_MODE_CONSUMER) {
+    const size_t cb = static_cast<size_t>(p->cand_in_blocks);
     w.slots_off = off;
-    off = align256(off + static_cast<size_t>(T) * p->cand_in_blocks * 4);
-    w.nslots_off = off;
-    off = align256(off + static_cast<size_t>(T) * 4);
+    off = align256(off + T * cb * 4);
+    w.srow_off = off;
+    off = align256(off + T * cb * 4);
+    w.ncount_off = off;
+    off = align256(off + T * 4);
   }
   w.total = off;
   return w;

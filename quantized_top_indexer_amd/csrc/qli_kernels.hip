@@ -1,25 +1,33 @@
 // HIP kernels of the quantized lightning indexer for CDNA4 (gfx950).
 //
-// Three kernels per call (DeepSeek V4.1 QLI developer guide, "数据流" and
-// "当前 A3 契约"):
-//   consumer_prep  (consumer mode only) one workgroup per token: sort and
+// One call = up to four kernels (DeepSeek V4.1 QLI developer guide, "数据流"
+// and "当前 A3 契约"):
+//   consumer_prep  (consumer mode) one workgroup per token: sort and
 //                  de-duplicate the incoming candidate block ids, drop ids
-//                  without a visible position -> a dense slot list.
-//   score          one workgroup (4 waves) per (token, 256-slot chunk):
-//                  stage 64 paged K rows per wave in LDS, INT8 MFMA
-//                  (v_mfma_i32_32x32x32_i8) of the token's [N x 128] queries
-//                  against them, then the golden FP16/FP32 epilogue, the
-//                  8-position block maximum, and order-preserving u32 keys.
-//   select         one workgroup per token: radix select of the position
-//                  top-k (and, in source mode, of the candidate blocks with
-//                  the last visible block pinned), emitted in ascending
-//                  order by a stream compaction, -1 tail.
+//                  without a visible position, resolve each kept block to its
+//                  page row -> dense slot list + eligible count.
+//   plan           one workgroup: cut the batch into groups (up to 4
+//                  consecutive query tokens of one request in plain/source
+//                  mode, one token in consumer mode) and prefix-sum their
+//                  256-slot work units, so that a persistent kernel can split
+//                  any mix of decode tokens and prefill chunks evenly.
+//   score          persistent, two workgroups per CU.  Each workgroup walks a
+//                  contiguous range of work items (group, 256-slot chunk) with
+//                  a three-stage software pipeline: page lookup two items
+//                  ahead, K + scale loads one item ahead (registers), and for
+//                  the current item an LDS tile shared by the group's tokens,
+//                  INT8 MFMA (v_mfma_i32_32x32x32_i8, queries x keys), the
+//                  golden FP16/FP32 epilogue, block maxima and order keys.
+//   select         one workgroup per (token, positions|blocks): keys held in
+//                  registers, radix select on 11/11/10-bit digits, then one
+//                  block scan for an ordered compaction that emits the winners
+//                  already in ascending order, -1 tail.
 //
-// Exactness: the epilogue follows the golden order with one IEEE RNE
-// rounding per step and sums heads in ascending order from +0.0f, so the
-// scores, and therefore every selection, are bit-identical to a sequential
-// reference.  The file is built with -ffp-contract=off so that no FP16
-// product is fused into the FP32 accumulation.
+// Exactness: the epilogue applies one IEEE round-to-nearest-even per golden
+// step and sums heads in ascending order from +0.0f in a single lane, so the
+// scores and every selection are bit-identical to a sequential reference.
+// Built with -ffp-contract=off; the two mixed-precision steps that must not
+// be re-associated are written as explicit v_fma_mix instructions.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,9 +42,28 @@ namespace {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef int16_t s2 __attribute__((ext_vector_type(2)));
+
+struct PlanHdr {
+  int32_t ngroups;
+  int32_t units;
+  int32_t pad[62];
+};
+
+// A group: ntok consecutive query tokens t0.. of request b sharing K tiles.
+//   p0    raw position of t0
+//   L     compressed length of the request (0 when its metadata is invalid)
+//   n0    eligible slots of t0 (dense: its visible count; consumer: ncount)
+//   nlast eligible slots of the group's last token (>= every member's)
+//   nch   256-slot work items: ceil(nlast / 256)
+struct Group {
+  int32_t t0, ntok, b, nch, p0, L, n0, nlast;
+};
 
 struct KArgs {
-  int mode, ratio, B, T, topk, cb, cb_in, R, bt_stride, num_pages, max_k_len, nchunks;
+  float one;  // 1.0f
+  int mode, ratio, rshift, B, T, topk, cb, cb_in, R, rlog, bt_stride, num_pages, max_k_len;
   int64_t kstride, sstride, ncap, nbcap;
   const int8_t* q;
   const uint16_t* qs;
@@ -54,59 +81,80 @@ struct KArgs {
   uint32_t* status;
   uint32_t* keys;
   uint32_t* bkeys;
+  PlanHdr* hdr;
+  Group* groups;
+  int32_t* ustart;
   int32_t* slots;
-  int32_t* nslots;
+  int32_t* srow;
+  int32_t* ncount;
 };
 
 __device__ __forceinline__ void raise_flag(const KArgs& a, uint32_t bit) {
   if (a.status) atomicOr(a.status, bit);
 }
 
-// Request b of token t and its visible compressed count V (causal mask
-// mode 3: the queries are the request's last raw positions; the query at
-// raw position p sees entries j < floor((p+1)/r)).  Out-of-contract
-// metadata is flagged and clamped so that every access stays in bounds.
+__device__ __forceinline__ int request_of(const KArgs& a, int t) {
+  int lo = 0, hi = a.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.qsl[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Per-request causal view (causal mask mode 3): the request's n_b queries
+// are its last raw positions, the raw length is L*r + residual, and the
+// query at raw position p sees compressed entries j < floor((p+1)/r).
+// Out-of-contract metadata gives L = 0 (nothing visible) and a flag.
+struct ReqView {
+  int q0, q1, L;
+  int64_t S;
+};
+
+__device__ __forceinline__ ReqView request_view(const KArgs& a, int b, bool report) {
+  ReqView v;
+  v.q0 = a.qsl[b];
+  v.q1 = a.qsl[b + 1];
+  int L = a.klen[b];
+  const int s = a.smod ? a.smod[b] : 0;
+  if (L < 0 || L > a.max_k_len) {
+    if (report) raise_flag(a, QLI_DEV_BAD_LENGTH);
+    L = 0;
+  } else if (s < 0 || s >= a.ratio) {
+    if (report) raise_flag(a, QLI_DEV_BAD_METADATA);
+    L = 0;
+  } else if (static_cast<int64_t>(v.q1) - v.q0 > static_cast<int64_t>(L) * a.ratio + s) {
+    if (report) raise_flag(a, QLI_DEV_BAD_METADATA);
+    L = 0;
+  }
+  v.L = L;
+  v.S = L == 0 ? static_cast<int64_t>(v.q1) - v.q0 : static_cast<int64_t>(L) * a.ratio + s;
+  return v;
+}
+
+// visible count of the query at raw position p
+__device__ __forceinline__ int visible(const KArgs& a, int64_t p, int L) {
+  const int64_t V = (p + 1) >> a.rshift;
+  return static_cast<int>(V < L ? V : L);
+}
+
 struct TokView {
   int b;
   int V;
 };
 
-__device__ TokView token_view(const KArgs& a, int t, bool report) {
-  int lo = 0, hi = a.B - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (a.qsl[mid] <= t) lo = mid;
-    else hi = mid - 1;
-  }
-  const int b = lo;
-  const int q0 = a.qsl[b], q1 = a.qsl[b + 1];
-  int L = a.klen[b];
-  int s = a.smod ? a.smod[b] : 0;
-  if (L < 0 || L > a.max_k_len) {
-    if (report) raise_flag(a, QLI_DEV_BAD_LENGTH);
-    return {b, 0};
-  }
-  if (s < 0 || s >= a.ratio) {
-    if (report) raise_flag(a, QLI_DEV_BAD_METADATA);
-    return {b, 0};
-  }
-  const int64_t n = static_cast<int64_t>(q1) - q0;
-  const int64_t S = static_cast<int64_t>(L) * a.ratio + s;
-  if (t < q0 || t >= q1 || n > S) {
-    if (report) raise_flag(a, QLI_DEV_BAD_METADATA);
-    return {b, 0};
-  }
-  const int64_t p = S - n + (t - q0);
-  int64_t V = (p + 1) / a.ratio;
-  if (V > L) V = L;
-  return {b, static_cast<int>(V)};
+__device__ __forceinline__ TokView token_view(const KArgs& a, int t) {
+  const int b = request_of(a, t);
+  const ReqView r = request_view(a, b, false);
+  if (t < r.q0 || t >= r.q1) return {b, 0};
+  const int64_t p = r.S - (r.q1 - r.q0) + (t - r.q0);
+  return {b, visible(a, p, r.L)};
 }
 
-// Page holding compressed position `pos` of request b, or -1.
-__device__ __forceinline__ int page_of(const KArgs& a, const int32_t* btrow, int pos) {
-  const int idx = pos / a.R;
+__device__ __forceinline__ int page_checked(const KArgs& a, int b, int idx) {
   if (idx >= a.bt_stride) return -1;
-  const int page = btrow[idx];
+  const int page = a.bt[static_cast<int64_t>(b) * a.bt_stride + idx];
   return (page >= 0 && page < a.num_pages) ? page : -1;
 }
 
@@ -119,388 +167,96 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ _Float16 h_from_bits(uint16_t v) { return __builtin_bit_cast(_Float16, v); }
-__device__ __forceinline__ uint16_t h_bits(_Float16 v) { return __builtin_bit_cast(uint16_t, v); }
+__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
+__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 
-// ---------------------------------------------------------------------------
-// score
-// ---------------------------------------------------------------------------
-//
-// Wave w of a workgroup owns slots [s0, s0 + 64).  MFMA operands
-// (v_mfma_i32_32x32x32_i8, 64 lanes):
-//   A (queries): lane l supplies row l%32 of a 32-head tile, 16 bytes of the
-//     head dimension; B (keys): lane l supplies column l%32 (one position),
-//     the same 16 bytes.  Dim d = 64*(l/32) + 16*step + byte feeds both, so
-//     the K reduction pairs q[h,d] with k[j,d] whatever the hardware order.
-//   C: lane l holds column l%32, rows 8*(i/4) + 4*(l/32) + i%4 (i < 16).
-// A rows are permuted so that C register i of lane group g = l/32 in head
-// tile m is head g*(N/2) + 16*m + i: lanes 0..31 then hold heads
-// 0..N/2-1, lanes 32..63 heads N/2..N-1 of the same positions, and one
-// v_permlane32_swap gives every lane all N heads of one position in
-// ascending order (lane L -> slot s0 + L).
-template <int NH, bool CONSUMER>
-__global__ __launch_bounds__(256) void score_kernel(KArgs a) {
-  constexpr int MT = NH / 32;  // 32-head tiles
-  constexpr int HALF = NH / 2;
-  const int64_t wg = blockIdx.x;
-  const int t = static_cast<int>(wg / a.nchunks);
-  const int chunk = static_cast<int>(wg % a.nchunks);
-  const TokView tv = token_view(a, t, threadIdx.x == 0 && chunk == 0);
-  const int n_t = CONSUMER ? a.nslots[t] * 8 : tv.V;
-  const int base = chunk * kChunk;
-  if (base >= n_t) return;  // uniform over the workgroup
-
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int s0 = base + wave * 64;
-  const int32_t* btrow = a.bt + static_cast<int64_t>(tv.b) * a.bt_stride;
-  const int32_t* slots = CONSUMER ? a.slots + static_cast<int64_t>(t) * a.cb_in : nullptr;
-
-  __shared__ __attribute__((aligned(16))) int8_t lds[4 * 64 * 128];
-  int8_t* my = lds + wave * (64 * 128);
-
-  // ---- stage K: load u covers slots s0+8u .. s0+8u+7 (one 1 KB run) ------
-  uint32_t bad = 0;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int r8 = lane >> 3, col = lane & 7;
-    const int row = 8 * u + r8;
-    const int slot = s0 + row;
-    i32x4 v = {0, 0, 0, 0};
-    if (slot < n_t) {
-      const int pos = CONSUMER ? slots[slot >> 3] * 8 + (slot & 7) : slot;
-      if (pos < tv.V) {
-        const int page = page_of(a, btrow, pos);
-        if (page >= 0) {
-          const int8_t* src = a.k + static_cast<int64_t>(page) * a.kstride +
-                              static_cast<int64_t>(pos % a.R) * 128 + col * 16;
-          v = *reinterpret_cast<const i32x4*>(src);
-        } else {
-          bad = 1;
-        }
-      }
-    }
-    *reinterpret_cast<i32x4*>(my + row * 128 + ((col ^ (row & 7)) << 4)) = v;
-  }
-  if (bad) raise_flag(a, QLI_DEV_BAD_PAGE);
-
-  // ---- queries as MFMA A operands ------------------------------------------
-  i32x4 qa[MT][4];
-  {
-    const int r = lane & 31;
-    const int g = lane >> 5;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int head = ((r >> 2) & 1) * HALF + 16 * m + 4 * (r >> 3) + (r & 3);
-      const int8_t* qrow = a.q + (static_cast<int64_t>(t) * NH + head) * 128 + 64 * g;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) qa[m][s] = *reinterpret_cast<const i32x4*>(qrow + 16 * s);
-    }
-  }
-
-  // per-head multipliers m_h = fp16(w_h * q_scale_h) for this lane's heads
-  _Float16 mh[HALF];
-  {
-    const int g = lane >> 5;
-    const uint16_t* wr = a.w + static_cast<int64_t>(t) * NH + g * HALF;
-    const uint16_t* qr = a.qs + static_cast<int64_t>(t) * NH + g * HALF;
-#pragma unroll
-    for (int j = 0; j < HALF; ++j) mh[j] = h_from_bits(wr[j]) * h_from_bits(qr[j]);
-  }
-
-  __syncthreads();
-
-  // ---- INT8 MFMA -----------------------------------------------------------
-  i32x16 acc[MT][2];
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[m][n][i] = 0;
-
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int row = 32 * n + (lane & 31);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int col = 4 * (lane >> 5) + s;
-      const i32x4 bk = *reinterpret_cast<const i32x4*>(my + row * 128 + ((col ^ (row & 7)) << 4));
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-        acc[m][n] = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[m][s], bk, acc[m][n], 0, 0, 0);
-    }
-  }
-
-  // ---- golden epilogue -------------------------------------------------------
-  // x = fp16(qk/1024) (qk*2^-10 is exact in FP32), ReLU, p = fp16(x*m)
-  uint32_t pk[2][HALF / 2];
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        _Float16 p2[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          _Float16 x = static_cast<_Float16>(static_cast<float>(acc[m][n][i + e]) * 0.0009765625f);
-          x = x > static_cast<_Float16>(0.0f) ? x : static_cast<_Float16>(0.0f);
-          p2[e] = x * mh[16 * m + i + e];
-        }
-        pk[n][(16 * m + i) >> 1] = static_cast<uint32_t>(h_bits(p2[0])) |
-                                   (static_cast<uint32_t>(h_bits(p2[1])) << 16);
-      }
-    }
-  }
-  // lanes 0..31: heads lo of tile 0 / lanes 32..63: heads hi of tile 1 stay;
-  // the other halves cross over, so each lane ends with all heads of slot s0+lane
-  uint32_t lo[HALF / 2], hi[HALF / 2];
-#pragma unroll
-  for (int j = 0; j < HALF / 2; ++j) {
-    auto r = __builtin_amdgcn_permlane32_swap(pk[0][j], pk[1][j], false, false);
-    lo[j] = r[0];
-    hi[j] = r[1];
-  }
-  float sum = 0.0f;
-#pragma unroll
-  for (int j = 0; j < HALF / 2; ++j) {
-    sum = sum + static_cast<float>(h_from_bits(static_cast<uint16_t>(lo[j] & 0xFFFFu)));
-    sum = sum + static_cast<float>(h_from_bits(static_cast<uint16_t>(lo[j] >> 16)));
-  }
-#pragma unroll
-  for (int j = 0; j < HALF / 2; ++j) {
-    sum = sum + static_cast<float>(h_from_bits(static_cast<uint16_t>(hi[j] & 0xFFFFu)));
-    sum = sum + static_cast<float>(h_from_bits(static_cast<uint16_t>(hi[j] >> 16)));
-  }
-
-  // ---- K scale, key, block max ------------------------------------------------
-  const int slot = s0 + lane;
-  uint32_t key = 0;
-  if (slot < n_t) {
-    const int pos = CONSUMER ? slots[slot >> 3] * 8 + (slot & 7) : slot;
-    if (pos < tv.V) {
-      const int page = page_of(a, btrow, pos);
-      if (page >= 0) {
-        const uint8_t* sp = a.ks + static_cast<int64_t>(page) * a.sstride +
-                            static_cast<int64_t>(pos % a.R) * 2;
-        const float kscale = static_cast<float>(h_from_bits(*reinterpret_cast<const uint16_t*>(sp)));
-        const float score = sum * kscale;
-        key = order_key(score);
-        if (a.dbg) a.dbg[static_cast<int64_t>(t) * a.max_k_len + pos] = score;
-      }
-    }
-  }
-  a.keys[static_cast<int64_t>(t) * a.ncap + slot] = key;
-  if (!CONSUMER && a.mode == QLI_MODE_SOURCE) {
-    uint32_t bk = key;
-    bk = max(bk, static_cast<uint32_t>(__shfl_xor(static_cast<int>(bk), 1)));
-    bk = max(bk, static_cast<uint32_t>(__shfl_xor(static_cast<int>(bk), 2)));
-    bk = max(bk, static_cast<uint32_t>(__shfl_xor(static_cast<int>(bk), 4)));
-    if ((lane & 7) == 0 && slot < n_t) a.bkeys[static_cast<int64_t>(t) * a.nbcap + (slot >> 3)] = bk;
-  }
+// ReLU of two fp16 values given as bits: an fp16 is negative (or -0) exactly
+// when its bit pattern is a negative int16, so max(bits, 0) as int16 gives
+// x for x > 0 and +0 otherwise (no NaN can occur here).
+__device__ __forceinline__ uint32_t relu_h2(uint32_t v) {
+  const s2 x = __builtin_bit_cast(s2, v);
+  const s2 z = {0, 0};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, z));
 }
 
-// ---------------------------------------------------------------------------
-// block-wide helpers (1024 threads)
-// ---------------------------------------------------------------------------
-constexpr int kSelThreads = 1024;
+// Accumulator word holding the bits of 24576 + qk/512 (the MFMA accumulator
+// is seeded with the bits of 24576.0f, whose ulp is 2^-9, so the integer sum
+// of the seed and qk is exactly that float for |qk| < 2^22) -> fp16(qk/1024):
+// 0.5*F - 12288 is exact, and the conversion rounds it once (RNE).  Written
+// as an fma so that it becomes one v_fma_mixlo_f16 (an fma by 1.0 would be
+// folded into an add); no inline assembly touches MFMA results, so the
+// compiler inserts the MFMA-to-VALU wait states.
+constexpr int32_t kSeedBits = 0x46C00000;  // 24576.0f
+__device__ __forceinline__ _Float16 qk_to_half(int32_t acc) {
+  return static_cast<_Float16>(__builtin_fmaf(__int_as_float(acc), 0.5f, -12288.0f));
+}
 
+// s + float(h) with one FP32 rounding: fma(h, one, s) with one == 1.0 held
+// in a kernel argument (opaque to constant folding) selects v_fma_mix_f32.
+__device__ __forceinline__ float add_h(float s, _Float16 h, float one) {
+  return __builtin_fmaf(static_cast<float>(h), one, s);
+}
+
+template <int BS>
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    uint32_t o = static_cast<uint32_t>(__shfl_up(static_cast<int>(v), d));
+    const uint32_t o = static_cast<uint32_t>(__shfl_up(static_cast<int>(v), d));
     if (lane >= d) v += o;
   }
   return v;
 }
 
-// Exclusive prefix of v over the workgroup; *total receives the sum.
+// Exclusive prefix of v over a workgroup of BS threads (BS/64 <= 16 waves);
+// *total receives the sum.  Uses sh[0..47].
+template <int BS>
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total, uint32_t* sh) {
+  constexpr int NW = BS / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t inc = wave_inclusive_scan(v, lane);
+  const uint32_t inc = wave_inclusive_scan<BS>(v, lane);
   if (lane == 63) sh[wave] = inc;
   __syncthreads();
   if (wave == 0) {
-    uint32_t w = lane < kSelThreads / 64 ? sh[lane] : 0u;
-    uint32_t wi = wave_inclusive_scan(w, lane);
-    if (lane < kSelThreads / 64) sh[32 + lane] = wi - w;
-    if (lane == kSelThreads / 64 - 1) sh[63] = wi;
+    const uint32_t x = lane < NW ? sh[lane] : 0u;
+    const uint32_t xi = wave_inclusive_scan<BS>(x, lane);
+    if (lane < NW) sh[16 + lane] = xi - x;
+    if (lane == NW - 1) sh[32] = xi;
   }
   __syncthreads();
-  const uint32_t out = sh[32 + wave] + inc - v;
-  *total = sh[63];
+  const uint32_t out = sh[16 + wave] + inc - v;
+  *total = sh[32];
   __syncthreads();
   return out;
-}
-
-// Keys of the items a selection ranks.
-struct KeySrc {
-  const uint32_t* keys;
-  int pin;  // index forced to the top, or -1
-  __device__ __forceinline__ uint32_t operator()(int i) const {
-    return i == pin ? 0xFFFFFFFFu : keys[i];
-  }
-};
-
-// Select the best min(k, #nonzero) of keys[0..n) by (key desc, index asc)
-// and write map(index) for them in ascending index order to out[0..k),
-// -1 after.  Radix select over 8-bit digits (MSB first) finds the k-th key
-// T; everything above T is taken, plus the lowest-index keys equal to T.
-template <class Map>
-__device__ void select_topk(KeySrc src, int n, int k, int32_t* out, Map map, uint32_t* hist,
-                            uint32_t* sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t prefix = 0, mask = 0;
-  int krem = k;
-  bool take_all = false;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += kSelThreads) {
-      const uint32_t key = src(i);
-      if (key != 0 && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // suffix sums: lane l covers bins 4l..4l+3
-      uint32_t c = hist[4 * lane] + hist[4 * lane + 1] + hist[4 * lane + 2] + hist[4 * lane + 3];
-      // inclusive suffix scan over lanes
-      uint32_t s = c;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        uint32_t o = static_cast<uint32_t>(__shfl_down(static_cast<int>(s), d));
-        if (lane + d < 64) s += o;
-      }
-      const uint32_t above_lane = s - c;  // bins > 4l+3
-      const uint32_t total = static_cast<uint32_t>(__shfl(static_cast<int>(s), 0));
-      if (pass == 0 && total <= static_cast<uint32_t>(k)) {
-        if (lane == 0) sh[0] = 1u;  // every eligible key is selected
-      } else {
-        if (lane == 0) sh[0] = 0u;
-        if (above_lane < static_cast<uint32_t>(krem) && s >= static_cast<uint32_t>(krem)) {
-          uint32_t cum = above_lane;
-          for (int bidx = 3; bidx >= 0; --bidx) {
-            const uint32_t h = hist[4 * lane + bidx];
-            if (cum + h >= static_cast<uint32_t>(krem)) {
-              sh[1] = static_cast<uint32_t>(4 * lane + bidx);
-              sh[2] = cum;
-              break;
-            }
-            cum += h;
-          }
-        }
-      }
-    }
-    __syncthreads();
-    if (sh[0]) {
-      take_all = true;
-      __syncthreads();
-      break;
-    }
-    const uint32_t digit = sh[1];
-    krem -= static_cast<int>(sh[2]);
-    prefix |= digit << shift;
-    mask |= 255u << shift;
-    __syncthreads();
-  }
-
-  // stream compaction in ascending index order
-  const uint32_t thr = prefix;
-  const uint32_t need = take_all ? 0u : static_cast<uint32_t>(krem);
-  uint32_t run_sel = 0, run_eq = 0;
-  for (int base = 0; base < n; base += kSelThreads * 4) {
-    uint32_t keys[4];
-    uint32_t neq = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = base + tid * 4 + e;
-      keys[e] = i < n ? src(i) : 0u;
-      if (!take_all && keys[e] == thr && keys[e] != 0) ++neq;
-    }
-    uint32_t tot_eq;
-    uint32_t eq_rank = block_exclusive_scan(neq, &tot_eq, sh) + run_eq;
-    bool sel[4];
-    uint32_t nsel = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (take_all) {
-        sel[e] = keys[e] != 0;
-      } else {
-        const bool eq = keys[e] == thr && keys[e] != 0;
-        sel[e] = keys[e] > thr || (eq && eq_rank < need);
-        if (eq) ++eq_rank;
-      }
-      nsel += sel[e] ? 1u : 0u;
-    }
-    uint32_t tot_sel;
-    uint32_t at = block_exclusive_scan(nsel, &tot_sel, sh) + run_sel;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (sel[e] && at < static_cast<uint32_t>(k)) out[at++] = map(base + tid * 4 + e);
-    run_sel += tot_sel;
-    run_eq += tot_eq;
-  }
-  for (int i = static_cast<int>(run_sel) + tid; i < k; i += kSelThreads) out[i] = -1;
-  __syncthreads();
-}
-
-struct MapIdentity {
-  __device__ __forceinline__ int32_t operator()(int i) const { return i; }
-};
-
-struct MapSlots {
-  const int32_t* slots;
-  __device__ __forceinline__ int32_t operator()(int i) const { return slots[i >> 3] * 8 + (i & 7); }
-};
-
-__global__ __launch_bounds__(kSelThreads) void select_kernel(KArgs a) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh[64];
-  const int t = blockIdx.x;
-  const TokView tv = token_view(a, t, false);
-  int32_t* out = a.topk_out + static_cast<int64_t>(t) * a.topk;
-  const uint32_t* keys = a.keys + static_cast<int64_t>(t) * a.ncap;
-  if (a.mode == QLI_MODE_CONSUMER) {
-    const int32_t* slots = a.slots + static_cast<int64_t>(t) * a.cb_in;
-    const int n = a.nslots[t] * 8;
-    select_topk(KeySrc{keys, -1}, n, a.topk, out, MapSlots{slots}, hist, sh);
-  } else {
-    select_topk(KeySrc{keys, -1}, tv.V, a.topk, out, MapIdentity{}, hist, sh);
-  }
-  if (a.mode == QLI_MODE_SOURCE) {
-    const int nb = (tv.V + 7) / 8;
-    int32_t* cout = a.cand_out + static_cast<int64_t>(t) * a.cb;
-    select_topk(KeySrc{a.bkeys + static_cast<int64_t>(t) * a.nbcap, nb - 1}, nb, a.cb, cout,
-                MapIdentity{}, hist, sh);
-  }
 }
 
 // ---------------------------------------------------------------------------
 // consumer_prep: sorted unique visible incoming block ids per token
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kSelThreads) void consumer_prep_kernel(KArgs a) {
+constexpr int kPrepThreads = 1024;
+
+__global__ __launch_bounds__(kPrepThreads) void consumer_prep_kernel(KArgs a) {
   __shared__ int32_t v[QLI_MAX_CAND_BLOCKS];
   __shared__ uint32_t sh[64];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
-  const TokView tv = token_view(a, t, tid == 0);
-  const int nblocks = (tv.V + 7) / 8;
+  const int b = request_of(a, t);
+  const ReqView r = request_view(a, b, tid == 0);
+  const int V = (t >= r.q0 && t < r.q1)
+                    ? visible(a, r.S - (r.q1 - r.q0) + (t - r.q0), r.L) : 0;
+  const int nblocks = (V + 7) / 8;
   const int cbi = a.cb_in;
   int n2 = 64;
   while (n2 < cbi) n2 <<= 1;
   const int32_t* cin = a.cand_in + static_cast<int64_t>(t) * cbi;
-  for (int i = tid; i < n2; i += kSelThreads) {
+  for (int i = tid; i < n2; i += kPrepThreads) {
     int c = i < cbi ? cin[i] : INT32_MAX;
     if (c < 0 || c >= nblocks) c = INT32_MAX;
     v[i] = c;
   }
   __syncthreads();
-  // bitonic sort, ascending
-  for (int size = 2; size <= n2; size <<= 1) {
+  for (int size = 2; size <= n2; size <<= 1) {  // bitonic sort, ascending
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < n2 / 2; i += kSelThreads) {
+      for (int i = tid; i < n2 / 2; i += kPrepThreads) {
         const int lo = 2 * i - (i & (stride - 1));
         const int hi = lo + stride;
         const bool up = (lo & size) == 0;
@@ -513,8 +269,8 @@ __global__ __launch_bounds__(kSelThreads) void consumer_prep_kernel(KArgs a) {
       __syncthreads();
     }
   }
-  // unique compaction (each thread two consecutive entries)
   int32_t* slots = a.slots + static_cast<int64_t>(t) * cbi;
+  int32_t* srow = a.srow + static_cast<int64_t>(t) * cbi;
   const int i0 = 2 * tid;
   bool f[2];
   uint32_t cnt = 0;
@@ -525,11 +281,572 @@ __global__ __launch_bounds__(kSelThreads) void consumer_prep_kernel(KArgs a) {
     cnt += f[e] ? 1u : 0u;
   }
   uint32_t total;
-  uint32_t at = block_exclusive_scan(cnt, &total, sh);
+  uint32_t at = block_exclusive_scan<kPrepThreads>(cnt, &total, sh);
+  bool bad = false;
 #pragma unroll
-  for (int e = 0; e < 2; ++e)
-    if (f[e]) slots[at++] = v[i0 + e];
-  if (tid == 0) a.nslots[t] = static_cast<int32_t>(total);
+  for (int e = 0; e < 2; ++e) {
+    if (!f[e]) continue;
+    const int blk = v[i0 + e];
+    const int pos0 = blk * 8;
+    const int page = page_checked(a, b, pos0 >> a.rlog);
+    if (page < 0) bad = true;
+    slots[at] = blk;
+    srow[at] = page < 0 ? -1 : page * a.R + (pos0 & (a.R - 1));
+    if (at + 1 == total) {
+      // eligible slots: every kept block is full except possibly the last
+      // visible one, which is the largest id and therefore the last slot
+      const int tail = V - pos0;
+      a.ncount[t] = 8 * (static_cast<int>(total) - 1) + (tail < 8 ? tail : 8);
+    }
+    ++at;
+  }
+  if (bad) raise_flag(a, QLI_DEV_BAD_PAGE);
+  if (tid == 0 && total == 0) a.ncount[t] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// plan: groups and their work-unit prefix
+// ---------------------------------------------------------------------------
+constexpr int kPlanThreads = 1024;
+
+// Group starting at token t of request b, if t starts one.
+__device__ __forceinline__ bool group_at(const KArgs& a, int b, const ReqView& r, int t, int G,
+                                         Group& g) {
+  if ((t - r.q0) % G != 0) return false;
+  g.t0 = t;
+  g.ntok = min(G, r.q1 - t);
+  g.b = b;
+  g.L = r.L;
+  const int64_t p0 = r.S - (r.q1 - r.q0) + (t - r.q0);
+  g.p0 = static_cast<int>(p0);
+  if (a.mode == QLI_MODE_CONSUMER) {
+    g.n0 = a.ncount[t];
+    g.nlast = g.n0;
+  } else {
+    g.n0 = visible(a, p0, r.L);
+    g.nlast = visible(a, p0 + g.ntok - 1, r.L);
+  }
+  g.nch = (g.nlast + kChunk - 1) / kChunk;
+  return true;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(KArgs a) {
+  __shared__ uint32_t sh[64];
+  const int tid = threadIdx.x;
+  const int T = a.T;
+  const int G = a.mode == QLI_MODE_CONSUMER ? 1 : kGroupTokens;
+  const int per = (T + kPlanThreads - 1) / kPlanThreads;
+  const int t_lo = min(T, tid * per);
+  const int t_hi = min(T, t_lo + per);
+  uint32_t ng = 0, nu = 0;
+  if (t_lo < t_hi) {
+    int b = request_of(a, t_lo);
+    ReqView r = request_view(a, b, true);
+    for (int t = t_lo; t < t_hi; ++t) {
+      while (t >= r.q1 && b + 1 < a.B) r = request_view(a, ++b, true);
+      if (t < r.q0 || t >= r.q1) continue;
+      Group g;
+      if (group_at(a, b, r, t, G, g)) {
+        ++ng;
+        nu += static_cast<uint32_t>(g.nch * g.ntok);
+      }
+    }
+  }
+  uint32_t tot_g, tot_u;
+  uint32_t gi = block_exclusive_scan<kPlanThreads>(ng, &tot_g, sh);
+  uint32_t ui = block_exclusive_scan<kPlanThreads>(nu, &tot_u, sh);
+  if (t_lo < t_hi) {
+    int b = request_of(a, t_lo);
+    ReqView r = request_view(a, b, false);
+    for (int t = t_lo; t < t_hi; ++t) {
+      while (t >= r.q1 && b + 1 < a.B) r = request_view(a, ++b, false);
+      if (t < r.q0 || t >= r.q1) continue;
+      Group g;
+      if (group_at(a, b, r, t, G, g)) {
+        a.groups[gi] = g;
+        a.ustart[gi] = static_cast<int32_t>(ui);
+        ++gi;
+        ui += static_cast<uint32_t>(g.nch * g.ntok);
+      }
+    }
+  }
+  if (tid == 0) {
+    a.hdr->ngroups = static_cast<int32_t>(tot_g);
+    a.hdr->units = static_cast<int32_t>(tot_u);
+    a.ustart[tot_g] = static_cast<int32_t>(tot_u);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// score: persistent, pipelined
+// ---------------------------------------------------------------------------
+constexpr int kScoreThreads = 256;
+
+// Work-item cursor (wave-uniform).
+struct Cursor {
+  int g, c, unit;
+  bool valid;
+  Group grp;
+};
+
+__device__ __forceinline__ void load_group(const KArgs& a, int g, Cursor& cu) {
+  cu.g = g;
+  cu.grp = a.groups[g];
+  cu.unit = a.ustart[g];
+  cu.c = 0;
+}
+
+__device__ Cursor first_item(const KArgs& a, int ng, int lo, int hi) {
+  Cursor cu;
+  cu.valid = false;
+  if (ng <= 0) return cu;
+  int l = 0, h = ng - 1;
+  while (l < h) {  // last group with ustart <= lo
+    const int m = (l + h + 1) >> 1;
+    if (a.ustart[m] <= lo) l = m;
+    else h = m - 1;
+  }
+  load_group(a, l, cu);
+  const int off = lo - cu.unit;
+  cu.c = (off + cu.grp.ntok - 1) / cu.grp.ntok;
+  while (cu.c >= cu.grp.nch) {
+    if (cu.g + 1 >= ng) return cu;
+    load_group(a, cu.g + 1, cu);
+  }
+  cu.unit += cu.c * cu.grp.ntok;
+  cu.valid = cu.unit < hi;
+  return cu;
+}
+
+__device__ Cursor next_item(const KArgs& a, int ng, Cursor cu, int hi) {
+  if (!cu.valid) return cu;
+  cu.c += 1;
+  cu.unit += cu.grp.ntok;
+  while (cu.c >= cu.grp.nch) {
+    if (cu.g + 1 >= ng) {
+      cu.valid = false;
+      return cu;
+    }
+    load_group(a, cu.g + 1, cu);
+  }
+  cu.valid = cu.unit < hi;
+  return cu;
+}
+
+// Page and first row of the 8 K blocks (8 rows each) this wave stages for
+// an item: block q = 4u + wave of the item's 256 slots; page -1 = none.
+struct Addr {
+  int pg[8];
+  int rw[8];
+};
+
+template <bool CONSUMER>
+__device__ __forceinline__ void stage_addr(const KArgs& a, const Cursor& cu, int wave, Addr& ad,
+                                           bool& bad) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int q = 4 * u + wave;
+    int pg = -1, rw = 0;
+    if (cu.valid) {
+      if (CONSUMER) {
+        const int s = cu.c * 32 + q;
+        if (8 * s < cu.grp.n0) {
+          const int v = a.srow[static_cast<int64_t>(cu.grp.t0) * a.cb_in + s];
+          if (v >= 0) {
+            pg = v >> a.rlog;
+            rw = v & (a.R - 1);
+          }
+        }
+      } else {
+        const int pos0 = cu.c * kChunk + 8 * q;
+        if (pos0 < cu.grp.nlast) {
+          const int page = page_checked(a, cu.grp.b, pos0 >> a.rlog);
+          if (page >= 0) {
+            pg = page;
+            rw = pos0 & (a.R - 1);
+          } else {
+            bad = true;
+          }
+        }
+      }
+    }
+    ad.pg[u] = pg;
+    ad.rw[u] = rw;
+  }
+}
+
+// K rows (8 x 16 B per lane) and the 8 blocks' scales (16 B, lanes 0..7).
+__device__ __forceinline__ void stage_load(const KArgs& a, const Addr& ad, int lane, i32x4 (&kr)[8],
+                                           i32x4& sc) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    i32x4 v = {0, 0, 0, 0};
+    if (ad.pg[u] >= 0) {
+      const int8_t* src = a.k + static_cast<int64_t>(ad.pg[u]) * a.kstride +
+                          static_cast<int64_t>(ad.rw[u] + (lane >> 3)) * 128 + (lane & 7) * 16;
+      v = *reinterpret_cast<const i32x4*>(src);
+    }
+    kr[u] = v;
+  }
+  int pj = ad.pg[0], rj = ad.rw[0];
+#pragma unroll
+  for (int u = 1; u < 8; ++u) {
+    if (lane == u) {
+      pj = ad.pg[u];
+      rj = ad.rw[u];
+    }
+  }
+  i32x4 s = {-1, -1, -1, -1};  // 0xFFFF halves: no K row
+  if (lane < 8 && pj >= 0)
+    s = *reinterpret_cast<const i32x4*>(a.ks + static_cast<int64_t>(pj) * a.sstride +
+                                        static_cast<int64_t>(rj) * 2);
+  sc = s;
+}
+
+__device__ __forceinline__ void stage_store(int8_t* tile, uint16_t* ksc, const i32x4 (&kr)[8],
+                                            const i32x4& sc, int wave, int lane) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int row = 8 * (4 * u + wave) + (lane >> 3);
+    const int col = lane & 7;
+    *reinterpret_cast<i32x4*>(tile + row * 128 + ((col ^ (row & 7)) << 4)) = kr[u];
+  }
+  if (lane < 8) *reinterpret_cast<i32x4*>(ksc + 8 * (4 * lane + wave)) = sc;
+}
+
+// Queries of one token as MFMA A operands, and its fp16 head multipliers.
+// A rows are permuted so that C register i of lane group g in head tile m
+// is head g*(N/2) + 16m + i (see score_kernel).
+template <int NH>
+struct QState {
+  i32x4 qa[NH / 32][4];
+  h2 mh[NH / 4];
+  int tok;
+};
+
+template <int NH>
+__device__ __forceinline__ void load_q(const KArgs& a, int t, int lane, QState<NH>& qs) {
+  constexpr int HALF = NH / 2;
+  const int r = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int m = 0; m < NH / 32; ++m) {
+    const int head = ((r >> 2) & 1) * HALF + 16 * m + 4 * (r >> 3) + (r & 3);
+    const int8_t* qrow = a.q + (static_cast<int64_t>(t) * NH + head) * 128 + 64 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qs.qa[m][s] = *reinterpret_cast<const i32x4*>(qrow + 16 * s);
+  }
+  const uint32_t* wr = reinterpret_cast<const uint32_t*>(a.w + static_cast<int64_t>(t) * NH + g * HALF);
+  const uint32_t* qr = reinterpret_cast<const uint32_t*>(a.qs + static_cast<int64_t>(t) * NH + g * HALF);
+#pragma unroll
+  for (int j = 0; j < HALF / 2; ++j) qs.mh[j] = as_h2(wr[j]) * as_h2(qr[j]);  // fp16 RNE
+  qs.tok = t;
+}
+
+// One (token, 64-slot sub-tile) of the current item: MFMA + epilogue.
+//
+// MFMA operands (v_mfma_i32_32x32x32_i8, 64 lanes): A = queries, lane l
+// supplies row l%32 of a 32-head tile, 16 bytes of the head dimension;
+// B = keys, lane l supplies column l%32 (one position), the same 16 bytes
+// (dim d = 64*(l/32) + 16*step + byte for both, so the reduction pairs
+// q[h,d] with k[j,d]).  C: lane l holds column l%32, rows 8*(i/4) +
+// 4*(l/32) + i%4.  With the A permutation, lanes 0..31 hold heads
+// 0..N/2-1 and lanes 32..63 heads N/2..N-1 of the same 64 positions, and
+// one v_permlane32_swap per register pair leaves each lane L with all N
+// heads of slot s0+L, summed in ascending head order.
+template <int NH, bool CONSUMER>
+__device__ __forceinline__ void score_subtile(const KArgs& a, const QState<NH>& qs,
+                                              const int8_t* tile, const uint16_t* ksc, int sub,
+                                              int t, int s0, int n_i, int lane, const i32x16& seed) {
+  constexpr int MT = NH / 32;
+  constexpr int HALF = NH / 2;
+  i32x16 acc[MT][2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int row = 64 * sub + 32 * n + (lane & 31);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int col = 4 * (lane >> 5) + s;
+      const i32x4 bk = *reinterpret_cast<const i32x4*>(tile + row * 128 + ((col ^ (row & 7)) << 4));
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        acc[m][n] = __builtin_amdgcn_mfma_i32_32x32x32_i8(qs.qa[m][s], bk, s == 0 ? seed : acc[m][n],
+                                                         0, 0, 0);
+    }
+  }
+  // x = fp16(qk/1024), ReLU, p = fp16(x * m), packed two heads per word
+  uint32_t pk[2][HALF / 2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const int32_t a0 = acc[m][n][i], a1 = acc[m][n][i + 1];
+        const h2 x0 = {qk_to_half(a0), qk_to_half(a1)};
+        const h2 x = as_h2(relu_h2(as_u32(x0)));
+        pk[n][(16 * m + i) >> 1] = as_u32(x * qs.mh[(16 * m + i) >> 1]);
+      }
+  const float one = a.one;
+  float sum = 0.0f;
+  uint32_t hi[HALF / 2];
+#pragma unroll
+  for (int j = 0; j < HALF / 2; ++j) {
+    const auto r = __builtin_amdgcn_permlane32_swap(pk[0][j], pk[1][j], false, false);
+    const uint32_t lo = r[0];
+    const h2 pl = as_h2(lo);
+    sum = add_h(sum, pl[0], one);
+    sum = add_h(sum, pl[1], one);
+    hi[j] = r[1];
+  }
+#pragma unroll
+  for (int j = 0; j < HALF / 2; ++j) {
+    const h2 ph = as_h2(hi[j]);
+    sum = add_h(sum, ph[0], one);
+    sum = add_h(sum, ph[1], one);
+  }
+  const int slot = s0 + lane;
+  const uint16_t kb = ksc[64 * sub + lane];
+  uint32_t key = 0;
+  if (slot < n_i && kb != 0xFFFFu) {
+    const float score = sum * static_cast<float>(__builtin_bit_cast(_Float16, kb));
+    key = order_key(score);
+    if (a.dbg) {
+      const int pos = CONSUMER ? a.slots[static_cast<int64_t>(t) * a.cb_in + (slot >> 3)] * 8 + (slot & 7)
+                               : slot;
+      a.dbg[static_cast<int64_t>(t) * a.max_k_len + pos] = score;
+    }
+  }
+  a.keys[static_cast<int64_t>(t) * a.ncap + slot] = key;
+  if (!CONSUMER && a.mode == QLI_MODE_SOURCE) {
+    uint32_t bk = key;
+    bk = max(bk, static_cast<uint32_t>(__shfl_xor(static_cast<int>(bk), 1)));
+    bk = max(bk, static_cast<uint32_t>(__shfl_xor(static_cast<int>(bk), 2)));
+    bk = max(bk, static_cast<uint32_t>(__shfl_xor(static_cast<int>(bk), 4)));
+    if ((lane & 7) == 0 && slot < n_i) a.bkeys[static_cast<int64_t>(t) * a.nbcap + (slot >> 3)] = bk;
+  }
+}
+
+template <int NH, bool CONSUMER>
+__global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(KArgs a) {
+  __shared__ __attribute__((aligned(16))) int8_t tile[2][kChunk * 128];
+  __shared__ __attribute__((aligned(16))) uint16_t ksc[2][kChunk];
+
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int ng = a.hdr->ngroups;
+  const int U = a.hdr->units;
+  const int W = gridDim.x, wg = blockIdx.x;
+  const int lo = static_cast<int>(static_cast<int64_t>(wg) * U / W);
+  const int hi = static_cast<int>(static_cast<int64_t>(wg + 1) * U / W);
+  if (lo >= hi) return;
+
+  i32x16 seed;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) seed[i] = kSeedBits;
+
+  bool bad = false;
+  Cursor cur = first_item(a, ng, lo, hi);
+  Cursor n1 = next_item(a, ng, cur, hi);
+  Cursor n2 = next_item(a, ng, n1, hi);
+  Addr ad0, ad1;
+  stage_addr<CONSUMER>(a, cur, wave, ad0, bad);
+  i32x4 kr[8];
+  i32x4 sc;
+  stage_load(a, ad0, lane, kr, sc);
+  stage_addr<CONSUMER>(a, n1, wave, ad1, bad);
+
+  QState<NH> qs;
+  qs.tok = -1;
+  int buf = 0;
+  while (cur.valid) {
+    stage_store(tile[buf], ksc[buf], kr, sc, wave, lane);
+    stage_load(a, ad1, lane, kr, sc);  // next item, in flight during compute
+    Addr ad2;
+    stage_addr<CONSUMER>(a, n2, wave, ad2, bad);
+    __syncthreads();
+    const Group& gr = cur.grp;
+    const int np = 4 * gr.ntok;
+    for (int q = wave; q < np; q += 4) {
+      const int sub = q / gr.ntok, ti = q - sub * gr.ntok;
+      const int t = gr.t0 + ti;
+      const int n_i = CONSUMER ? gr.n0 : visible(a, static_cast<int64_t>(gr.p0) + ti, gr.L);
+      const int s0 = cur.c * kChunk + 64 * sub;
+      if (s0 >= n_i) continue;
+      if (t != qs.tok) load_q<NH>(a, t, lane, qs);
+      score_subtile<NH, CONSUMER>(a, qs, tile[buf], ksc[buf], sub, t, s0, n_i, lane, seed);
+    }
+    cur = n1;
+    n1 = n2;
+    n2 = next_item(a, ng, n2, hi);
+    ad1 = ad2;
+    buf ^= 1;
+  }
+  if (bad && lane == 0) raise_flag(a, QLI_DEV_BAD_PAGE);
+}
+
+// ---------------------------------------------------------------------------
+// select
+// ---------------------------------------------------------------------------
+// LDS: histogram (2048 bins), scan scratch, and a chunk of up to sel_chunk
+// keys stored with one pad word per 32 (index i at i + i/32) so that both
+// the strided histogram reads and the per-thread contiguous compaction reads
+// are free of bank conflicts.
+constexpr int kSelMaxChunk = 32768;
+constexpr int kSelFixedWords = 2048 + 64 + 8;
+
+__host__ __device__ constexpr int sel_lds_bytes(int chunk) {
+  return (kSelFixedWords + chunk + chunk / 32) * 4;
+}
+
+__device__ __forceinline__ int padded(int i) { return i + (i >> 5); }
+
+// Select the best min(k, #nonzero) of keys[0..n) by (key desc, index asc)
+// and write map(index) for them in ascending index order to out[0..k),
+// -1 after.  pin (or -1) is forced to the top.
+template <int BS, class Map>
+__device__ void select_topk(const uint32_t* keys, int n, int k, int pin, int32_t* out, Map map,
+                            int chunk, uint32_t* lds) {
+  uint32_t* hist = lds;
+  uint32_t* sh = lds + 2048;
+  uint32_t* misc = lds + 2048 + 64;
+  uint32_t* kl = lds + kSelFixedWords;
+  const int tid = threadIdx.x;
+  const int nch = (n + chunk - 1) / chunk;
+  auto load = [&](int ch) {  // coalesced: 16 B per thread per step
+    const int base = ch * chunk;
+    const int len = min(chunk, n - base);
+    for (int i = 4 * tid; i < chunk; i += 4 * BS) {
+      uint32_t v[4];
+      if (i + 3 < len) {
+        const i32x4 x = *reinterpret_cast<const i32x4*>(keys + base + i);
+        v[0] = x[0];
+        v[1] = x[1];
+        v[2] = x[2];
+        v[3] = x[3];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = i + e < len ? keys[base + i + e] : 0u;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kl[padded(i + e)] = base + i + e == pin ? 0xFFFFFFFFu : v[e];
+    }
+    __syncthreads();
+  };
+  if (nch == 1) load(0);
+
+  uint32_t prefix = 0, mask = 0;
+  int krem = k;
+  bool take_all = false;
+  constexpr int BPT = 2048 / BS;  // histogram bins per thread
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const uint32_t nb = pass == 2 ? 1024u : 2048u;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) hist[tid * BPT + j] = 0;
+    __syncthreads();
+    for (int ch = 0; ch < nch; ++ch) {
+      if (nch > 1) load(ch);
+      const int len = min(chunk, n - ch * chunk);
+      for (int i = tid; i < len; i += BS) {
+        const uint32_t key = kl[padded(i)];
+        if (key != 0 && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (nb - 1)], 1u);
+      }
+      if (nch > 1) __syncthreads();
+    }
+    __syncthreads();
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) c += hist[tid * BPT + j];
+    uint32_t total;
+    const uint32_t excl = block_exclusive_scan<BS>(c, &total, sh);
+    if (pass == 0 && total <= static_cast<uint32_t>(k)) {
+      take_all = true;
+      break;
+    }
+    const uint32_t above = total - excl - c;  // keys in higher bins
+    if (above < static_cast<uint32_t>(krem) && above + c >= static_cast<uint32_t>(krem)) {
+      uint32_t cum = above;
+      for (int j = BPT - 1; j >= 0; --j) {
+        const uint32_t h = hist[tid * BPT + j];
+        if (cum + h >= static_cast<uint32_t>(krem)) {
+          misc[0] = static_cast<uint32_t>(tid * BPT + j);
+          misc[1] = cum;
+          break;
+        }
+        cum += h;
+      }
+    }
+    __syncthreads();
+    krem -= static_cast<int>(misc[1]);
+    prefix |= misc[0] << shift;
+    mask |= (nb - 1) << shift;
+    __syncthreads();
+  }
+
+  // ordered compaction: offset = (keys > T before me) + min(need, keys == T before me)
+  const uint32_t thr = take_all ? 0u : prefix;
+  const uint32_t need = take_all ? 0u : static_cast<uint32_t>(krem);
+  const int kpt = chunk / BS;  // keys per thread, contiguous
+  uint32_t run_gt = 0, run_eq = 0;
+  for (int ch = 0; ch < nch; ++ch) {
+    if (nch > 1) load(ch);
+    const int first = tid * kpt;
+    uint32_t gt = 0, eq = 0;
+    for (int e = 0; e < kpt; ++e) {
+      const uint32_t key = kl[padded(first + e)];
+      gt += key > thr ? 1u : 0u;
+      eq += (key == thr && thr != 0) ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan<BS>((gt << 16) | eq, &tot, sh);
+    uint32_t eq_rank = run_eq + (ex & 0xFFFFu);
+    uint32_t at = run_gt + (ex >> 16) + min(need, eq_rank);
+    const int base = ch * chunk + first;
+    for (int e = 0; e < kpt; ++e) {
+      const uint32_t key = kl[padded(first + e)];
+      bool sel = key > thr;
+      if (key == thr && thr != 0) {
+        sel = eq_rank < need;
+        ++eq_rank;
+      }
+      if (sel) out[at++] = map(base + e);
+    }
+    run_gt += tot >> 16;
+    run_eq += tot & 0xFFFFu;
+    if (nch > 1) __syncthreads();
+  }
+  const int count = static_cast<int>(run_gt + min(need, run_eq));
+  for (int i = count + tid; i < k; i += BS) out[i] = -1;
+}
+
+struct MapIdentity {
+  __device__ __forceinline__ int32_t operator()(int i) const { return i; }
+};
+
+struct MapSlots {
+  const int32_t* slots;
+  __device__ __forceinline__ int32_t operator()(int i) const { return slots[i >> 3] * 8 + (i & 7); }
+};
+
+template <int BS>
+__global__ __launch_bounds__(BS) void select_kernel(KArgs a, int chunk) {
+  extern __shared__ uint32_t sel_lds[];
+  const int t = blockIdx.x;
+  if (blockIdx.y == 0) {
+    int32_t* out = a.topk_out + static_cast<int64_t>(t) * a.topk;
+    const uint32_t* keys = a.keys + static_cast<int64_t>(t) * a.ncap;
+    if (a.mode == QLI_MODE_CONSUMER) {
+      select_topk<BS>(keys, a.ncount[t], a.topk, -1, out,
+                      MapSlots{a.slots + static_cast<int64_t>(t) * a.cb_in}, chunk, sel_lds);
+    } else {
+      select_topk<BS>(keys, token_view(a, t).V, a.topk, -1, out, MapIdentity{}, chunk, sel_lds);
+    }
+  } else {
+    const int nb = (token_view(a, t).V + 7) / 8;
+    select_topk<BS>(a.bkeys + static_cast<int64_t>(t) * a.nbcap, nb, a.cb, nb - 1,
+                    a.cand_out + static_cast<int64_t>(t) * a.cb, MapIdentity{}, chunk, sel_lds);
+  }
 }
 
 }  // namespace
@@ -564,6 +881,35 @@ struct Stamp {
     g_pending.push_back({kernel, start, stop});
   }
 };
+
+int g_cu_count[64];
+bool g_lds_attr[64][3];
+
+// Raise a kernel's dynamic LDS limit once per device (needed above 64 KB).
+template <class Kernel>
+bool allow_dynamic_lds(Kernel kernel, int slot, int bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  if (!g_lds_attr[dev][slot]) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+      return false;
+    g_lds_attr[dev][slot] = true;
+  }
+  return true;
+}
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!g_cu_count[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    g_cu_count[dev] = n;
+  }
+  return g_cu_count[dev];
+}
 }  // namespace
 
 int timing_enable(int on) {
@@ -599,18 +945,20 @@ int timing_read(double* ms, int64_t* count, int reset) {
 int launch(const qli_params* p, const WsLayout& w, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   KArgs a;
+  a.one = 1.0f;
   a.mode = p->mode;
   a.ratio = p->ratio;
+  a.rshift = p->ratio == 2 ? 1 : 0;
   a.B = p->batch;
   a.T = p->num_tokens;
   a.topk = p->topk;
   a.cb = p->cand_blocks;
   a.cb_in = p->cand_in_blocks;
   a.R = p->page_rows;
+  a.rlog = p->page_rows == 128 ? 7 : 6;
   a.bt_stride = p->bt_stride;
   a.num_pages = p->num_pages;
   a.max_k_len = p->max_k_len;
-  a.nchunks = static_cast<int>(w.ncap / kChunk);
   a.kstride = p->k_page_stride;
   a.sstride = p->s_page_stride;
   a.ncap = w.ncap;
@@ -630,31 +978,51 @@ int launch(const qli_params* p, const WsLayout& w, void* stream) {
   a.dbg = p->dbg_scores;
   a.status = p->status_out;
   char* ws = static_cast<char*>(p->workspace);
+  const bool consumer = p->mode == QLI_MODE_CONSUMER;
+  const bool source = p->mode == QLI_MODE_SOURCE;
   a.keys = reinterpret_cast<uint32_t*>(ws + w.keys_off);
-  a.bkeys = p->mode == QLI_MODE_SOURCE ? reinterpret_cast<uint32_t*>(ws + w.bkeys_off) : nullptr;
-  a.slots = p->mode == QLI_MODE_CONSUMER ? reinterpret_cast<int32_t*>(ws + w.slots_off) : nullptr;
-  a.nslots = p->mode == QLI_MODE_CONSUMER ? reinterpret_cast<int32_t*>(ws + w.nslots_off) : nullptr;
+  a.bkeys = source ? reinterpret_cast<uint32_t*>(ws + w.bkeys_off) : nullptr;
+  a.hdr = reinterpret_cast<PlanHdr*>(ws + w.plan_off);
+  a.groups = reinterpret_cast<Group*>(ws + w.groups_off);
+  a.ustart = reinterpret_cast<int32_t*>(ws + w.ustart_off);
+  a.slots = consumer ? reinterpret_cast<int32_t*>(ws + w.slots_off) : nullptr;
+  a.srow = consumer ? reinterpret_cast<int32_t*>(ws + w.srow_off) : nullptr;
+  a.ncount = consumer ? reinterpret_cast<int32_t*>(ws + w.ncount_off) : nullptr;
 
   const unsigned T = static_cast<unsigned>(p->num_tokens);
-  const bool consumer = p->mode == QLI_MODE_CONSUMER;
   if (consumer) {
     Stamp s(QLI_KERNEL_CONSUMER_PREP, st);
-    consumer_prep_kernel<<<T, kSelThreads, 0, st>>>(a);
+    consumer_prep_kernel<<<T, kPrepThreads, 0, st>>>(a);
   }
-  if (a.nchunks > 0) {
+  {
+    Stamp s(QLI_KERNEL_PLAN, st);
+    plan_kernel<<<1, kPlanThreads, 0, st>>>(a);
+  }
+  if (w.ncap > 0) {
     Stamp s(QLI_KERNEL_SCORE, st);
-    const unsigned grid = T * static_cast<unsigned>(a.nchunks);
+    const unsigned grid = static_cast<unsigned>(2 * cu_count());
     if (p->num_heads == 64) {
-      if (consumer) score_kernel<64, true><<<grid, 256, 0, st>>>(a);
-      else score_kernel<64, false><<<grid, 256, 0, st>>>(a);
+      if (consumer) score_kernel<64, true><<<grid, kScoreThreads, 0, st>>>(a);
+      else score_kernel<64, false><<<grid, kScoreThreads, 0, st>>>(a);
     } else {
-      if (consumer) score_kernel<32, true><<<grid, 256, 0, st>>>(a);
-      else score_kernel<32, false><<<grid, 256, 0, st>>>(a);
+      if (consumer) score_kernel<32, true><<<grid, kScoreThreads, 0, st>>>(a);
+      else score_kernel<32, false><<<grid, kScoreThreads, 0, st>>>(a);
     }
   }
   {
     Stamp s(QLI_KERNEL_SELECT, st);
-    select_kernel<<<T, kSelThreads, 0, st>>>(a);
+    const int64_t longest = w.ncap > w.nbcap ? w.ncap : w.nbcap;
+    const dim3 grid(T, source ? 2 : 1);
+    if (longest <= 4096) {
+      if (!allow_dynamic_lds(select_kernel<256>, 0, sel_lds_bytes(4096))) return QLI_ERR_HIP;
+      select_kernel<256><<<grid, 256, sel_lds_bytes(4096), st>>>(a, 4096);
+    } else if (longest <= 16384) {
+      if (!allow_dynamic_lds(select_kernel<512>, 1, sel_lds_bytes(16384))) return QLI_ERR_HIP;
+      select_kernel<512><<<grid, 512, sel_lds_bytes(16384), st>>>(a, 16384);
+    } else {
+      if (!allow_dynamic_lds(select_kernel<1024>, 2, sel_lds_bytes(kSelMaxChunk))) return QLI_ERR_HIP;
+      select_kernel<1024><<<grid, 1024, sel_lds_bytes(kSelMaxChunk), st>>>(a, kSelMaxChunk);
+    }
   }
   return hipGetLastError() == hipSuccess ? QLI_OK : QLI_ERR_HIP;
 }

@@ -112,6 +112,8 @@ def test_valid_params_pass(lib):
     ("k_page_stride", 131072 + 8, Q.QLI_ERR_INVALID_ARG),
     ("k_page_stride", 64 * 128 - 16, Q.QLI_ERR_INVALID_ARG),
     ("s_page_stride", 131073, Q.QLI_ERR_INVALID_ARG),
+    ("s_page_stride", 131072 + 8, Q.QLI_ERR_INVALID_ARG),
+    ("k_scale", 0x7F0000000000 + 4096 * 4 + 2, Q.QLI_ERR_INVALID_ARG),
     ("reserved0", 1, Q.QLI_ERR_INVALID_ARG),
     ("q", None, Q.QLI_ERR_INVALID_ARG),
     ("k_cache", None, Q.QLI_ERR_INVALID_ARG),
@@ -155,11 +157,12 @@ def test_zero_tokens_is_a_noop(lib):
 
 def test_workspace_bytes(lib):
     p = base_params(mode=2, ratio=2, T=4)
-    # keys: 4 tokens * roundup(128, 256) slots * 4 B; block keys: 4 * 64 * 4 B
-    assert Q.qli_workspace_bytes(p) == 4 * 256 * 4 + 4 * 64 * 4
+    # keys: 4 tokens * roundup(128, 256) slots * 4 B; block keys: 4 * 64 * 4 B;
+    # plan header 256 B, groups 4 * 32 B, group prefix 5 * 4 B (each 256-B aligned)
+    assert Q.qli_workspace_bytes(p) == 4 * 256 * 4 + 4 * 64 * 4 + 256 + 256 + 256
     p = base_params(mode=3, ratio=2, T=4)
-    # keys: 4 * 64*8 * 4; slots: 4 * 64 * 4; nslots: 4 * 4 -> 256-B aligned
-    assert Q.qli_workspace_bytes(p) == 4 * 512 * 4 + 4 * 64 * 4 + 256
+    # keys: 4 * 64*8 * 4; plan 3 * 256; slots + page rows: 2 * 4 * 64 * 4; counts 256
+    assert Q.qli_workspace_bytes(p) == 4 * 512 * 4 + 3 * 256 + 2 * 4 * 64 * 4 + 256
     p.head_dim = 3
     assert Q.qli_workspace_bytes(p) == 0
 
