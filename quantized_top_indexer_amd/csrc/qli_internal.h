@@ -11,8 +11,8 @@ namespace qli {
 // Carve-up of the caller's workspace.
 //   keys   [T, ncap]    u32 order-preserving score keys by slot (0 = not eligible)
 //   bkeys  [T, nbcap]   u32 block-max keys (source mode)
-//   plan   header (group count, work units), groups [T] x 32 B, ustart [T+1]:
-//          the work list the plan kernel builds for the persistent score kernel
+//   plan   header (group counts, work units), groups [2][T] x 32 B, ustart [2][T+1]:
+//          the two work lists the plan kernel builds for the persistent score kernel
 //   slots  [T, cand_in_blocks] sorted unique visible incoming block ids (consumer)
 //   srow   [T, cand_in_blocks] page*page_rows + row of each slot block (consumer)
 //   ncount [T]          eligible positions per token (consumer)
@@ -46,16 +46,18 @@ inline WsLayout ws_layout(const qli_params* p) {
   w.keys_off = off;
   off = align256(off + T * static_cast<size_t>(w.ncap) * 4);
   if (p->mode == QLI_MODE_SOURCE) {
-    w.nbcap = ((static_cast<int64_t>(p->max_k_len) + 7) / 8 + 63) / 64 * 64;
+    // covers every block id below max_k_len and every 8-slot group below ncap
+    const int64_t nb = (static_cast<int64_t>(p->max_k_len) + 7) / 8;
+    w.nbcap = ((nb > w.ncap / 8 ? nb : w.ncap / 8) + 63) / 64 * 64;
     w.bkeys_off = off;
     off = align256(off + T * static_cast<size_t>(w.nbcap) * 4);
   }
   w.plan_off = off;
   off = align256(off + 256);
   w.groups_off = off;
-  off = align256(off + T * 32);
+  off = align256(off + 2 * T * 32);
   w.ustart_off = off;
-  off = align256(off + (T + 1) * 4);
+  off = align256(off + 2 * (T + 1) * 4);
   if (p->mode == QLI_MODE_CONSUMER) {
     const size_t cb = static_cast<size_t>(p->cand_in_blocks);
     w.slots_off = off;

@@ -45,10 +45,13 @@ typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef int16_t s2 __attribute__((ext_vector_type(2)));
 
+// Work list: list 0 holds multi groups (4 consecutive query tokens of one
+// request sharing every K tile: the leading full quadruples of each request
+// in plain/source mode), list 1 single-token groups (every other token).
 struct PlanHdr {
-  int32_t ngroups;
-  int32_t units;
-  int32_t pad[62];
+  int32_t ngroups[2];
+  int32_t units[2];
+  int32_t pad[60];
 };
 
 // A group: ntok consecutive query tokens t0.. of request b sharing K tiles.
@@ -82,8 +85,8 @@ struct KArgs {
   uint32_t* keys;
   uint32_t* bkeys;
   PlanHdr* hdr;
-  Group* groups;
-  int32_t* ustart;
+  Group* groups;    // [2][T]
+  int32_t* ustart;  // [2][T + 1]
   int32_t* slots;
   int32_t* srow;
   int32_t* ncount;
@@ -309,12 +312,21 @@ __global__ __launch_bounds__(kPrepThreads) void consumer_prep_kernel(KArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kPlanThreads = 1024;
 
-// Group starting at token t of request b, if t starts one.
-__device__ __forceinline__ bool group_at(const KArgs& a, int b, const ReqView& r, int t, int G,
-                                         Group& g) {
-  if ((t - r.q0) % G != 0) return false;
+// 0: token t belongs to a multi group it does not start; 1: starts a multi
+// group; 2: forms a single group.
+__device__ __forceinline__ int group_kind(const KArgs& a, const ReqView& r, int t) {
+  if (a.mode == QLI_MODE_CONSUMER) return 2;
+  const int i = t - r.q0;
+  const int full = (r.q1 - r.q0) / kGroupTokens * kGroupTokens;
+  if (i < full) return i % kGroupTokens == 0 ? 1 : 0;
+  return 2;
+}
+
+__device__ __forceinline__ Group make_group(const KArgs& a, int b, const ReqView& r, int t,
+                                            int ntok) {
+  Group g;
   g.t0 = t;
-  g.ntok = min(G, r.q1 - t);
+  g.ntok = ntok;
   g.b = b;
   g.L = r.L;
   const int64_t p0 = r.S - (r.q1 - r.q0) + (t - r.q0);
@@ -324,56 +336,60 @@ __device__ __forceinline__ bool group_at(const KArgs& a, int b, const ReqView& r
     g.nlast = g.n0;
   } else {
     g.n0 = visible(a, p0, r.L);
-    g.nlast = visible(a, p0 + g.ntok - 1, r.L);
+    g.nlast = visible(a, p0 + ntok - 1, r.L);
   }
   g.nch = (g.nlast + kChunk - 1) / kChunk;
-  return true;
+  return g;
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KArgs a) {
   __shared__ uint32_t sh[64];
   const int tid = threadIdx.x;
   const int T = a.T;
-  const int G = a.mode == QLI_MODE_CONSUMER ? 1 : kGroupTokens;
   const int per = (T + kPlanThreads - 1) / kPlanThreads;
   const int t_lo = min(T, tid * per);
   const int t_hi = min(T, t_lo + per);
-  uint32_t ng = 0, nu = 0;
+  uint32_t ng[2] = {0, 0}, nu[2] = {0, 0};
   if (t_lo < t_hi) {
     int b = request_of(a, t_lo);
     ReqView r = request_view(a, b, true);
     for (int t = t_lo; t < t_hi; ++t) {
       while (t >= r.q1 && b + 1 < a.B) r = request_view(a, ++b, true);
       if (t < r.q0 || t >= r.q1) continue;
-      Group g;
-      if (group_at(a, b, r, t, G, g)) {
-        ++ng;
-        nu += static_cast<uint32_t>(g.nch * g.ntok);
-      }
+      const int kind = group_kind(a, r, t);
+      if (kind == 0) continue;
+      const Group g = make_group(a, b, r, t, kind == 1 ? kGroupTokens : 1);
+      ++ng[kind - 1];
+      nu[kind - 1] += static_cast<uint32_t>(g.nch * g.ntok);
     }
   }
-  uint32_t tot_g, tot_u;
-  uint32_t gi = block_exclusive_scan<kPlanThreads>(ng, &tot_g, sh);
-  uint32_t ui = block_exclusive_scan<kPlanThreads>(nu, &tot_u, sh);
+  uint32_t tot_g[2], tot_u[2], gi[2], ui[2];
+  for (int l = 0; l < 2; ++l) {
+    gi[l] = block_exclusive_scan<kPlanThreads>(ng[l], &tot_g[l], sh);
+    ui[l] = block_exclusive_scan<kPlanThreads>(nu[l], &tot_u[l], sh);
+  }
   if (t_lo < t_hi) {
     int b = request_of(a, t_lo);
     ReqView r = request_view(a, b, false);
     for (int t = t_lo; t < t_hi; ++t) {
       while (t >= r.q1 && b + 1 < a.B) r = request_view(a, ++b, false);
       if (t < r.q0 || t >= r.q1) continue;
-      Group g;
-      if (group_at(a, b, r, t, G, g)) {
-        a.groups[gi] = g;
-        a.ustart[gi] = static_cast<int32_t>(ui);
-        ++gi;
-        ui += static_cast<uint32_t>(g.nch * g.ntok);
-      }
+      const int kind = group_kind(a, r, t);
+      if (kind == 0) continue;
+      const int l = kind - 1;
+      const Group g = make_group(a, b, r, t, kind == 1 ? kGroupTokens : 1);
+      a.groups[l * T + gi[l]] = g;
+      a.ustart[l * (T + 1) + gi[l]] = static_cast<int32_t>(ui[l]);
+      ++gi[l];
+      ui[l] += static_cast<uint32_t>(g.nch * g.ntok);
     }
   }
   if (tid == 0) {
-    a.hdr->ngroups = static_cast<int32_t>(tot_g);
-    a.hdr->units = static_cast<int32_t>(tot_u);
-    a.ustart[tot_g] = static_cast<int32_t>(tot_u);
+    for (int l = 0; l < 2; ++l) {
+      a.hdr->ngroups[l] = static_cast<int32_t>(tot_g[l]);
+      a.hdr->units[l] = static_cast<int32_t>(tot_u[l]);
+      a.ustart[l * (T + 1) + tot_g[l]] = static_cast<int32_t>(tot_u[l]);
+    }
   }
 }
 
@@ -382,164 +398,222 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kScoreThreads = 256;
 
-// Work-item cursor (wave-uniform).
+// Work-item cursor over one list (wave-uniform).
 struct Cursor {
   int g, c, unit;
   bool valid;
   Group grp;
 };
 
-__device__ __forceinline__ void load_group(const KArgs& a, int g, Cursor& cu) {
+struct ListView {
+  const Group* groups;
+  const int32_t* ustart;
+  int ng;
+};
+
+__device__ __forceinline__ void load_group(const ListView& L, int g, Cursor& cu) {
   cu.g = g;
-  cu.grp = a.groups[g];
-  cu.unit = a.ustart[g];
+  cu.grp = L.groups[g];
+  cu.unit = L.ustart[g];
   cu.c = 0;
 }
 
-__device__ Cursor first_item(const KArgs& a, int ng, int lo, int hi) {
+__device__ Cursor first_item(const ListView& L, int lo, int hi) {
   Cursor cu;
   cu.valid = false;
-  if (ng <= 0) return cu;
-  int l = 0, h = ng - 1;
+  cu.g = 0;
+  cu.c = 0;
+  cu.unit = 0;
+  cu.grp = Group{0, 1, 0, 0, 0, 0, 0, 0};
+  if (L.ng <= 0) return cu;
+  int l = 0, h = L.ng - 1;
   while (l < h) {  // last group with ustart <= lo
     const int m = (l + h + 1) >> 1;
-    if (a.ustart[m] <= lo) l = m;
+    if (L.ustart[m] <= lo) l = m;
     else h = m - 1;
   }
-  load_group(a, l, cu);
+  load_group(L, l, cu);
   const int off = lo - cu.unit;
   cu.c = (off + cu.grp.ntok - 1) / cu.grp.ntok;
   while (cu.c >= cu.grp.nch) {
-    if (cu.g + 1 >= ng) return cu;
-    load_group(a, cu.g + 1, cu);
+    if (cu.g + 1 >= L.ng) return cu;
+    load_group(L, cu.g + 1, cu);
   }
   cu.unit += cu.c * cu.grp.ntok;
   cu.valid = cu.unit < hi;
   return cu;
 }
 
-__device__ Cursor next_item(const KArgs& a, int ng, Cursor cu, int hi) {
+__device__ Cursor next_item(const ListView& L, Cursor cu, int hi) {
   if (!cu.valid) return cu;
   cu.c += 1;
   cu.unit += cu.grp.ntok;
   while (cu.c >= cu.grp.nch) {
-    if (cu.g + 1 >= ng) {
+    if (cu.g + 1 >= L.ng) {
       cu.valid = false;
       return cu;
     }
-    load_group(a, cu.g + 1, cu);
+    load_group(L, cu.g + 1, cu);
   }
   cu.valid = cu.unit < hi;
   return cu;
 }
 
-// Page and first row of the 8 K blocks (8 rows each) this wave stages for
-// an item: block q = 4u + wave of the item's 256 slots; page -1 = none.
+// Staging of one work item.  The block lookups run ahead of the K loads and
+// every global load is issued unconditionally (a block without K rows reads
+// page 0, row 0, which always exists, and is masked through its scale), so
+// that the number of loads in flight is fixed and known to the compiler.
+//
+// Lane j < 8 of wave w owns block q = 4j + w of the item's 32 blocks of 8
+// slots.  stage_addr only issues the lookup of that block's page (dense:
+// block-table entry; consumer: the prepared page row of the slot block) and
+// records what it needs to check it; resolve() uses the loaded value later.
 struct Addr {
-  int pg[8];
-  int rw[8];
+  int raw;   // loaded block-table entry / prepared page row
+  int meta;  // bit 31: block wanted; bit 30: table index in range; low bits: row in page
 };
 
 template <bool CONSUMER>
-__device__ __forceinline__ void stage_addr(const KArgs& a, const Cursor& cu, int wave, Addr& ad,
-                                           bool& bad) {
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int q = 4 * u + wave;
-    int pg = -1, rw = 0;
-    if (cu.valid) {
-      if (CONSUMER) {
-        const int s = cu.c * 32 + q;
-        if (8 * s < cu.grp.n0) {
-          const int v = a.srow[static_cast<int64_t>(cu.grp.t0) * a.cb_in + s];
-          if (v >= 0) {
-            pg = v >> a.rlog;
-            rw = v & (a.R - 1);
-          }
-        }
-      } else {
-        const int pos0 = cu.c * kChunk + 8 * q;
-        if (pos0 < cu.grp.nlast) {
-          const int page = page_checked(a, cu.grp.b, pos0 >> a.rlog);
-          if (page >= 0) {
-            pg = page;
-            rw = pos0 & (a.R - 1);
-          } else {
-            bad = true;
-          }
-        }
-      }
-    }
-    ad.pg[u] = pg;
-    ad.rw[u] = rw;
+__device__ __forceinline__ void stage_addr(const KArgs& a, const Group& gr, int c, bool valid,
+                                           int wave, int lane, Addr& ad) {
+  const int j = lane & 7;
+  const int q = 4 * j + wave;
+  if (CONSUMER) {
+    const int s = c * 32 + q;
+    ad.raw = a.srow[static_cast<int64_t>(gr.t0) * a.cb_in + min(s, a.cb_in - 1)];
+    ad.meta = (valid && 8 * s < gr.n0) ? (3 << 30) : 0;
+  } else {
+    const int pos0 = c * kChunk + 8 * q;
+    const int idx = pos0 >> a.rlog;
+    ad.raw = a.bt[static_cast<int64_t>(gr.b) * a.bt_stride + min(idx, a.bt_stride - 1)];
+    ad.meta = ((valid && pos0 < gr.nlast) ? (1 << 31) : 0) | (idx < a.bt_stride ? (1 << 30) : 0) |
+              (pos0 & (a.R - 1));
   }
 }
 
-// K rows (8 x 16 B per lane) and the 8 blocks' scales (16 B, lanes 0..7).
-__device__ __forceinline__ void stage_load(const KArgs& a, const Addr& ad, int lane, i32x4 (&kr)[8],
+// page * page_rows + first row of the lane's block, or -1 (no K rows).
+template <bool CONSUMER>
+__device__ __forceinline__ int resolve(const KArgs& a, const Addr& ad, bool& bad) {
+  const bool want = ad.meta < 0;  // bit 31
+  if (CONSUMER) return want && ad.raw >= 0 ? ad.raw : -1;
+  const bool ok = want && (ad.meta & (1 << 30)) && ad.raw >= 0 && ad.raw < a.num_pages;
+  bad |= want && !ok;
+  return ok ? ad.raw * a.R + (ad.meta & (a.R - 1)) : -1;
+}
+
+// K rows of the wave's 8 blocks (8 x 16 B per lane) and their scales
+// (16 B per block; lanes j and j + 8k all read block j's run), given the
+// resolved block rows v (lane j holds block j's row, or -1).
+__device__ __forceinline__ void stage_load(const KArgs& a, int v, int lane, i32x4 (&kr)[8],
                                            i32x4& sc) {
+  const int lane_off = (lane >> 3) * 128 + (lane & 7) * 16;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    i32x4 v = {0, 0, 0, 0};
-    if (ad.pg[u] >= 0) {
-      const int8_t* src = a.k + static_cast<int64_t>(ad.pg[u]) * a.kstride +
-                          static_cast<int64_t>(ad.rw[u] + (lane >> 3)) * 128 + (lane & 7) * 16;
-      v = *reinterpret_cast<const i32x4*>(src);
-    }
-    kr[u] = v;
+    const int vu = __builtin_amdgcn_readlane(v, u);
+    const int row = vu < 0 ? 0 : vu;
+    const int8_t* src = a.k + static_cast<int64_t>(row >> a.rlog) * a.kstride +
+                        static_cast<int64_t>(row & (a.R - 1)) * 128 + lane_off;
+    kr[u] = *reinterpret_cast<const i32x4*>(src);
   }
-  int pj = ad.pg[0], rj = ad.rw[0];
-#pragma unroll
-  for (int u = 1; u < 8; ++u) {
-    if (lane == u) {
-      pj = ad.pg[u];
-      rj = ad.rw[u];
-    }
-  }
-  i32x4 s = {-1, -1, -1, -1};  // 0xFFFF halves: no K row
-  if (lane < 8 && pj >= 0)
-    s = *reinterpret_cast<const i32x4*>(a.ks + static_cast<int64_t>(pj) * a.sstride +
-                                        static_cast<int64_t>(rj) * 2);
-  sc = s;
+  const int row = v < 0 ? 0 : v;
+  sc = *reinterpret_cast<const i32x4*>(a.ks + static_cast<int64_t>(row >> a.rlog) * a.sstride +
+                                       static_cast<int64_t>(row & (a.R - 1)) * 2);
 }
 
+// Into LDS: K tile rows with the XOR swizzle, scales of valid blocks (0xFFFF
+// halves mark a block without K rows).
 __device__ __forceinline__ void stage_store(int8_t* tile, uint16_t* ksc, const i32x4 (&kr)[8],
-                                            const i32x4& sc, int wave, int lane) {
+                                            const i32x4& sc, int v, int wave, int lane) {
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int row = 8 * (4 * u + wave) + (lane >> 3);
     const int col = lane & 7;
     *reinterpret_cast<i32x4*>(tile + row * 128 + ((col ^ (row & 7)) << 4)) = kr[u];
   }
-  if (lane < 8) *reinterpret_cast<i32x4*>(ksc + 8 * (4 * lane + wave)) = sc;
+  if (lane < 8) {
+    const i32x4 none = {-1, -1, -1, -1};
+    *reinterpret_cast<i32x4*>(ksc + 8 * (4 * lane + wave)) = v < 0 ? none : sc;
+  }
 }
 
 // Queries of one token as MFMA A operands, and its fp16 head multipliers.
-// A rows are permuted so that C register i of lane group g in head tile m
-// is head g*(N/2) + 16m + i (see score_kernel).
-template <int NH>
+// A rows are permuted so that the C register i of lane group g of a head
+// tile is the head that the epilogue needs there (see score_subtile):
+//   SPLIT (32-head tiles scored one after the other): tile m, group g,
+//     register i -> head 32m + 16g + i;
+//   otherwise (all tiles interleaved): tile m, group g, register i ->
+//     head g*N/2 + 16m + i.
+template <int NH, bool SPLIT>
 struct QState {
   i32x4 qa[NH / 32][4];
-  h2 mh[NH / 4];
+  h2 mh[NH / 4];  // pairs of multipliers in the order the epilogue consumes them
   int tok;
 };
 
-template <int NH>
-__device__ __forceinline__ void load_q(const KArgs& a, int t, int lane, QState<NH>& qs) {
+template <int NH, bool SPLIT>
+__device__ __forceinline__ void load_q(const KArgs& a, int t, int lane, QState<NH, SPLIT>& qs) {
   constexpr int HALF = NH / 2;
   const int r = lane & 31, g = lane >> 5;
 #pragma unroll
   for (int m = 0; m < NH / 32; ++m) {
-    const int head = ((r >> 2) & 1) * HALF + 16 * m + 4 * (r >> 3) + (r & 3);
+    const int head = SPLIT ? 32 * m + ((r >> 2) & 1) * 16 + 4 * (r >> 3) + (r & 3)
+                           : ((r >> 2) & 1) * HALF + 16 * m + 4 * (r >> 3) + (r & 3);
     const int8_t* qrow = a.q + (static_cast<int64_t>(t) * NH + head) * 128 + 64 * g;
 #pragma unroll
     for (int s = 0; s < 4; ++s) qs.qa[m][s] = *reinterpret_cast<const i32x4*>(qrow + 16 * s);
   }
-  const uint32_t* wr = reinterpret_cast<const uint32_t*>(a.w + static_cast<int64_t>(t) * NH + g * HALF);
-  const uint32_t* qr = reinterpret_cast<const uint32_t*>(a.qs + static_cast<int64_t>(t) * NH + g * HALF);
+  const uint32_t* wr = reinterpret_cast<const uint32_t*>(a.w + static_cast<int64_t>(t) * NH);
+  const uint32_t* qr = reinterpret_cast<const uint32_t*>(a.qs + static_cast<int64_t>(t) * NH);
 #pragma unroll
-  for (int j = 0; j < HALF / 2; ++j) qs.mh[j] = as_h2(wr[j]) * as_h2(qr[j]);  // fp16 RNE
+  for (int j = 0; j < HALF / 2; ++j) {
+    // pair j covers heads (SPLIT) 32*(j/8) + 16g + 2*(j%8) or (else) g*N/2 + 2j
+    const int h0 = SPLIT ? 32 * (j >> 3) + 16 * g + 2 * (j & 7) : g * HALF + 2 * j;
+    qs.mh[j] = as_h2(wr[h0 >> 1]) * as_h2(qr[h0 >> 1]);  // fp16 RNE
+  }
   qs.tok = t;
+}
+
+// Query sources for score_subtile: fragments and multipliers in registers
+// (multi groups: every wave may hold another token), or in LDS (single
+// groups: the four waves share the token).
+template <int NH, bool SPLIT>
+struct QRegs {
+  const QState<NH, SPLIT>& q;
+  __device__ __forceinline__ i32x4 frag(int m, int s, int) const { return q.qa[m][s]; }
+  __device__ __forceinline__ h2 mul(int j, int) const { return q.mh[j]; }
+};
+
+// LDS layout: frag[m][s][lane] (16 B each), mul[j][group] (packed pairs).
+template <int NH>
+struct QLds {
+  const i32x4* fr;
+  const uint32_t* ml;
+  __device__ __forceinline__ i32x4 frag(int m, int s, int lane) const {
+    return fr[(m * 4 + s) * 64 + lane];
+  }
+  __device__ __forceinline__ h2 mul(int j, int lane) const { return as_h2(ml[j * 2 + (lane >> 5)]); }
+};
+
+// Fill QLds for token t (SPLIT layout), all threads of the workgroup.
+template <int NH>
+__device__ __forceinline__ void load_q_lds(const KArgs& a, int t, i32x4* fr, uint32_t* ml) {
+  constexpr int MT = NH / 32;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int e = tid; e < MT * 256; e += kScoreThreads) {
+    const int m = e >> 8, s = (e >> 6) & 3, l = e & 63;
+    const int r = l & 31, g = l >> 5;
+    const int head = 32 * m + ((r >> 2) & 1) * 16 + 4 * (r >> 3) + (r & 3);
+    fr[e] = *reinterpret_cast<const i32x4*>(a.q + (static_cast<int64_t>(t) * NH + head) * 128 + 64 * g +
+                                            16 * s);
+  }
+  if (tid < NH / 2) {  // pair j = tid >> 1 of group g = tid & 1: heads 32*(j/8) + 16g + 2*(j%8)
+    const int j = tid >> 1, g = tid & 1;
+    const int h0 = 32 * (j >> 3) + 16 * g + 2 * (j & 7);
+    const uint32_t* wr = reinterpret_cast<const uint32_t*>(a.w + static_cast<int64_t>(t) * NH);
+    const uint32_t* qr = reinterpret_cast<const uint32_t*>(a.qs + static_cast<int64_t>(t) * NH);
+    ml[tid] = as_u32(as_h2(wr[h0 >> 1]) * as_h2(qr[h0 >> 1]));  // fp16 RNE
+  }
 }
 
 // One (token, 64-slot sub-tile) of the current item: MFMA + epilogue.
@@ -553,116 +627,114 @@ __device__ __forceinline__ void load_q(const KArgs& a, int t, int lane, QState<N
 // 0..N/2-1 and lanes 32..63 heads N/2..N-1 of the same 64 positions, and
 // one v_permlane32_swap per register pair leaves each lane L with all N
 // heads of slot s0+L, summed in ascending head order.
-template <int NH, bool CONSUMER>
-__device__ __forceinline__ void score_subtile(const KArgs& a, const QState<NH>& qs,
+//
+// Every store is unconditional (slots past n_i receive key 0, block maxima
+// are written by all 8 lanes of a block), so the memory operations of a
+// sub-tile are fixed.
+template <int NH, int MODE, bool DBG, bool SPLIT, class QSrc>
+__device__ __forceinline__ void score_subtile(const KArgs& a, const QSrc& qs,
                                               const int8_t* tile, const uint16_t* ksc, int sub,
                                               int t, int s0, int n_i, int lane, const i32x16& seed) {
   constexpr int MT = NH / 32;
-  constexpr int HALF = NH / 2;
-  i32x16 acc[MT][2];
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int row = 64 * sub + 32 * n + (lane & 31);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int col = 4 * (lane >> 5) + s;
-      const i32x4 bk = *reinterpret_cast<const i32x4*>(tile + row * 128 + ((col ^ (row & 7)) << 4));
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-        acc[m][n] = __builtin_amdgcn_mfma_i32_32x32x32_i8(qs.qa[m][s], bk, s == 0 ? seed : acc[m][n],
-                                                         0, 0, 0);
-    }
-  }
-  // x = fp16(qk/1024), ReLU, p = fp16(x * m), packed two heads per word
-  uint32_t pk[2][HALF / 2];
-#pragma unroll
-  for (int n = 0; n < 2; ++n)
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const int32_t a0 = acc[m][n][i], a1 = acc[m][n][i + 1];
-        const h2 x0 = {qk_to_half(a0), qk_to_half(a1)};
-        const h2 x = as_h2(relu_h2(as_u32(x0)));
-        pk[n][(16 * m + i) >> 1] = as_u32(x * qs.mh[(16 * m + i) >> 1]);
-      }
+  constexpr int PASSES = SPLIT ? MT : 1;     // head tiles scored one after the other
+  constexpr int TPP = SPLIT ? 1 : MT;        // head tiles per pass
+  constexpr int PAIRS = 8 * TPP;             // packed pairs per lane group per pass
   const float one = a.one;
   float sum = 0.0f;
-  uint32_t hi[HALF / 2];
+  // the passes stay a loop: overlapping them would keep two head tiles of
+  // accumulators live
+#pragma unroll 1
+  for (int ps = 0; ps < PASSES; ++ps) {
+    i32x16 acc[TPP][2];
 #pragma unroll
-  for (int j = 0; j < HALF / 2; ++j) {
-    const auto r = __builtin_amdgcn_permlane32_swap(pk[0][j], pk[1][j], false, false);
-    const uint32_t lo = r[0];
-    const h2 pl = as_h2(lo);
-    sum = add_h(sum, pl[0], one);
-    sum = add_h(sum, pl[1], one);
-    hi[j] = r[1];
-  }
+    for (int n = 0; n < 2; ++n) {
+      const int row = 64 * sub + 32 * n + (lane & 31);
 #pragma unroll
-  for (int j = 0; j < HALF / 2; ++j) {
-    const h2 ph = as_h2(hi[j]);
-    sum = add_h(sum, ph[0], one);
-    sum = add_h(sum, ph[1], one);
+      for (int s = 0; s < 4; ++s) {
+        const int col = 4 * (lane >> 5) + s;
+        const i32x4 bk = *reinterpret_cast<const i32x4*>(tile + row * 128 + ((col ^ (row & 7)) << 4));
+#pragma unroll
+        for (int m = 0; m < TPP; ++m)
+          acc[m][n] = __builtin_amdgcn_mfma_i32_32x32x32_i8(qs.frag(ps * TPP + m, s, lane), bk,
+                                                           s == 0 ? seed : acc[m][n], 0, 0, 0);
+      }
+    }
+    // x = fp16(qk/1024), ReLU, p = fp16(x * m), packed two heads per word
+    uint32_t pk[2][PAIRS];
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int m = 0; m < TPP; ++m)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const int32_t a0 = acc[m][n][i], a1 = acc[m][n][i + 1];
+          const h2 x0 = {qk_to_half(a0), qk_to_half(a1)};
+          const h2 x = as_h2(relu_h2(as_u32(x0)));
+          pk[n][(16 * m + i) >> 1] = as_u32(x * qs.mul(ps * PAIRS + ((16 * m + i) >> 1), lane));
+        }
+    uint32_t hi[PAIRS];
+#pragma unroll
+    for (int j = 0; j < PAIRS; ++j) {
+      const auto r = __builtin_amdgcn_permlane32_swap(pk[0][j], pk[1][j], false, false);
+      const uint32_t lo = r[0];
+      const h2 pl = as_h2(lo);
+      sum = add_h(sum, pl[0], one);
+      sum = add_h(sum, pl[1], one);
+      hi[j] = r[1];
+    }
+#pragma unroll
+    for (int j = 0; j < PAIRS; ++j) {
+      const h2 ph = as_h2(hi[j]);
+      sum = add_h(sum, ph[0], one);
+      sum = add_h(sum, ph[1], one);
+    }
   }
   const int slot = s0 + lane;
   const uint16_t kb = ksc[64 * sub + lane];
-  uint32_t key = 0;
-  if (slot < n_i && kb != 0xFFFFu) {
-    const float score = sum * static_cast<float>(__builtin_bit_cast(_Float16, kb));
-    key = order_key(score);
-    if (a.dbg) {
-      const int pos = CONSUMER ? a.slots[static_cast<int64_t>(t) * a.cb_in + (slot >> 3)] * 8 + (slot & 7)
-                               : slot;
-      a.dbg[static_cast<int64_t>(t) * a.max_k_len + pos] = score;
-    }
+  const bool valid = slot < n_i && kb != 0xFFFFu;
+  const float score = sum * static_cast<float>(__builtin_bit_cast(_Float16, kb));
+  const uint32_t key = valid ? order_key(score) : 0u;
+  if (DBG && valid) {
+    const int pos = MODE == QLI_MODE_CONSUMER
+                        ? a.slots[static_cast<int64_t>(t) * a.cb_in + (slot >> 3)] * 8 + (slot & 7)
+                        : slot;
+    a.dbg[static_cast<int64_t>(t) * a.max_k_len + pos] = score;
   }
   a.keys[static_cast<int64_t>(t) * a.ncap + slot] = key;
-  if (!CONSUMER && a.mode == QLI_MODE_SOURCE) {
+  if (MODE == QLI_MODE_SOURCE) {
     uint32_t bk = key;
     bk = max(bk, static_cast<uint32_t>(__shfl_xor(static_cast<int>(bk), 1)));
     bk = max(bk, static_cast<uint32_t>(__shfl_xor(static_cast<int>(bk), 2)));
     bk = max(bk, static_cast<uint32_t>(__shfl_xor(static_cast<int>(bk), 4)));
-    if ((lane & 7) == 0 && slot < n_i) a.bkeys[static_cast<int64_t>(t) * a.nbcap + (slot >> 3)] = bk;
+    a.bkeys[static_cast<int64_t>(t) * a.nbcap + (slot >> 3)] = bk;
   }
 }
 
-template <int NH, bool CONSUMER>
-__global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(KArgs a) {
-  __shared__ __attribute__((aligned(16))) int8_t tile[2][kChunk * 128];
-  __shared__ __attribute__((aligned(16))) uint16_t ksc[2][kChunk];
-
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int lane = threadIdx.x & 63;
-  const int ng = a.hdr->ngroups;
-  const int U = a.hdr->units;
-  const int W = gridDim.x, wg = blockIdx.x;
-  const int lo = static_cast<int>(static_cast<int64_t>(wg) * U / W);
-  const int hi = static_cast<int>(static_cast<int64_t>(wg + 1) * U / W);
-  if (lo >= hi) return;
-
-  i32x16 seed;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) seed[i] = kSeedBits;
-
-  bool bad = false;
-  Cursor cur = first_item(a, ng, lo, hi);
-  Cursor n1 = next_item(a, ng, cur, hi);
-  Cursor n2 = next_item(a, ng, n1, hi);
-  Addr ad0, ad1;
-  stage_addr<CONSUMER>(a, cur, wave, ad0, bad);
+// Multi groups (prefill shapes): each item is 256 slots for up to 4 tokens;
+// wave w scores the (token, sub-tile) pairs w, w+4, ... so that with 4
+// tokens every wave keeps one token's queries.  One item of K in flight.
+template <int NH, int MODE, bool DBG>
+__device__ void run_multi(const KArgs& a, const ListView& L, int lo, int hi, int8_t (*tile)[kChunk * 128],
+                          uint16_t (*ksc)[kChunk], int wave, int lane, const i32x16& seed, bool& bad) {
+  constexpr bool CONSUMER = MODE == QLI_MODE_CONSUMER;
+  Cursor cur = first_item(L, lo, hi);
+  Cursor n1 = next_item(L, cur, hi);
+  Cursor n2 = next_item(L, n1, hi);
+  Addr ad;
+  stage_addr<CONSUMER>(a, cur.grp, cur.c, cur.valid, wave, lane, ad);
   i32x4 kr[8];
   i32x4 sc;
-  stage_load(a, ad0, lane, kr, sc);
-  stage_addr<CONSUMER>(a, n1, wave, ad1, bad);
-
-  QState<NH> qs;
+  int v = resolve<CONSUMER>(a, ad, bad);
+  stage_addr<CONSUMER>(a, n1.grp, n1.c, n1.valid, wave, lane, ad);
+  stage_load(a, v, lane, kr, sc);
+  QState<NH, false> qs;
   qs.tok = -1;
   int buf = 0;
   while (cur.valid) {
-    stage_store(tile[buf], ksc[buf], kr, sc, wave, lane);
-    stage_load(a, ad1, lane, kr, sc);  // next item, in flight during compute
-    Addr ad2;
-    stage_addr<CONSUMER>(a, n2, wave, ad2, bad);
+    stage_store(tile[buf], ksc[buf], kr, sc, v, wave, lane);
+    v = resolve<CONSUMER>(a, ad, bad);
+    stage_addr<CONSUMER>(a, n2.grp, n2.c, n2.valid, wave, lane, ad);
+    stage_load(a, v, lane, kr, sc);
     __syncthreads();
     const Group& gr = cur.grp;
     const int np = 4 * gr.ntok;
@@ -672,16 +744,110 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(KArgs a) {
       const int n_i = CONSUMER ? gr.n0 : visible(a, static_cast<int64_t>(gr.p0) + ti, gr.L);
       const int s0 = cur.c * kChunk + 64 * sub;
       if (s0 >= n_i) continue;
-      if (t != qs.tok) load_q<NH>(a, t, lane, qs);
-      score_subtile<NH, CONSUMER>(a, qs, tile[buf], ksc[buf], sub, t, s0, n_i, lane, seed);
+      if (t != qs.tok) load_q<NH, false>(a, t, lane, qs);
+      score_subtile<NH, MODE, DBG, false>(a, QRegs<NH, false>{qs}, tile[buf], ksc[buf], sub, t, s0,
+                                          n_i, lane, seed);
     }
     cur = n1;
     n1 = n2;
-    n2 = next_item(a, ng, n2, hi);
-    ad1 = ad2;
+    n2 = next_item(L, n2, hi);
     buf ^= 1;
   }
-  if (bad && lane == 0) raise_flag(a, QLI_DEV_BAD_PAGE);
+}
+
+// Single-token groups (decode shapes): wave w scores sub-tile w of every
+// item.  Per token segment the queries are loaded once; inside a segment the
+// loop body has a fixed set of memory operations and keeps two items of K in
+// flight (register sets A and B alternate; the body is unrolled twice).
+// Each step resolves the block rows looked up one step earlier, issues the
+// next lookup, then the K loads: with in-order memory counters a lookup is
+// always older than the K loads that must stay in flight.
+template <int NH, int MODE, bool DBG>
+__device__ void run_single(const KArgs& a, const ListView& L, int lo, int hi,
+                           int8_t (*tile)[kChunk * 128], uint16_t (*ksc)[kChunk], i32x4* qfr,
+                           uint32_t* qml, int wave, int lane, const i32x16& seed, bool& bad) {
+  constexpr bool CONSUMER = MODE == QLI_MODE_CONSUMER;
+  Cursor cu = first_item(L, lo, hi);
+  int buf = 0;
+  const QLds<NH> qs{qfr, qml};
+  while (cu.valid) {
+    const Group gr = cu.grp;
+    const int c0 = cu.c;
+    const int c_end = min(gr.nch, c0 + (hi - cu.unit));
+    const int t = gr.t0;
+    const int n = gr.n0;
+    __syncthreads();  // the previous segment's last item is scored
+    load_q_lds<NH>(a, t, qfr, qml);
+    Addr ad;
+    i32x4 krA[8], krB[8];
+    i32x4 scA, scB;
+    stage_addr<CONSUMER>(a, gr, c0, true, wave, lane, ad);
+    int vA = resolve<CONSUMER>(a, ad, bad);
+    stage_addr<CONSUMER>(a, gr, c0 + 1, c0 + 1 < c_end, wave, lane, ad);
+    stage_load(a, vA, lane, krA, scA);
+    int vB = resolve<CONSUMER>(a, ad, bad);
+    stage_addr<CONSUMER>(a, gr, c0 + 2, c0 + 2 < c_end, wave, lane, ad);
+    stage_load(a, vB, lane, krB, scB);
+    __syncthreads();  // queries in LDS
+    for (int c = c0; c < c_end; c += 2) {
+      stage_store(tile[buf], ksc[buf], krA, scA, vA, wave, lane);
+      vA = resolve<CONSUMER>(a, ad, bad);
+      stage_addr<CONSUMER>(a, gr, c + 3, c + 3 < c_end, wave, lane, ad);
+      stage_load(a, vA, lane, krA, scA);
+      __syncthreads();
+      score_subtile<NH, MODE, DBG, true>(a, qs, tile[buf], ksc[buf], wave, t, c * kChunk + 64 * wave,
+                                         n, lane, seed);
+      buf ^= 1;
+      if (c + 1 >= c_end) break;
+      stage_store(tile[buf], ksc[buf], krB, scB, vB, wave, lane);
+      vB = resolve<CONSUMER>(a, ad, bad);
+      stage_addr<CONSUMER>(a, gr, c + 4, c + 4 < c_end, wave, lane, ad);
+      stage_load(a, vB, lane, krB, scB);
+      __syncthreads();
+      score_subtile<NH, MODE, DBG, true>(a, qs, tile[buf], ksc[buf], wave, t,
+                                         (c + 1) * kChunk + 64 * wave, n, lane, seed);
+      buf ^= 1;
+    }
+    // next token segment
+    cu.c = c_end - 1;
+    cu.unit += (c_end - 1 - c0);
+    cu = next_item(L, cu, hi);
+  }
+}
+
+// The workgroups split between the two lists in proportion to their units.
+template <int NH, int MODE, bool DBG>
+__global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(KArgs a) {
+  __shared__ __attribute__((aligned(16))) int8_t tile[2][kChunk * 128];
+  __shared__ __attribute__((aligned(16))) uint16_t ksc[2][kChunk];
+  __shared__ __attribute__((aligned(16))) i32x4 qfr[NH / 32 * 256];
+  __shared__ uint32_t qml[NH / 2];
+
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int Um = a.hdr->units[0], Us = a.hdr->units[1];
+  const int W = gridDim.x;
+  int Wm = 0;
+  if (Um > 0 && Us == 0) Wm = W;
+  else if (Um > 0) Wm = min(W - 1, max(1, static_cast<int>(static_cast<int64_t>(W) * Um / (Um + Us))));
+  const bool multi = static_cast<int>(blockIdx.x) < Wm;
+  const int wg = multi ? blockIdx.x : blockIdx.x - Wm;
+  const int nw = multi ? Wm : W - Wm;
+  const int U = multi ? Um : Us;
+  const int lo = static_cast<int>(static_cast<int64_t>(wg) * U / nw);
+  const int hi = static_cast<int>(static_cast<int64_t>(wg + 1) * U / nw);
+  if (lo >= hi) return;
+  const int l = multi ? 0 : 1;
+  const ListView L{a.groups + static_cast<int64_t>(l) * a.T,
+                   a.ustart + static_cast<int64_t>(l) * (a.T + 1), a.hdr->ngroups[l]};
+
+  i32x16 seed;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) seed[i] = kSeedBits;
+  bool bad = false;
+  if (multi) run_multi<NH, MODE, DBG>(a, L, lo, hi, tile, ksc, wave, lane, seed, bad);
+  else run_single<NH, MODE, DBG>(a, L, lo, hi, tile, ksc, qfr, qml, wave, lane, seed, bad);
+  if (bad) raise_flag(a, QLI_DEV_BAD_PAGE);
 }
 
 // ---------------------------------------------------------------------------
@@ -942,6 +1108,24 @@ int timing_read(double* ms, int64_t* count, int reset) {
   return rc;
 }
 
+template <int NH, int MODE>
+void launch_score_dbg(bool dbg, unsigned grid, hipStream_t st, const KArgs& a) {
+  if (dbg) score_kernel<NH, MODE, true><<<grid, kScoreThreads, 0, st>>>(a);
+  else score_kernel<NH, MODE, false><<<grid, kScoreThreads, 0, st>>>(a);
+}
+
+template <int NH>
+void launch_score_mode(int mode, bool dbg, unsigned grid, hipStream_t st, const KArgs& a) {
+  if (mode == QLI_MODE_PLAIN) launch_score_dbg<NH, QLI_MODE_PLAIN>(dbg, grid, st, a);
+  else if (mode == QLI_MODE_SOURCE) launch_score_dbg<NH, QLI_MODE_SOURCE>(dbg, grid, st, a);
+  else launch_score_dbg<NH, QLI_MODE_CONSUMER>(dbg, grid, st, a);
+}
+
+void launch_score(int heads, int mode, bool dbg, unsigned grid, hipStream_t st, const KArgs& a) {
+  if (heads == 64) launch_score_mode<64>(mode, dbg, grid, st, a);
+  else launch_score_mode<32>(mode, dbg, grid, st, a);
+}
+
 int launch(const qli_params* p, const WsLayout& w, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   KArgs a;
@@ -983,7 +1167,7 @@ int launch(const qli_params* p, const WsLayout& w, void* stream) {
   a.keys = reinterpret_cast<uint32_t*>(ws + w.keys_off);
   a.bkeys = source ? reinterpret_cast<uint32_t*>(ws + w.bkeys_off) : nullptr;
   a.hdr = reinterpret_cast<PlanHdr*>(ws + w.plan_off);
-  a.groups = reinterpret_cast<Group*>(ws + w.groups_off);
+  a.groups = reinterpret_cast<Group*>(ws + w.groups_off);  // [2][T]
   a.ustart = reinterpret_cast<int32_t*>(ws + w.ustart_off);
   a.slots = consumer ? reinterpret_cast<int32_t*>(ws + w.slots_off) : nullptr;
   a.srow = consumer ? reinterpret_cast<int32_t*>(ws + w.srow_off) : nullptr;
@@ -1001,13 +1185,7 @@ int launch(const qli_params* p, const WsLayout& w, void* stream) {
   if (w.ncap > 0) {
     Stamp s(QLI_KERNEL_SCORE, st);
     const unsigned grid = static_cast<unsigned>(2 * cu_count());
-    if (p->num_heads == 64) {
-      if (consumer) score_kernel<64, true><<<grid, kScoreThreads, 0, st>>>(a);
-      else score_kernel<64, false><<<grid, kScoreThreads, 0, st>>>(a);
-    } else {
-      if (consumer) score_kernel<32, true><<<grid, kScoreThreads, 0, st>>>(a);
-      else score_kernel<32, false><<<grid, kScoreThreads, 0, st>>>(a);
-    }
+    launch_score(p->num_heads, p->mode, p->dbg_scores != nullptr, grid, st, a);
   }
   {
     Stamp s(QLI_KERNEL_SELECT, st);

@@ -158,7 +158,7 @@ def test_zero_tokens_is_a_noop(lib):
 def test_workspace_bytes(lib):
     p = base_params(mode=2, ratio=2, T=4)
     # keys: 4 tokens * roundup(128, 256) slots * 4 B; block keys: 4 * 64 * 4 B;
-    # plan header 256 B, groups 4 * 32 B, group prefix 5 * 4 B (each 256-B aligned)
+    # plan header 256 B, groups 2 * 4 * 32 B, group prefixes 2 * 5 * 4 B (each 256-B aligned)
     assert Q.qli_workspace_bytes(p) == 4 * 256 * 4 + 4 * 64 * 4 + 256 + 256 + 256
     p = base_params(mode=3, ratio=2, T=4)
     # keys: 4 * 64*8 * 4; plan 3 * 256; slots + page rows: 2 * 4 * 64 * 4; counts 256
