@@ -62,6 +62,12 @@ def load_library(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"QLI HIP library not built ({path}); run __graft_entry__.build()")
+    # torch bundles its own HIP runtime, whose file name differs from the
+    # soname this library asks for: if this library were loaded first, the
+    # process would end up with two runtimes, and torch's streams and device
+    # memory would be foreign to ours.  Loading torch first makes the dynamic
+    # linker resolve our dependency to torch's (already loaded) runtime.
+    import torch  # noqa: F401
     L = C.CDLL(path)
     L.qli_abi_version.restype = C.c_int
     L.qli_validate.restype = C.c_int

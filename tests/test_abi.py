@@ -176,3 +176,14 @@ def test_status_strings(lib):
 def test_output_shapes():
     assert Q.output_shapes(7, 16, 64, Q.QLI_MODE_SOURCE) == ((7, 1, 16), (7, 1, 64))
     assert Q.output_shapes(7, 16, 64, Q.QLI_MODE_CONSUMER) == ((7, 1, 16), None)
+
+
+def test_one_hip_runtime_per_process():
+    """Loading the library before torch must not bring a second HIP runtime
+    into the process (torch's streams would be foreign to it)."""
+    code = ("import quantized_top_indexer_amd as Q; Q.load_library(); import torch; "
+            "m = open('/proc/self/maps').read().splitlines(); "
+            "print(len({l.split()[-1] for l in m if 'libamdhip64' in l}))")
+    out = subprocess.run(["python", "-c", code], capture_output=True, text=True, check=True,
+                         cwd=ROOT).stdout.strip()
+    assert out == "1"
