@@ -73,10 +73,11 @@ enum qli_status {
   QLI_ERR_HIP = 5          /* a kernel launch failed */
 };
 
-/* Candidate modes ("三种候选模式共享同一个原生算子": three modes, one op). */
+/* Candidate modes: all three run through the same operator (guide, section
+   on candidate modes). */
 enum qli_mode { QLI_MODE_PLAIN = 1, QLI_MODE_SOURCE = 2, QLI_MODE_CONSUMER = 3 };
 
-/* INT8 is quantisation mode 2 in the guide's numbering ("量化模式 2"). */
+/* INT8 is quantisation mode 2 in the guide's numbering of quantisation modes. */
 #define QLI_QUANT_INT8 2
 
 /* Bits the kernels OR into *status_out when a device-side metadata value is

@@ -53,7 +53,7 @@ int qli_abi_version(void) { return QLI_ABI_VERSION; }
 int qli_validate(const qli_params* p) {
   int rc = check_scalars(p);
   if (rc != QLI_OK) return rc;
-  // residual: absent at ratio 1 ("残差张量必须不存在"), needed at ratio 2
+  // residual: the guide requires it to be absent at ratio 1; ratio 2 needs it
   if (p->ratio == 1 && p->seq_mod) return QLI_ERR_INVALID_ARG;
   if (p->mode == QLI_MODE_CONSUMER && !p->cand_in) return QLI_ERR_NO_SOURCE;
   if (p->num_tokens == 0) return QLI_OK;

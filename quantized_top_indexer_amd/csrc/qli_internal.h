@@ -13,6 +13,8 @@ namespace qli {
 //   bkeys  [T, nbcap]   u32 block-max keys (source mode)
 //   plan   header (group counts, work units), groups [2][T] x 32 B, ustart [2][T+1]:
 //          the two work lists the plan kernel builds for the persistent score kernel
+//   wgs    [kMaxScoreWGs] x 64 B: each score workgroup's list, first item and range
+//   tokv   [T]          visible compressed count per token (written by the plan)
 //   slots  [T, cand_in_blocks] sorted unique visible incoming block ids (consumer)
 //   srow   [T, cand_in_blocks] page*page_rows + row of each slot block (consumer)
 //   ncount [T]          eligible positions per token (consumer)
@@ -24,6 +26,8 @@ struct WsLayout {
   size_t plan_off = 0;
   size_t groups_off = 0;
   size_t ustart_off = 0;
+  size_t wgs_off = 0;
+  size_t tokv_off = 0;
   size_t slots_off = 0;
   size_t srow_off = 0;
   size_t ncount_off = 0;
@@ -32,6 +36,8 @@ struct WsLayout {
 
 constexpr int kChunk = 256;       // score slots per work item
 constexpr int kGroupTokens = 4;   // tokens of one request sharing a K tile (plain/source)
+constexpr int kMaxScoreWGs = 2048;  // score grid cap (two workgroups per CU)
+constexpr int kWgStartBytes = 64;
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -58,6 +64,10 @@ inline WsLayout ws_layout(const qli_params* p) {
   off = align256(off + 2 * T * 32);
   w.ustart_off = off;
   off = align256(off + 2 * (T + 1) * 4);
+  w.wgs_off = off;
+  off = align256(off + static_cast<size_t>(kMaxScoreWGs) * kWgStartBytes);
+  w.tokv_off = off;
+  off = align256(off + T * 4);
   if (p->mode == QLI_MODE_CONSUMER) {
     const size_t cb = static_cast<size_t>(p->cand_in_blocks);
     w.slots_off = off;

@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -64,9 +65,21 @@ struct Group {
   int32_t t0, ntok, b, nch, p0, L, n0, nlast;
 };
 
+// Where score workgroup w starts (written by the plan kernel, read with one
+// load so that the first K loads follow after a single dependent lookup):
+// its list, that list's group count, the group g holding its first item,
+// the item index c in g and its first work unit, and the end hi of its unit
+// range.  g < 0: the workgroup has no work.
+struct WgStart {
+  Group grp;
+  int32_t list, ng, g, c, unit, hi, pad[2];
+};
+static_assert(sizeof(WgStart) == kWgStartBytes, "WgStart size");
+
 struct KArgs {
   float one;  // 1.0f
   int mode, ratio, rshift, B, T, topk, cb, cb_in, R, rlog, bt_stride, num_pages, max_k_len;
+  int score_grid;
   int64_t kstride, sstride, ncap, nbcap;
   const int8_t* q;
   const uint16_t* qs;
@@ -87,20 +100,32 @@ struct KArgs {
   PlanHdr* hdr;
   Group* groups;    // [2][T]
   int32_t* ustart;  // [2][T + 1]
+  WgStart* wgs;     // [score_grid]
   int32_t* slots;
   int32_t* srow;
   int32_t* ncount;
+  int32_t* tokv;    // [T] visible compressed count per token (plan)
 };
 
 __device__ __forceinline__ void raise_flag(const KArgs& a, uint32_t bit) {
   if (a.status) atomicOr(a.status, bit);
 }
 
-__device__ __forceinline__ int request_of(const KArgs& a, int t) {
-  int lo = 0, hi = a.B - 1;
+// Request metadata, read from global memory or from an LDS copy.
+struct Meta {
+  const int32_t* qsl;
+  const int32_t* klen;
+  const int32_t* smod;  // null at ratio 1
+};
+
+__device__ __forceinline__ Meta global_meta(const KArgs& a) { return Meta{a.qsl, a.klen, a.smod}; }
+
+// request of token t: the last b with qsl[b] <= t
+__device__ __forceinline__ int request_of(const Meta& m, int B, int t) {
+  int lo = 0, hi = B - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (a.qsl[mid] <= t) lo = mid;
+    if (m.qsl[mid] <= t) lo = mid;
     else hi = mid - 1;
   }
   return lo;
@@ -115,12 +140,12 @@ struct ReqView {
   int64_t S;
 };
 
-__device__ __forceinline__ ReqView request_view(const KArgs& a, int b, bool report) {
+__device__ __forceinline__ ReqView request_view(const KArgs& a, const Meta& m, int b, bool report) {
   ReqView v;
-  v.q0 = a.qsl[b];
-  v.q1 = a.qsl[b + 1];
-  int L = a.klen[b];
-  const int s = a.smod ? a.smod[b] : 0;
+  v.q0 = m.qsl[b];
+  v.q1 = m.qsl[b + 1];
+  int L = m.klen[b];
+  const int s = m.smod ? m.smod[b] : 0;
   if (L < 0 || L > a.max_k_len) {
     if (report) raise_flag(a, QLI_DEV_BAD_LENGTH);
     L = 0;
@@ -140,19 +165,6 @@ __device__ __forceinline__ ReqView request_view(const KArgs& a, int b, bool repo
 __device__ __forceinline__ int visible(const KArgs& a, int64_t p, int L) {
   const int64_t V = (p + 1) >> a.rshift;
   return static_cast<int>(V < L ? V : L);
-}
-
-struct TokView {
-  int b;
-  int V;
-};
-
-__device__ __forceinline__ TokView token_view(const KArgs& a, int t) {
-  const int b = request_of(a, t);
-  const ReqView r = request_view(a, b, false);
-  if (t < r.q0 || t >= r.q1) return {b, 0};
-  const int64_t p = r.S - (r.q1 - r.q0) + (t - r.q0);
-  return {b, visible(a, p, r.L)};
 }
 
 __device__ __forceinline__ int page_checked(const KArgs& a, int b, int idx) {
@@ -200,28 +212,56 @@ __device__ __forceinline__ float add_h(float s, _Float16 h, float one) {
   return __builtin_fmaf(static_cast<float>(h), one, s);
 }
 
-template <int BS>
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t o = static_cast<uint32_t>(__shfl_up(static_cast<int>(v), d));
-    if (lane >= d) v += o;
-  }
+// Cross-lane steps on DPP (no LDS traffic).  dpp_or0: lanes without a
+// source (shifted out of their row, or rows outside row_mask) read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_or0(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROW_MASK, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_all(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+
+// Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 within each
+// row of 16, then the row totals through the row-15 and row-31 broadcasts.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+  v += dpp_or0<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_or0<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_or0<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_or0<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_or0<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_or0<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
 
-// Exclusive prefix of v over a workgroup of BS threads (BS/64 <= 16 waves);
-// *total receives the sum.  Uses sh[0..47].
+// op over the 64 lanes (result in every lane): butterflies within each row,
+// then the four row values.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_allreduce(uint32_t v, Op op) {
+  v = op(v, dpp_all<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = op(v, dpp_all<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = op(v, dpp_all<0x124>(v));  // row_ror:4
+  v = op(v, dpp_all<0x128>(v));  // row_ror:8
+  const uint32_t r0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0));
+  const uint32_t r1 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16));
+  const uint32_t r2 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 32));
+  const uint32_t r3 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48));
+  return op(op(r0, r1), op(r2, r3));
+}
+
 template <int BS>
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total, uint32_t* sh) {
   constexpr int NW = BS / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t inc = wave_inclusive_scan<BS>(v, lane);
+  const uint32_t inc = wave_inclusive_scan(v);
   if (lane == 63) sh[wave] = inc;
   __syncthreads();
   if (wave == 0) {
     const uint32_t x = lane < NW ? sh[lane] : 0u;
-    const uint32_t xi = wave_inclusive_scan<BS>(x, lane);
+    const uint32_t xi = wave_inclusive_scan(x);
     if (lane < NW) sh[16 + lane] = xi - x;
     if (lane == NW - 1) sh[32] = xi;
   }
@@ -240,10 +280,18 @@ constexpr int kPrepThreads = 1024;
 __global__ __launch_bounds__(kPrepThreads) void consumer_prep_kernel(KArgs a) {
   __shared__ int32_t v[QLI_MAX_CAND_BLOCKS];
   __shared__ uint32_t sh[64];
+  __shared__ int s_req;
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
-  const int b = request_of(a, t);
-  const ReqView r = request_view(a, b, tid == 0);
+  // the request holding t, found by all threads at once (one round of
+  // loads instead of a dependent binary search)
+  if (tid == 0) s_req = 0;
+  __syncthreads();
+  for (int i = tid; i < a.B; i += kPrepThreads)
+    if (a.qsl[i] <= t && t < a.qsl[i + 1]) s_req = i;
+  __syncthreads();
+  const int b = s_req;
+  const ReqView r = request_view(a, global_meta(a), b, tid == 0);
   const int V = (t >= r.q0 && t < r.q1)
                     ? visible(a, r.S - (r.q1 - r.q0) + (t - r.q0), r.L) : 0;
   const int nblocks = (V + 7) / 8;
@@ -342,19 +390,75 @@ __device__ __forceinline__ Group make_group(const KArgs& a, int b, const ReqView
   return g;
 }
 
+// Score workgroups of the multi list: a share of the grid in proportion to
+// its work units (at least one for each non-empty list).
+__device__ __forceinline__ int multi_workgroups(int W, int Um, int Us) {
+  if (Um <= 0) return 0;
+  if (Us <= 0) return W;
+  return min(W - 1, max(1, static_cast<int>(static_cast<int64_t>(W) * Um / (Um + Us))));
+}
+
+// Workgroup w of a list with U units over nw workgroups owns the items whose
+// first unit lies in [floor(w*U/nw), floor((w+1)*U/nw)).  Every group of a
+// list has the same token count NT, so group g (units [a, a + nch*NT))
+// holds the first item of exactly the workgroups whose range starts in
+// (a - NT, a + (nch - 1)*NT]; the thread that writes g writes their entries.
+__device__ __forceinline__ int64_t ceil_div(int64_t x, int64_t y) {
+  return x <= 0 ? 0 : (x + y - 1) / y;
+}
+
+__device__ void write_starts(const KArgs& a, int list, int ng, int gidx, const Group& g, int unit0,
+                             int NT, int nw, int U, int base) {
+  const int64_t e = unit0 + static_cast<int64_t>(g.nch - 1) * NT;
+  const int w0 = static_cast<int>(ceil_div((static_cast<int64_t>(unit0) - NT + 1) * nw, U));
+  const int w1 = static_cast<int>(min(static_cast<int64_t>(nw), ceil_div((e + 1) * nw, U)));
+  for (int w = w0; w < w1; ++w) {
+    const int lo = static_cast<int>(static_cast<int64_t>(w) * U / nw);
+    const int c = static_cast<int>(ceil_div(lo - unit0, NT));
+    WgStart st;
+    st.grp = g;
+    st.list = list;
+    st.ng = ng;
+    st.g = gidx;
+    st.c = c;
+    st.unit = unit0 + c * NT;
+    st.hi = static_cast<int>(static_cast<int64_t>(w + 1) * U / nw);
+    st.pad[0] = st.pad[1] = 0;
+    a.wgs[base + w] = st;
+  }
+}
+
+constexpr int kPlanLdsRequests = 4096;  // metadata of up to this many requests is staged in LDS
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KArgs a) {
   __shared__ uint32_t sh[64];
+  __shared__ int32_t s_meta[3 * kPlanLdsRequests + 1];
   const int tid = threadIdx.x;
   const int T = a.T;
+  Meta m = global_meta(a);
+  if (a.B <= kPlanLdsRequests) {
+    int32_t* q = s_meta;
+    int32_t* l = s_meta + kPlanLdsRequests + 1;
+    int32_t* r = s_meta + 2 * kPlanLdsRequests + 1;
+    for (int i = tid; i <= a.B; i += kPlanThreads) {
+      q[i] = a.qsl[i];
+      if (i < a.B) {
+        l[i] = a.klen[i];
+        if (a.smod) r[i] = a.smod[i];
+      }
+    }
+    __syncthreads();
+    m = Meta{q, l, a.smod ? r : nullptr};
+  }
   const int per = (T + kPlanThreads - 1) / kPlanThreads;
   const int t_lo = min(T, tid * per);
   const int t_hi = min(T, t_lo + per);
   uint32_t ng[2] = {0, 0}, nu[2] = {0, 0};
   if (t_lo < t_hi) {
-    int b = request_of(a, t_lo);
-    ReqView r = request_view(a, b, true);
+    int b = request_of(m, a.B, t_lo);
+    ReqView r = request_view(a, m, b, true);
     for (int t = t_lo; t < t_hi; ++t) {
-      while (t >= r.q1 && b + 1 < a.B) r = request_view(a, ++b, true);
+      while (t >= r.q1 && b + 1 < a.B) r = request_view(a, m, ++b, true);
       if (t < r.q0 || t >= r.q1) continue;
       const int kind = group_kind(a, r, t);
       if (kind == 0) continue;
@@ -363,23 +467,41 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KArgs a) {
       nu[kind - 1] += static_cast<uint32_t>(g.nch * g.ntok);
     }
   }
+  // every start entry begins as "no work" (the scans' barriers order these
+  // stores before the ones below); workgroups whose range starts past the
+  // last item of their list keep it
+  for (int w = tid; w < a.score_grid; w += kPlanThreads) {
+    WgStart st = {};
+    st.g = -1;
+    a.wgs[w] = st;
+  }
   uint32_t tot_g[2], tot_u[2], gi[2], ui[2];
   for (int l = 0; l < 2; ++l) {
     gi[l] = block_exclusive_scan<kPlanThreads>(ng[l], &tot_g[l], sh);
     ui[l] = block_exclusive_scan<kPlanThreads>(nu[l], &tot_u[l], sh);
   }
+  const int W = a.score_grid;
+  const int Wm = multi_workgroups(W, static_cast<int>(tot_u[0]), static_cast<int>(tot_u[1]));
+  const int nw[2] = {Wm, W - Wm};
+  const int base[2] = {0, Wm};
+  const int NT[2] = {kGroupTokens, 1};
   if (t_lo < t_hi) {
-    int b = request_of(a, t_lo);
-    ReqView r = request_view(a, b, false);
+    int b = request_of(m, a.B, t_lo);
+    ReqView r = request_view(a, m, b, false);
     for (int t = t_lo; t < t_hi; ++t) {
-      while (t >= r.q1 && b + 1 < a.B) r = request_view(a, ++b, false);
-      if (t < r.q0 || t >= r.q1) continue;
+      while (t >= r.q1 && b + 1 < a.B) r = request_view(a, m, ++b, false);
+      const bool in = t >= r.q0 && t < r.q1;
+      a.tokv[t] = in ? visible(a, r.S - (r.q1 - r.q0) + (t - r.q0), r.L) : 0;
+      if (!in) continue;
       const int kind = group_kind(a, r, t);
       if (kind == 0) continue;
       const int l = kind - 1;
       const Group g = make_group(a, b, r, t, kind == 1 ? kGroupTokens : 1);
       a.groups[l * T + gi[l]] = g;
       a.ustart[l * (T + 1) + gi[l]] = static_cast<int32_t>(ui[l]);
+      if (g.nch > 0)
+        write_starts(a, l, static_cast<int>(tot_g[l]), static_cast<int>(gi[l]), g,
+                     static_cast<int>(ui[l]), NT[l], nw[l], static_cast<int>(tot_u[l]), base[l]);
       ++gi[l];
       ui[l] += static_cast<uint32_t>(g.nch * g.ntok);
     }
@@ -416,32 +538,6 @@ __device__ __forceinline__ void load_group(const ListView& L, int g, Cursor& cu)
   cu.grp = L.groups[g];
   cu.unit = L.ustart[g];
   cu.c = 0;
-}
-
-__device__ Cursor first_item(const ListView& L, int lo, int hi) {
-  Cursor cu;
-  cu.valid = false;
-  cu.g = 0;
-  cu.c = 0;
-  cu.unit = 0;
-  cu.grp = Group{0, 1, 0, 0, 0, 0, 0, 0};
-  if (L.ng <= 0) return cu;
-  int l = 0, h = L.ng - 1;
-  while (l < h) {  // last group with ustart <= lo
-    const int m = (l + h + 1) >> 1;
-    if (L.ustart[m] <= lo) l = m;
-    else h = m - 1;
-  }
-  load_group(L, l, cu);
-  const int off = lo - cu.unit;
-  cu.c = (off + cu.grp.ntok - 1) / cu.grp.ntok;
-  while (cu.c >= cu.grp.nch) {
-    if (cu.g + 1 >= L.ng) return cu;
-    load_group(L, cu.g + 1, cu);
-  }
-  cu.unit += cu.c * cu.grp.ntok;
-  cu.valid = cu.unit < hi;
-  return cu;
 }
 
 __device__ Cursor next_item(const ListView& L, Cursor cu, int hi) {
@@ -503,7 +599,10 @@ __device__ __forceinline__ int resolve(const KArgs& a, const Addr& ad, bool& bad
 
 // K rows of the wave's 8 blocks (8 x 16 B per lane) and their scales
 // (16 B per block; lanes j and j + 8k all read block j's run), given the
-// resolved block rows v (lane j holds block j's row, or -1).
+// resolved block rows v (lane j holds block j's row, or -1).  STREAM: K
+// rows are read once per call (single-token groups), so they bypass cache
+// retention (non-temporal loads).
+template <bool STREAM>
 __device__ __forceinline__ void stage_load(const KArgs& a, int v, int lane, i32x4 (&kr)[8],
                                            i32x4& sc) {
   const int lane_off = (lane >> 3) * 128 + (lane & 7) * 16;
@@ -513,7 +612,8 @@ __device__ __forceinline__ void stage_load(const KArgs& a, int v, int lane, i32x
     const int row = vu < 0 ? 0 : vu;
     const int8_t* src = a.k + static_cast<int64_t>(row >> a.rlog) * a.kstride +
                         static_cast<int64_t>(row & (a.R - 1)) * 128 + lane_off;
-    kr[u] = *reinterpret_cast<const i32x4*>(src);
+    const i32x4* p = reinterpret_cast<const i32x4*>(src);
+    kr[u] = STREAM ? __builtin_nontemporal_load(p) : *p;
   }
   const int row = v < 0 ? 0 : v;
   sc = *reinterpret_cast<const i32x4*>(a.ks + static_cast<int64_t>(row >> a.rlog) * a.sstride +
@@ -714,10 +814,9 @@ __device__ __forceinline__ void score_subtile(const KArgs& a, const QSrc& qs,
 // wave w scores the (token, sub-tile) pairs w, w+4, ... so that with 4
 // tokens every wave keeps one token's queries.  One item of K in flight.
 template <int NH, int MODE, bool DBG>
-__device__ void run_multi(const KArgs& a, const ListView& L, int lo, int hi, int8_t (*tile)[kChunk * 128],
+__device__ void run_multi(const KArgs& a, const ListView& L, Cursor cur, int hi, int8_t (*tile)[kChunk * 128],
                           uint16_t (*ksc)[kChunk], int wave, int lane, const i32x16& seed, bool& bad) {
   constexpr bool CONSUMER = MODE == QLI_MODE_CONSUMER;
-  Cursor cur = first_item(L, lo, hi);
   Cursor n1 = next_item(L, cur, hi);
   Cursor n2 = next_item(L, n1, hi);
   Addr ad;
@@ -726,7 +825,7 @@ __device__ void run_multi(const KArgs& a, const ListView& L, int lo, int hi, int
   i32x4 sc;
   int v = resolve<CONSUMER>(a, ad, bad);
   stage_addr<CONSUMER>(a, n1.grp, n1.c, n1.valid, wave, lane, ad);
-  stage_load(a, v, lane, kr, sc);
+  stage_load<false>(a, v, lane, kr, sc);
   QState<NH, false> qs;
   qs.tok = -1;
   int buf = 0;
@@ -734,7 +833,7 @@ __device__ void run_multi(const KArgs& a, const ListView& L, int lo, int hi, int
     stage_store(tile[buf], ksc[buf], kr, sc, v, wave, lane);
     v = resolve<CONSUMER>(a, ad, bad);
     stage_addr<CONSUMER>(a, n2.grp, n2.c, n2.valid, wave, lane, ad);
-    stage_load(a, v, lane, kr, sc);
+    stage_load<false>(a, v, lane, kr, sc);
     __syncthreads();
     const Group& gr = cur.grp;
     const int np = 4 * gr.ntok;
@@ -763,11 +862,10 @@ __device__ void run_multi(const KArgs& a, const ListView& L, int lo, int hi, int
 // next lookup, then the K loads: with in-order memory counters a lookup is
 // always older than the K loads that must stay in flight.
 template <int NH, int MODE, bool DBG>
-__device__ void run_single(const KArgs& a, const ListView& L, int lo, int hi,
+__device__ void run_single(const KArgs& a, const ListView& L, Cursor cu, int hi,
                            int8_t (*tile)[kChunk * 128], uint16_t (*ksc)[kChunk], i32x4* qfr,
                            uint32_t* qml, int wave, int lane, const i32x16& seed, bool& bad) {
   constexpr bool CONSUMER = MODE == QLI_MODE_CONSUMER;
-  Cursor cu = first_item(L, lo, hi);
   int buf = 0;
   const QLds<NH> qs{qfr, qml};
   while (cu.valid) {
@@ -784,16 +882,16 @@ __device__ void run_single(const KArgs& a, const ListView& L, int lo, int hi,
     stage_addr<CONSUMER>(a, gr, c0, true, wave, lane, ad);
     int vA = resolve<CONSUMER>(a, ad, bad);
     stage_addr<CONSUMER>(a, gr, c0 + 1, c0 + 1 < c_end, wave, lane, ad);
-    stage_load(a, vA, lane, krA, scA);
+    stage_load<true>(a, vA, lane, krA, scA);
     int vB = resolve<CONSUMER>(a, ad, bad);
     stage_addr<CONSUMER>(a, gr, c0 + 2, c0 + 2 < c_end, wave, lane, ad);
-    stage_load(a, vB, lane, krB, scB);
+    stage_load<true>(a, vB, lane, krB, scB);
     __syncthreads();  // queries in LDS
     for (int c = c0; c < c_end; c += 2) {
       stage_store(tile[buf], ksc[buf], krA, scA, vA, wave, lane);
       vA = resolve<CONSUMER>(a, ad, bad);
       stage_addr<CONSUMER>(a, gr, c + 3, c + 3 < c_end, wave, lane, ad);
-      stage_load(a, vA, lane, krA, scA);
+      stage_load<true>(a, vA, lane, krA, scA);
       __syncthreads();
       score_subtile<NH, MODE, DBG, true>(a, qs, tile[buf], ksc[buf], wave, t, c * kChunk + 64 * wave,
                                          n, lane, seed);
@@ -802,7 +900,7 @@ __device__ void run_single(const KArgs& a, const ListView& L, int lo, int hi,
       stage_store(tile[buf], ksc[buf], krB, scB, vB, wave, lane);
       vB = resolve<CONSUMER>(a, ad, bad);
       stage_addr<CONSUMER>(a, gr, c + 4, c + 4 < c_end, wave, lane, ad);
-      stage_load(a, vB, lane, krB, scB);
+      stage_load<true>(a, vB, lane, krB, scB);
       __syncthreads();
       score_subtile<NH, MODE, DBG, true>(a, qs, tile[buf], ksc[buf], wave, t,
                                          (c + 1) * kChunk + 64 * wave, n, lane, seed);
@@ -815,7 +913,7 @@ __device__ void run_single(const KArgs& a, const ListView& L, int lo, int hi,
   }
 }
 
-// The workgroups split between the two lists in proportion to their units.
+// Each workgroup takes its list, first item and unit range from the plan.
 template <int NH, int MODE, bool DBG>
 __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(KArgs a) {
   __shared__ __attribute__((aligned(16))) int8_t tile[2][kChunk * 128];
@@ -825,162 +923,239 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(KArgs a) {
 
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
-  const int Um = a.hdr->units[0], Us = a.hdr->units[1];
-  const int W = gridDim.x;
-  int Wm = 0;
-  if (Um > 0 && Us == 0) Wm = W;
-  else if (Um > 0) Wm = min(W - 1, max(1, static_cast<int>(static_cast<int64_t>(W) * Um / (Um + Us))));
-  const bool multi = static_cast<int>(blockIdx.x) < Wm;
-  const int wg = multi ? blockIdx.x : blockIdx.x - Wm;
-  const int nw = multi ? Wm : W - Wm;
-  const int U = multi ? Um : Us;
-  const int lo = static_cast<int>(static_cast<int64_t>(wg) * U / nw);
-  const int hi = static_cast<int>(static_cast<int64_t>(wg + 1) * U / nw);
-  if (lo >= hi) return;
-  const int l = multi ? 0 : 1;
+  const WgStart st = a.wgs[blockIdx.x];
+  if (st.g < 0 || st.unit >= st.hi) return;
+  const int l = st.list;
   const ListView L{a.groups + static_cast<int64_t>(l) * a.T,
-                   a.ustart + static_cast<int64_t>(l) * (a.T + 1), a.hdr->ngroups[l]};
+                   a.ustart + static_cast<int64_t>(l) * (a.T + 1), st.ng};
+  Cursor cu;
+  cu.g = st.g;
+  cu.c = st.c;
+  cu.unit = st.unit;
+  cu.grp = st.grp;
+  cu.valid = true;
 
   i32x16 seed;
 #pragma unroll
   for (int i = 0; i < 16; ++i) seed[i] = kSeedBits;
   bool bad = false;
-  if (multi) run_multi<NH, MODE, DBG>(a, L, lo, hi, tile, ksc, wave, lane, seed, bad);
-  else run_single<NH, MODE, DBG>(a, L, lo, hi, tile, ksc, qfr, qml, wave, lane, seed, bad);
+  if (l == 0) run_multi<NH, MODE, DBG>(a, L, cu, st.hi, tile, ksc, wave, lane, seed, bad);
+  else run_single<NH, MODE, DBG>(a, L, cu, st.hi, tile, ksc, qfr, qml, wave, lane, seed, bad);
   if (bad) raise_flag(a, QLI_DEV_BAD_PAGE);
 }
 
 // ---------------------------------------------------------------------------
 // select
 // ---------------------------------------------------------------------------
-// LDS: histogram (2048 bins), scan scratch, and a chunk of up to sel_chunk
-// keys stored with one pad word per 32 (index i at i + i/32) so that both
-// the strided histogram reads and the per-thread contiguous compaction reads
-// are free of bank conflicts.
-constexpr int kSelMaxChunk = 32768;
-constexpr int kSelFixedWords = 2048 + 64 + 8;
+// Each thread keeps its share of a chunk of keys in registers: wave w of a
+// chunk owns keys [w*KPW, (w+1)*KPW), read as 16-byte vectors so that one
+// load instruction covers 1 KB (lane l, vector j: keys 256 j + 4 l .. +3).
+// The chunk is 32 keys per thread (4096 for the 256-thread variant); longer
+// rows are processed chunk by chunk.  LDS: histogram (2048 bins) and scan
+// scratch.
+constexpr uint32_t kPinKey = 0xFFFFFFFFu;  // the forced block sorts above every score
 
-__host__ __device__ constexpr int sel_lds_bytes(int chunk) {
-  return (kSelFixedWords + chunk + chunk / 32) * 4;
-}
+__host__ __device__ constexpr int sel_chunk(int bs) { return bs == 256 ? 4096 : 32 * bs; }
 
-__device__ __forceinline__ int padded(int i) { return i + (i >> 5); }
+struct MinOp {
+  __device__ __forceinline__ uint32_t operator()(uint32_t x, uint32_t y) const { return min(x, y); }
+};
+struct MaxOp {
+  __device__ __forceinline__ uint32_t operator()(uint32_t x, uint32_t y) const { return max(x, y); }
+};
+struct AddOp {
+  __device__ __forceinline__ uint32_t operator()(uint32_t x, uint32_t y) const { return x + y; }
+};
 
 // Select the best min(k, #nonzero) of keys[0..n) by (key desc, index asc)
 // and write map(index) for them in ascending index order to out[0..k),
-// -1 after.  pin (or -1) is forced to the top.
-template <int BS, class Map>
-__device__ void select_topk(const uint32_t* keys, int n, int k, int pin, int32_t* out, Map map,
-                            int chunk, uint32_t* lds) {
+// -1 after.  pin (or -1) is forced to the top.  The row holds cap >= n
+// keys (a multiple of 64), so whole 16-byte vectors below cap may be read.
+//
+// Radix select over the range the keys actually occupy: the first digit is
+// taken from (key - min) with a shift that leaves at most 2048 bins, and
+// each further pass splits the chosen bin 2048 ways.  Scores of one query
+// share a narrow band of key values, so fixed top-bit digits would pile
+// them into a handful of bins.  A pass ends the search as soon as every key
+// of the boundary bin is needed.
+// MULTI = false: the caller guarantees n <= CHUNK (one chunk, loaded once).
+template <int BS, bool MULTI, class Map>
+__device__ __forceinline__ void select_topk(const uint32_t* keys, int n, int cap, int k, int pin,
+                                            int32_t* out, Map map, uint32_t* lds) {
+  constexpr int CHUNK = MULTI ? 16 * BS : sel_chunk(BS);  // fewer live keys when reloading
+  constexpr int NW = BS / 64;
+  constexpr int KPW = CHUNK / NW;        // keys per wave per chunk
+  constexpr int VPT = CHUNK / (4 * BS);  // 16-byte vectors per thread per chunk
   uint32_t* hist = lds;
   uint32_t* sh = lds + 2048;
   uint32_t* misc = lds + 2048 + 64;
-  uint32_t* kl = lds + kSelFixedWords;
-  const int tid = threadIdx.x;
-  const int nch = (n + chunk - 1) / chunk;
-  auto load = [&](int ch) {  // coalesced: 16 B per thread per step
-    const int base = ch * chunk;
-    const int len = min(chunk, n - base);
-    for (int i = 4 * tid; i < chunk; i += 4 * BS) {
-      uint32_t v[4];
-      if (i + 3 < len) {
-        const i32x4 x = *reinterpret_cast<const i32x4*>(keys + base + i);
-        v[0] = x[0];
-        v[1] = x[1];
-        v[2] = x[2];
-        v[3] = x[3];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = i + e < len ? keys[base + i + e] : 0u;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) kl[padded(i + e)] = base + i + e == pin ? 0xFFFFFFFFu : v[e];
-    }
-    __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nch = MULTI ? (n + CHUNK - 1) / CHUNK : 1;
+  uint32_t kr[4 * VPT];
+  auto index_of = [&](int ch, int j, int e) {
+    return ch * CHUNK + wave * KPW + 256 * j + 4 * lane + e;
   };
-  if (nch == 1) load(0);
-
-  uint32_t prefix = 0, mask = 0;
-  int krem = k;
-  bool take_all = false;
-  constexpr int BPT = 2048 / BS;  // histogram bins per thread
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const uint32_t nb = pass == 2 ? 1024u : 2048u;
+  auto load = [&](int ch) {  // every load is issued before the first use
+    i32x4 x[VPT];
 #pragma unroll
-    for (int j = 0; j < BPT; ++j) hist[tid * BPT + j] = 0;
-    __syncthreads();
-    for (int ch = 0; ch < nch; ++ch) {
-      if (nch > 1) load(ch);
-      const int len = min(chunk, n - ch * chunk);
-      for (int i = tid; i < len; i += BS) {
-        const uint32_t key = kl[padded(i)];
-        if (key != 0 && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (nb - 1)], 1u);
+    for (int j = 0; j < VPT; ++j)
+      x[j] = *reinterpret_cast<const i32x4*>(keys + min(index_of(ch, j, 0), cap - 4));
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int idx = index_of(ch, j, e);
+        const uint32_t v = idx < n ? static_cast<uint32_t>(x[j][e]) : 0u;
+        kr[4 * j + e] = idx == pin ? kPinKey : v;
       }
-      if (nch > 1) __syncthreads();
-    }
-    __syncthreads();
-    uint32_t c = 0;
+  };
+
+  // range and count of the scores (keys other than 0 and the pin)
+  uint32_t mn = 0xFFFFFFFFu, mx = 0, cnt = 0;
+  for (int ch = 0; ch < nch; ++ch) {
+    load(ch);
 #pragma unroll
-    for (int j = 0; j < BPT; ++j) c += hist[tid * BPT + j];
-    uint32_t total;
-    const uint32_t excl = block_exclusive_scan<BS>(c, &total, sh);
-    if (pass == 0 && total <= static_cast<uint32_t>(k)) {
-      take_all = true;
-      break;
+    for (int r = 0; r < 4 * VPT; ++r) {
+      const uint32_t v = kr[r];
+      const bool s = v != 0 && v != kPinKey;
+      mn = s ? min(mn, v) : mn;
+      mx = s ? max(mx, v) : mx;
+      cnt += s ? 1u : 0u;
     }
-    const uint32_t above = total - excl - c;  // keys in higher bins
-    if (above < static_cast<uint32_t>(krem) && above + c >= static_cast<uint32_t>(krem)) {
-      uint32_t cum = above;
-      for (int j = BPT - 1; j >= 0; --j) {
-        const uint32_t h = hist[tid * BPT + j];
-        if (cum + h >= static_cast<uint32_t>(krem)) {
-          misc[0] = static_cast<uint32_t>(tid * BPT + j);
-          misc[1] = cum;
+  }
+  mn = wave_allreduce(mn, MinOp{});
+  mx = wave_allreduce(mx, MaxOp{});
+  cnt = wave_allreduce(cnt, AddOp{});
+  if (lane == 0) {
+    sh[wave] = mn;
+    sh[16 + wave] = mx;
+    sh[32 + wave] = cnt;
+  }
+  __syncthreads();
+  mn = sh[0];
+  mx = sh[16];
+  cnt = sh[32];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    mn = min(mn, sh[w]);
+    mx = max(mx, sh[16 + w]);
+    cnt += sh[32 + w];
+  }
+  __syncthreads();
+  const bool pinned = pin >= 0 && pin < n;
+
+  // threshold: keys > thr are taken, then the first `need` keys == thr
+  uint32_t thr = 0, need = 0;
+  if (cnt + (pinned ? 1u : 0u) > static_cast<uint32_t>(k)) {
+    uint32_t krem = static_cast<uint32_t>(k) - (pinned ? 1u : 0u);
+    if (krem == 0) {
+      thr = kPinKey - 1;
+    } else {
+      uint32_t lo = mn, hi = mx;
+      int bits = hi == lo ? 0 : 32 - __clz(static_cast<int>(hi - lo));
+      constexpr int BPT = 2048 / BS;  // histogram bins per thread
+#pragma unroll 1
+      while (true) {
+        const int sft = max(0, bits - 11);
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) hist[tid * BPT + j] = 0;
+        __syncthreads();
+        for (int ch = 0; ch < nch; ++ch) {
+          if (MULTI && nch > 1) load(ch);
+#pragma unroll
+          for (int r = 0; r < 4 * VPT; ++r) {
+            const uint32_t key = kr[r];
+            if (key >= lo && key <= hi) atomicAdd(&hist[(key - lo) >> sft], 1u);
+            if ((r & 7) == 7) __builtin_amdgcn_sched_barrier(0);  // bounds live addresses
+          }
+        }
+        __syncthreads();
+        uint32_t c = 0;
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) c += hist[tid * BPT + j];
+        uint32_t total;
+        const uint32_t excl = block_exclusive_scan<BS>(c, &total, sh);
+        const uint32_t above_t = total - excl - c;  // keys in higher bins
+        if (above_t < krem && above_t + c >= krem) {
+          uint32_t cum = above_t;
+          for (int j = BPT - 1; j >= 0; --j) {
+            const uint32_t h = hist[tid * BPT + j];
+            if (cum + h >= krem) {
+              misc[0] = static_cast<uint32_t>(tid * BPT + j);
+              misc[1] = cum;
+              misc[2] = h;
+              break;
+            }
+            cum += h;
+          }
+        }
+        __syncthreads();
+        const uint32_t b = misc[0], above = misc[1], hb = misc[2];
+        krem -= above;
+        const uint32_t blo = lo + (b << sft);
+        if (hb == krem) {  // the whole boundary bin is taken
+          thr = blo - 1;
           break;
         }
-        cum += h;
+        if (sft == 0) {
+          thr = blo;
+          need = krem;
+          break;
+        }
+        lo = blo;
+        hi = static_cast<uint32_t>(min(static_cast<uint64_t>(hi),
+                                       static_cast<uint64_t>(blo) + (1ull << sft) - 1));
+        bits = sft;
+        __syncthreads();  // misc is rewritten by the next pass
       }
     }
-    __syncthreads();
-    krem -= static_cast<int>(misc[1]);
-    prefix |= misc[0] << shift;
-    mask |= (nb - 1) << shift;
-    __syncthreads();
   }
 
-  // ordered compaction: offset = (keys > T before me) + min(need, keys == T before me)
-  const uint32_t thr = take_all ? 0u : prefix;
-  const uint32_t need = take_all ? 0u : static_cast<uint32_t>(krem);
-  const int kpt = chunk / BS;  // keys per thread, contiguous
+  // ordered compaction: a key's output slot is (keys > thr before it) +
+  // min(need, keys == thr before it), both counted in index order (packed
+  // as gt << 16 | eq; a chunk holds at most 32768 keys)
   uint32_t run_gt = 0, run_eq = 0;
   for (int ch = 0; ch < nch; ++ch) {
-    if (nch > 1) load(ch);
-    const int first = tid * kpt;
-    uint32_t gt = 0, eq = 0;
-    for (int e = 0; e < kpt; ++e) {
-      const uint32_t key = kl[padded(first + e)];
-      gt += key > thr ? 1u : 0u;
-      eq += (key == thr && thr != 0) ? 1u : 0u;
+    if (MULTI && nch > 1) load(ch);
+    auto flag = [&](uint32_t key) {
+      return key > thr ? (1u << 16) : ((key == thr && need != 0) ? 1u : 0u);
+    };
+    uint32_t excl[VPT];  // this lane's prefix within its wave, per vector
+    uint32_t wsum = 0;   // running wave total over the vectors
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c += flag(kr[4 * j + e]);
+      const uint32_t inc = wave_inclusive_scan(c);
+      excl[j] = wsum + inc - c;
+      wsum += static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(inc), 63));
     }
-    uint32_t tot;
-    const uint32_t ex = block_exclusive_scan<BS>((gt << 16) | eq, &tot, sh);
-    uint32_t eq_rank = run_eq + (ex & 0xFFFFu);
-    uint32_t at = run_gt + (ex >> 16) + min(need, eq_rank);
-    const int base = ch * chunk + first;
-    for (int e = 0; e < kpt; ++e) {
-      const uint32_t key = kl[padded(first + e)];
-      bool sel = key > thr;
-      if (key == thr && thr != 0) {
-        sel = eq_rank < need;
-        ++eq_rank;
+    if (lane == 0) sh[wave] = wsum;
+    __syncthreads();
+    uint32_t wbase = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t x = sh[w];
+      wbase += w < wave ? x : 0u;
+      tot += x;
+    }
+    __syncthreads();  // sh is reused
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      uint32_t before = wbase + excl[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t f = flag(kr[4 * j + e]);
+        const uint32_t eq_rank = run_eq + (before & 0xFFFFu);
+        const bool sel = f == (1u << 16) || (f == 1u && eq_rank < need);
+        if (sel) out[run_gt + (before >> 16) + min(need, eq_rank)] = map(index_of(ch, j, e));
+        before += f;
       }
-      if (sel) out[at++] = map(base + e);
+      __builtin_amdgcn_sched_barrier(0);  // bounds live addresses
     }
     run_gt += tot >> 16;
     run_eq += tot & 0xFFFFu;
-    if (nch > 1) __syncthreads();
   }
   const int count = static_cast<int>(run_gt + min(need, run_eq));
   for (int i = count + tid; i < k; i += BS) out[i] = -1;
@@ -995,23 +1170,24 @@ struct MapSlots {
   __device__ __forceinline__ int32_t operator()(int i) const { return slots[i >> 3] * 8 + (i & 7); }
 };
 
-template <int BS>
-__global__ __launch_bounds__(BS) void select_kernel(KArgs a, int chunk) {
-  extern __shared__ uint32_t sel_lds[];
+template <int BS, bool MULTI>
+__global__ __launch_bounds__(BS) void select_kernel(KArgs a) {
+  __shared__ uint32_t sel_lds[2048 + 64 + 8];
   const int t = blockIdx.x;
   if (blockIdx.y == 0) {
     int32_t* out = a.topk_out + static_cast<int64_t>(t) * a.topk;
     const uint32_t* keys = a.keys + static_cast<int64_t>(t) * a.ncap;
+    const int cap = static_cast<int>(a.ncap);
     if (a.mode == QLI_MODE_CONSUMER) {
-      select_topk<BS>(keys, a.ncount[t], a.topk, -1, out,
-                      MapSlots{a.slots + static_cast<int64_t>(t) * a.cb_in}, chunk, sel_lds);
+      select_topk<BS, MULTI>(keys, a.ncount[t], cap, a.topk, -1, out,
+                      MapSlots{a.slots + static_cast<int64_t>(t) * a.cb_in}, sel_lds);
     } else {
-      select_topk<BS>(keys, token_view(a, t).V, a.topk, -1, out, MapIdentity{}, chunk, sel_lds);
+      select_topk<BS, MULTI>(keys, a.tokv[t], cap, a.topk, -1, out, MapIdentity{}, sel_lds);
     }
   } else {
-    const int nb = (token_view(a, t).V + 7) / 8;
-    select_topk<BS>(a.bkeys + static_cast<int64_t>(t) * a.nbcap, nb, a.cb, nb - 1,
-                    a.cand_out + static_cast<int64_t>(t) * a.cb, MapIdentity{}, chunk, sel_lds);
+    const int nb = (a.tokv[t] + 7) / 8;
+    select_topk<BS, MULTI>(a.bkeys + static_cast<int64_t>(t) * a.nbcap, nb, static_cast<int>(a.nbcap), a.cb,
+                    nb - 1, a.cand_out + static_cast<int64_t>(t) * a.cb, MapIdentity{}, sel_lds);
   }
 }
 
@@ -1049,22 +1225,6 @@ struct Stamp {
 };
 
 int g_cu_count[64];
-bool g_lds_attr[64][3];
-
-// Raise a kernel's dynamic LDS limit once per device (needed above 64 KB).
-template <class Kernel>
-bool allow_dynamic_lds(Kernel kernel, int slot, int bytes) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
-  if (!g_lds_attr[dev][slot]) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
-      return false;
-    g_lds_attr[dev][slot] = true;
-  }
-  return true;
-}
-
 int cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -1170,9 +1330,12 @@ int launch(const qli_params* p, const WsLayout& w, void* stream) {
   a.hdr = reinterpret_cast<PlanHdr*>(ws + w.plan_off);
   a.groups = reinterpret_cast<Group*>(ws + w.groups_off);  // [2][T]
   a.ustart = reinterpret_cast<int32_t*>(ws + w.ustart_off);
+  a.wgs = reinterpret_cast<WgStart*>(ws + w.wgs_off);
+  a.score_grid = std::min(kMaxScoreWGs, std::max(2, 2 * cu_count()));
   a.slots = consumer ? reinterpret_cast<int32_t*>(ws + w.slots_off) : nullptr;
   a.srow = consumer ? reinterpret_cast<int32_t*>(ws + w.srow_off) : nullptr;
   a.ncount = consumer ? reinterpret_cast<int32_t*>(ws + w.ncount_off) : nullptr;
+  a.tokv = reinterpret_cast<int32_t*>(ws + w.tokv_off);
 
   const unsigned T = static_cast<unsigned>(p->num_tokens);
   if (consumer) {
@@ -1185,23 +1348,19 @@ int launch(const qli_params* p, const WsLayout& w, void* stream) {
   }
   if (w.ncap > 0) {
     Stamp s(QLI_KERNEL_SCORE, st);
-    const unsigned grid = static_cast<unsigned>(2 * cu_count());
-    launch_score(p->num_heads, p->mode, p->dbg_scores != nullptr, grid, st, a);
+    launch_score(p->num_heads, p->mode, p->dbg_scores != nullptr, static_cast<unsigned>(a.score_grid), st,
+                 a);
   }
   {
     Stamp s(QLI_KERNEL_SELECT, st);
     const int64_t longest = w.ncap > w.nbcap ? w.ncap : w.nbcap;
     const dim3 grid(T, source ? 2 : 1);
-    if (longest <= 4096) {
-      if (!allow_dynamic_lds(select_kernel<256>, 0, sel_lds_bytes(4096))) return QLI_ERR_HIP;
-      select_kernel<256><<<grid, 256, sel_lds_bytes(4096), st>>>(a, 4096);
-    } else if (longest <= 16384) {
-      if (!allow_dynamic_lds(select_kernel<512>, 1, sel_lds_bytes(16384))) return QLI_ERR_HIP;
-      select_kernel<512><<<grid, 512, sel_lds_bytes(16384), st>>>(a, 16384);
-    } else {
-      if (!allow_dynamic_lds(select_kernel<1024>, 2, sel_lds_bytes(kSelMaxChunk))) return QLI_ERR_HIP;
-      select_kernel<1024><<<grid, 1024, sel_lds_bytes(kSelMaxChunk), st>>>(a, kSelMaxChunk);
-    }
+    // rows no longer than a chunk (every n <= its row capacity) take the
+    // single-chunk variants
+    if (longest <= sel_chunk(256)) select_kernel<256, false><<<grid, 256, 0, st>>>(a);
+    else if (longest <= sel_chunk(512)) select_kernel<512, false><<<grid, 512, 0, st>>>(a);
+    else if (longest <= sel_chunk(1024)) select_kernel<1024, false><<<grid, 1024, 0, st>>>(a);
+    else select_kernel<1024, true><<<grid, 1024, 0, st>>>(a);
   }
   return hipGetLastError() == hipSuccess ? QLI_OK : QLI_ERR_HIP;
 }

@@ -158,11 +158,13 @@ def test_zero_tokens_is_a_noop(lib):
 def test_workspace_bytes(lib):
     p = base_params(mode=2, ratio=2, T=4)
     # keys: 4 tokens * roundup(128, 256) slots * 4 B; block keys: 4 * 64 * 4 B;
-    # plan header 256 B, groups 2 * 4 * 32 B, group prefixes 2 * 5 * 4 B (each 256-B aligned)
-    assert Q.qli_workspace_bytes(p) == 4 * 256 * 4 + 4 * 64 * 4 + 256 + 256 + 256
+    # plan header 256 B, groups 2 * 4 * 32 B, group prefixes 2 * 5 * 4 B (each 256-B aligned),
+    # 2048 workgroup start entries of 64 B, per-token visible counts 4 * 4 B
+    starts = 2048 * 64 + 256
+    assert Q.qli_workspace_bytes(p) == 4 * 256 * 4 + 4 * 64 * 4 + 256 + 256 + 256 + starts
     p = base_params(mode=3, ratio=2, T=4)
     # keys: 4 * 64*8 * 4; plan 3 * 256; slots + page rows: 2 * 4 * 64 * 4; counts 256
-    assert Q.qli_workspace_bytes(p) == 4 * 512 * 4 + 3 * 256 + 2 * 4 * 64 * 4 + 256
+    assert Q.qli_workspace_bytes(p) == 4 * 512 * 4 + 3 * 256 + starts + 2 * 4 * 64 * 4 + 256
     p.head_dim = 3
     assert Q.qli_workspace_bytes(p) == 0
 
