@@ -276,21 +276,94 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total, uint32_t* 
 // consumer_prep: sorted unique visible incoming block ids per token
 // ---------------------------------------------------------------------------
 constexpr int kPrepThreads = 1024;
+constexpr int kPrepBitmapWords = 8192;  // bitmap of up to 2^18 block ids (32 KB of LDS)
 
+// The request holding token t, found by all threads at once (one round of
+// loads instead of a dependent binary search); every thread gets it.
+__device__ __forceinline__ int prep_request(const KArgs& a, int t, int* s_req) {
+  if (threadIdx.x == 0) *s_req = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < a.B; i += kPrepThreads)
+    if (a.qsl[i] <= t && t < a.qsl[i + 1]) *s_req = i;
+  __syncthreads();
+  return *s_req;
+}
+
+// Slot table of token t from its kept block ids in ascending order (sl[0 ..
+// total), in LDS): slots, page rows and the eligible count.
+__device__ __forceinline__ void prep_write(const KArgs& a, int t, int b, int V, const int32_t* sl,
+                                           int total) {
+  int32_t* slots = a.slots + static_cast<int64_t>(t) * a.cb_in;
+  int32_t* srow = a.srow + static_cast<int64_t>(t) * a.cb_in;
+  bool bad = false;
+  for (int i = threadIdx.x; i < total; i += kPrepThreads) {
+    const int blk = sl[i];
+    const int pos0 = blk * 8;
+    const int page = page_checked(a, b, pos0 >> a.rlog);
+    bad |= page < 0;
+    slots[i] = blk;
+    srow[i] = page < 0 ? -1 : page * a.R + (pos0 & (a.R - 1));
+  }
+  if (bad) raise_flag(a, QLI_DEV_BAD_PAGE);
+  if (threadIdx.x == 0) {
+    // every kept block is full except possibly the last visible one, which
+    // is the largest id and therefore the last slot
+    const int tail = total > 0 ? V - sl[total - 1] * 8 : 0;
+    a.ncount[t] = total > 0 ? 8 * (total - 1) + min(tail, 8) : 0;
+  }
+}
+
+// Sorted unique visible incoming block ids per token, through a bitmap of
+// the visible block ids: duplicates merge, and a prefix count of set bits
+// places every id (contexts of up to 2^18 blocks).
 __global__ __launch_bounds__(kPrepThreads) void consumer_prep_kernel(KArgs a) {
-  __shared__ int32_t v[QLI_MAX_CAND_BLOCKS];
+  __shared__ uint32_t bm[kPrepBitmapWords];
+  __shared__ int32_t sl[QLI_MAX_CAND_BLOCKS];
   __shared__ uint32_t sh[64];
   __shared__ int s_req;
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
-  // the request holding t, found by all threads at once (one round of
-  // loads instead of a dependent binary search)
-  if (tid == 0) s_req = 0;
+  const int b = prep_request(a, t, &s_req);
+  const ReqView r = request_view(a, global_meta(a), b, tid == 0);
+  const int V = (t >= r.q0 && t < r.q1)
+                    ? visible(a, r.S - (r.q1 - r.q0) + (t - r.q0), r.L) : 0;
+  const int nblocks = (V + 7) / 8;
+  const int nwords = (nblocks + 31) / 32;  // <= kPrepBitmapWords (checked at launch)
+  for (int i = tid; i < nwords; i += kPrepThreads) bm[i] = 0;
   __syncthreads();
-  for (int i = tid; i < a.B; i += kPrepThreads)
-    if (a.qsl[i] <= t && t < a.qsl[i + 1]) s_req = i;
+  const int32_t* cin = a.cand_in + static_cast<int64_t>(t) * a.cb_in;
+  for (int i = tid; i < a.cb_in; i += kPrepThreads) {
+    const int c = cin[i];
+    if (c >= 0 && c < nblocks) atomicOr(&bm[c >> 5], 1u << (c & 31));
+  }
   __syncthreads();
-  const int b = s_req;
+  const int wpt = (nwords + kPrepThreads - 1) / kPrepThreads;
+  const int w0 = min(nwords, tid * wpt), w1 = min(nwords, w0 + wpt);
+  uint32_t cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += __popc(bm[w]);
+  uint32_t total;
+  uint32_t at = block_exclusive_scan<kPrepThreads>(cnt, &total, sh);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t bits = bm[w];
+    while (bits) {
+      const int j = __ffs(bits) - 1;
+      bits &= bits - 1;
+      sl[at++] = 32 * w + j;
+    }
+  }
+  __syncthreads();
+  prep_write(a, t, b, V, sl, static_cast<int>(total));
+}
+
+// The same by a bitonic sort of the incoming ids (any context length).
+__global__ __launch_bounds__(kPrepThreads) void consumer_prep_sort_kernel(KArgs a) {
+  __shared__ int32_t v[QLI_MAX_CAND_BLOCKS];
+  __shared__ int32_t sl[QLI_MAX_CAND_BLOCKS];
+  __shared__ uint32_t sh[64];
+  __shared__ int s_req;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int b = prep_request(a, t, &s_req);
   const ReqView r = request_view(a, global_meta(a), b, tid == 0);
   const int V = (t >= r.q0 && t < r.q1)
                     ? visible(a, r.S - (r.q1 - r.q0) + (t - r.q0), r.L) : 0;
@@ -320,8 +393,6 @@ __global__ __launch_bounds__(kPrepThreads) void consumer_prep_kernel(KArgs a) {
       __syncthreads();
     }
   }
-  int32_t* slots = a.slots + static_cast<int64_t>(t) * cbi;
-  int32_t* srow = a.srow + static_cast<int64_t>(t) * cbi;
   const int i0 = 2 * tid;
   bool f[2];
   uint32_t cnt = 0;
@@ -333,26 +404,11 @@ __global__ __launch_bounds__(kPrepThreads) void consumer_prep_kernel(KArgs a) {
   }
   uint32_t total;
   uint32_t at = block_exclusive_scan<kPrepThreads>(cnt, &total, sh);
-  bool bad = false;
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    if (!f[e]) continue;
-    const int blk = v[i0 + e];
-    const int pos0 = blk * 8;
-    const int page = page_checked(a, b, pos0 >> a.rlog);
-    if (page < 0) bad = true;
-    slots[at] = blk;
-    srow[at] = page < 0 ? -1 : page * a.R + (pos0 & (a.R - 1));
-    if (at + 1 == total) {
-      // eligible slots: every kept block is full except possibly the last
-      // visible one, which is the largest id and therefore the last slot
-      const int tail = V - pos0;
-      a.ncount[t] = 8 * (static_cast<int>(total) - 1) + (tail < 8 ? tail : 8);
-    }
-    ++at;
-  }
-  if (bad) raise_flag(a, QLI_DEV_BAD_PAGE);
-  if (tid == 0 && total == 0) a.ncount[t] = 0;
+  for (int e = 0; e < 2; ++e)
+    if (f[e]) sl[at++] = v[i0 + e];
+  __syncthreads();
+  prep_write(a, t, b, V, sl, static_cast<int>(total));
 }
 
 // ---------------------------------------------------------------------------
@@ -390,70 +446,111 @@ __device__ __forceinline__ Group make_group(const KArgs& a, int b, const ReqView
   return g;
 }
 
+// floor(p / q) for 0 <= p < 2^53 and 0 < q < 2^31: the correctly rounded
+// double quotient is within one of the floor, and one integer check fixes it
+// (the integer divide would be a long software sequence).
+__device__ __forceinline__ int64_t floor_div(int64_t p, int64_t q) {
+  int64_t f = static_cast<int64_t>(static_cast<double>(p) / static_cast<double>(q));
+  if (f * q > p) --f;
+  else if ((f + 1) * q <= p) ++f;
+  return f;
+}
+
+__device__ __forceinline__ int64_t ceil_div(int64_t x, int64_t y) {
+  return x <= 0 ? 0 : floor_div(x + y - 1, y);
+}
+
 // Score workgroups of the multi list: a share of the grid in proportion to
 // its work units (at least one for each non-empty list).
 __device__ __forceinline__ int multi_workgroups(int W, int Um, int Us) {
   if (Um <= 0) return 0;
   if (Us <= 0) return W;
-  return min(W - 1, max(1, static_cast<int>(static_cast<int64_t>(W) * Um / (Um + Us))));
+  const int share = static_cast<int>(floor_div(static_cast<int64_t>(W) * Um,
+                                               static_cast<int64_t>(Um) + Us));
+  return min(W - 1, max(1, share));
 }
 
-// Workgroup w of a list with U units over nw workgroups owns the items whose
-// first unit lies in [floor(w*U/nw), floor((w+1)*U/nw)).  Every group of a
-// list has the same token count NT, so group g (units [a, a + nch*NT))
-// holds the first item of exactly the workgroups whose range starts in
-// (a - NT, a + (nch - 1)*NT]; the thread that writes g writes their entries.
-__device__ __forceinline__ int64_t ceil_div(int64_t x, int64_t y) {
-  return x <= 0 ? 0 : (x + y - 1) / y;
+// Exclusive prefix of N values at once over a workgroup of BS threads
+// (BS/64 <= 16 waves); total[i] receives the sums.  Uses sh[0 .. 16 N).
+template <int BS, int N>
+__device__ __forceinline__ void block_exclusive_scan_n(uint32_t (&v)[N], uint32_t (&total)[N],
+                                                       uint32_t* sh) {
+  constexpr int NW = BS / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t inc[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) inc[i] = wave_inclusive_scan(v[i]);
+  if (lane == 63) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) sh[16 * i + wave] = inc[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    uint32_t before = 0, t = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t x = sh[16 * i + w];
+      before += w < wave ? x : 0u;
+      t += x;
+    }
+    v[i] = before + inc[i] - v[i];
+    total[i] = t;
+  }
+  __syncthreads();
 }
 
-__device__ void write_starts(const KArgs& a, int list, int ng, int gidx, const Group& g, int unit0,
-                             int NT, int nw, int U, int base) {
+// One list's split of the score grid: nw workgroups over U work units;
+// workgroup w owns the items whose first unit lies in
+// [floor(w*U/nw), floor((w+1)*U/nw)).
+struct Split {
+  int list, ng, NT, nw, U, base;
+  int q, r;  // U = q*nw + r
+};
+
+// Every group of a list has the same token count NT, so group g (units
+// [a, a + nch*NT)) holds the first item of exactly the workgroups whose
+// range starts in (a - NT, a + (nch - 1)*NT]; the thread that writes g
+// writes their entries.  Consecutive range starts differ by q or q + 1.
+__device__ void write_starts(const KArgs& a, const Split& sp, int gidx, const Group& g, int unit0) {
+  const int NT = sp.NT, nw = sp.nw;
   const int64_t e = unit0 + static_cast<int64_t>(g.nch - 1) * NT;
-  const int w0 = static_cast<int>(ceil_div((static_cast<int64_t>(unit0) - NT + 1) * nw, U));
-  const int w1 = static_cast<int>(min(static_cast<int64_t>(nw), ceil_div((e + 1) * nw, U)));
+  const int w0 = static_cast<int>(ceil_div((static_cast<int64_t>(unit0) - NT + 1) * nw, sp.U));
+  const int w1 = static_cast<int>(min(static_cast<int64_t>(nw), ceil_div((e + 1) * nw, sp.U)));
+  if (w0 >= w1) return;
+  const int64_t p0 = static_cast<int64_t>(w0) * sp.U;
+  int lo = static_cast<int>(floor_div(p0, nw));
+  int rem = static_cast<int>(p0 - static_cast<int64_t>(lo) * nw);
   for (int w = w0; w < w1; ++w) {
-    const int lo = static_cast<int>(static_cast<int64_t>(w) * U / nw);
-    const int c = static_cast<int>(ceil_div(lo - unit0, NT));
+    const int carry = rem + sp.r >= nw ? 1 : 0;
+    const int hi = lo + sp.q + carry;
+    rem = rem + sp.r - carry * nw;
+    const int off = lo - unit0;
+    const int c = off <= 0 ? 0 : (NT == 1 ? off : (off + 3) >> 2);  // NT is 1 or 4
     WgStart st;
     st.grp = g;
-    st.list = list;
-    st.ng = ng;
+    st.list = sp.list;
+    st.ng = sp.ng;
     st.g = gidx;
     st.c = c;
     st.unit = unit0 + c * NT;
-    st.hi = static_cast<int>(static_cast<int64_t>(w + 1) * U / nw);
+    st.hi = hi;
     st.pad[0] = st.pad[1] = 0;
-    a.wgs[base + w] = st;
+    a.wgs[sp.base + w] = st;
+    lo = hi;
   }
 }
 
 constexpr int kPlanLdsRequests = 4096;  // metadata of up to this many requests is staged in LDS
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(KArgs a) {
-  __shared__ uint32_t sh[64];
-  __shared__ int32_t s_meta[3 * kPlanLdsRequests + 1];
+// The plan proper, on request metadata m (an LDS copy or global memory).
+__device__ __forceinline__ void plan_body(const KArgs& a, const Meta& m, uint32_t* sh) {
   const int tid = threadIdx.x;
   const int T = a.T;
-  Meta m = global_meta(a);
-  if (a.B <= kPlanLdsRequests) {
-    int32_t* q = s_meta;
-    int32_t* l = s_meta + kPlanLdsRequests + 1;
-    int32_t* r = s_meta + 2 * kPlanLdsRequests + 1;
-    for (int i = tid; i <= a.B; i += kPlanThreads) {
-      q[i] = a.qsl[i];
-      if (i < a.B) {
-        l[i] = a.klen[i];
-        if (a.smod) r[i] = a.smod[i];
-      }
-    }
-    __syncthreads();
-    m = Meta{q, l, a.smod ? r : nullptr};
-  }
   const int per = (T + kPlanThreads - 1) / kPlanThreads;
   const int t_lo = min(T, tid * per);
   const int t_hi = min(T, t_lo + per);
-  uint32_t ng[2] = {0, 0}, nu[2] = {0, 0};
+  uint32_t cnt[4] = {0, 0, 0, 0};  // groups and units of list 0, then of list 1
   if (t_lo < t_hi) {
     int b = request_of(m, a.B, t_lo);
     ReqView r = request_view(a, m, b, true);
@@ -463,29 +560,36 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KArgs a) {
       const int kind = group_kind(a, r, t);
       if (kind == 0) continue;
       const Group g = make_group(a, b, r, t, kind == 1 ? kGroupTokens : 1);
-      ++ng[kind - 1];
-      nu[kind - 1] += static_cast<uint32_t>(g.nch * g.ntok);
+      const uint32_t units = static_cast<uint32_t>(g.nch * g.ntok);
+      if (kind == 1) {
+        cnt[0] += 1;
+        cnt[1] += units;
+      } else {
+        cnt[2] += 1;
+        cnt[3] += units;
+      }
     }
   }
-  // every start entry begins as "no work" (the scans' barriers order these
-  // stores before the ones below); workgroups whose range starts past the
-  // last item of their list keep it
-  for (int w = tid; w < a.score_grid; w += kPlanThreads) {
-    WgStart st = {};
-    st.g = -1;
-    a.wgs[w] = st;
-  }
-  uint32_t tot_g[2], tot_u[2], gi[2], ui[2];
-  for (int l = 0; l < 2; ++l) {
-    gi[l] = block_exclusive_scan<kPlanThreads>(ng[l], &tot_g[l], sh);
-    ui[l] = block_exclusive_scan<kPlanThreads>(nu[l], &tot_u[l], sh);
-  }
+  uint32_t tot[4];
+  block_exclusive_scan_n<kPlanThreads, 4>(cnt, tot, sh);  // also orders the clears below
   const int W = a.score_grid;
-  const int Wm = multi_workgroups(W, static_cast<int>(tot_u[0]), static_cast<int>(tot_u[1]));
-  const int nw[2] = {Wm, W - Wm};
-  const int base[2] = {0, Wm};
-  const int NT[2] = {kGroupTokens, 1};
+  const int Wm = multi_workgroups(W, static_cast<int>(tot[1]), static_cast<int>(tot[3]));
+  auto split = [&](int l) {
+    Split sp;
+    sp.list = l;
+    sp.ng = static_cast<int>(tot[2 * l]);
+    sp.NT = l == 0 ? kGroupTokens : 1;
+    sp.nw = l == 0 ? Wm : W - Wm;
+    sp.U = static_cast<int>(tot[2 * l + 1]);
+    sp.base = l == 0 ? 0 : Wm;
+    sp.q = sp.nw > 0 ? sp.U / sp.nw : 0;
+    sp.r = sp.nw > 0 ? sp.U - sp.q * sp.nw : 0;
+    return sp;
+  };
+  const Split sp0 = split(0), sp1 = split(1);
   if (t_lo < t_hi) {
+    // running group index and first unit of list 0, then of list 1
+    uint32_t g0 = cnt[0], u0 = cnt[1], g1 = cnt[2], u1 = cnt[3];
     int b = request_of(m, a.B, t_lo);
     ReqView r = request_view(a, m, b, false);
     for (int t = t_lo; t < t_hi; ++t) {
@@ -497,21 +601,58 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KArgs a) {
       if (kind == 0) continue;
       const int l = kind - 1;
       const Group g = make_group(a, b, r, t, kind == 1 ? kGroupTokens : 1);
-      a.groups[l * T + gi[l]] = g;
-      a.ustart[l * (T + 1) + gi[l]] = static_cast<int32_t>(ui[l]);
-      if (g.nch > 0)
-        write_starts(a, l, static_cast<int>(tot_g[l]), static_cast<int>(gi[l]), g,
-                     static_cast<int>(ui[l]), NT[l], nw[l], static_cast<int>(tot_u[l]), base[l]);
-      ++gi[l];
-      ui[l] += static_cast<uint32_t>(g.nch * g.ntok);
+      const uint32_t gi = l == 0 ? g0 : g1, ui = l == 0 ? u0 : u1;
+      a.groups[l * T + gi] = g;
+      a.ustart[l * (T + 1) + gi] = static_cast<int32_t>(ui);
+      if (g.nch > 0) {
+        if (l == 0) write_starts(a, sp0, static_cast<int>(gi), g, static_cast<int>(ui));
+        else write_starts(a, sp1, static_cast<int>(gi), g, static_cast<int>(ui));
+      }
+      const uint32_t units = static_cast<uint32_t>(g.nch * g.ntok);
+      if (l == 0) {
+        g0 += 1;
+        u0 += units;
+      } else {
+        g1 += 1;
+        u1 += units;
+      }
     }
   }
   if (tid == 0) {
     for (int l = 0; l < 2; ++l) {
-      a.hdr->ngroups[l] = static_cast<int32_t>(tot_g[l]);
-      a.hdr->units[l] = static_cast<int32_t>(tot_u[l]);
-      a.ustart[l * (T + 1) + tot_g[l]] = static_cast<int32_t>(tot_u[l]);
+      a.hdr->ngroups[l] = static_cast<int32_t>(tot[2 * l]);
+      a.hdr->units[l] = static_cast<int32_t>(tot[2 * l + 1]);
+      a.ustart[l * (T + 1) + tot[2 * l]] = static_cast<int32_t>(tot[2 * l + 1]);
     }
+  }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(KArgs a) {
+  __shared__ uint32_t sh[64];
+  __shared__ int32_t s_qsl[kPlanLdsRequests + 1];
+  __shared__ int32_t s_klen[kPlanLdsRequests];
+  __shared__ int32_t s_smod[kPlanLdsRequests];
+  const int tid = threadIdx.x;
+  // every start entry begins as "no work" (the barriers below order these
+  // stores before the ones the plan writes); workgroups whose range starts
+  // past the last item of their list keep it
+  for (int w = tid; w < a.score_grid; w += kPlanThreads) {
+    WgStart st = {};
+    st.g = -1;
+    a.wgs[w] = st;
+  }
+  if (a.B <= kPlanLdsRequests) {
+    for (int i = tid; i <= a.B; i += kPlanThreads) {
+      s_qsl[i] = a.qsl[i];
+      if (i < a.B) {
+        s_klen[i] = a.klen[i];
+        s_smod[i] = a.smod ? a.smod[i] : 0;
+      }
+    }
+    __syncthreads();
+    plan_body(a, Meta{s_qsl, s_klen, a.smod ? s_smod : nullptr}, sh);
+  } else {
+    plan_body(a, global_meta(a), sh);
   }
 }
 
@@ -1340,7 +1481,11 @@ int launch(const qli_params* p, const WsLayout& w, void* stream) {
   const unsigned T = static_cast<unsigned>(p->num_tokens);
   if (consumer) {
     Stamp s(QLI_KERNEL_CONSUMER_PREP, st);
-    consumer_prep_kernel<<<T, kPrepThreads, 0, st>>>(a);
+    const int64_t max_blocks = (static_cast<int64_t>(p->max_k_len) + 7) / 8;
+    if (max_blocks <= 32 * static_cast<int64_t>(kPrepBitmapWords))
+      consumer_prep_kernel<<<T, kPrepThreads, 0, st>>>(a);
+    else
+      consumer_prep_sort_kernel<<<T, kPrepThreads, 0, st>>>(a);
   }
   {
     Stamp s(QLI_KERNEL_PLAN, st);

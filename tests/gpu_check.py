@@ -15,14 +15,17 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_gpu(pb, cand_in=None, debug=False, layout=None, status=None):
-    """One library call on cuda:0; numpy outputs."""
+def run_gpu(pb, cand_in=None, debug=False, layout=None, status=None, max_k_len=None):
+    """One library call on cuda:0; numpy outputs (max_k_len: a looser bound
+    than the problem's longest context)."""
     import torch
 
     import quantized_top_indexer_amd as Q
     from qli_workloads.device import call_kwargs, to_device
     dev = to_device(pb, "cuda", cand_in=cand_in, **(layout or {}))
     kw = call_kwargs(pb, dev)
+    if max_k_len is not None:
+        kw["max_k_len"] = max_k_len
     if pb.mode == 3 and kw["cand_in"] is None:
         raise ValueError("consumer call without candidates")
     idx, cand, dbg = Q.score_topk(**kw, debug_scores=debug, status_out=status)

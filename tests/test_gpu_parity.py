@@ -98,6 +98,24 @@ def test_heavy_ties(mode):
     check_invariants(pb, gpu)
 
 
+def test_consumer_long_context_bound():
+    """A context bound above 2^21 positions takes the sorting candidate
+    preparation instead of the bitmap one: same outputs, same as the oracle."""
+    pb = small_problem(320, ratio=2, N=32, mode=3, topk=100, cb_in=128,
+                       requests=((3, 3000), (1, 1), (2, 15)), cand_policy="messy")
+    base = run_gpu(pb, debug=True)
+    bound = (1 << 21) + 8
+    R = pb.k_pages.shape[1]
+    bt = np.zeros((pb.block_table.shape[0], -(-bound // R)), np.int32)
+    bt[:, :pb.block_table.shape[1]] = pb.block_table
+    pb.block_table = bt
+    big = run_gpu(pb, debug=True, max_k_len=bound)
+    assert np.array_equal(base["topk"], big["topk"])
+    L = base["scores"].shape[1]
+    assert np.array_equal(base["scores"], big["scores"][:, :L], equal_nan=True)
+    compare(pb, big, oracle_rows(pb, scores=True))
+
+
 def test_layout_invariance():
     """A larger page stride with K and scales moved inside the page gives
     identical outputs (the kernels only follow the strides)."""
