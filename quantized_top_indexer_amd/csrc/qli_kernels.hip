@@ -701,20 +701,23 @@ __device__ Cursor next_item(const ListView& L, Cursor cu, int hi) {
 // page 0, row 0, which always exists, and is masked through its scale), so
 // that the number of loads in flight is fixed and known to the compiler.
 //
-// Lane j < 8 of wave w owns block q = 4j + w of the item's 32 blocks of 8
-// slots.  stage_addr only issues the lookup of that block's page (dense:
-// block-table entry; consumer: the prepared page row of the slot block) and
-// records what it needs to check it; resolve() uses the loaded value later.
+// Lane j < 8 of wave w owns block q of the item's 32 blocks of 8 slots:
+// q = 4j + w when the waves share the item (multi groups), q = 8w + j when
+// each wave stages the 64 slots it scores itself (OWN, single groups: the
+// waves then need no workgroup barrier per item).  stage_addr only issues
+// the lookup of that block's page (dense: block-table entry; consumer: the
+// prepared page row of the slot block) and records what it needs to check
+// it; resolve() uses the loaded value later.
 struct Addr {
   int raw;   // loaded block-table entry / prepared page row
   int meta;  // bit 31: block wanted; bit 30: table index in range; low bits: row in page
 };
 
-template <bool CONSUMER>
+template <bool CONSUMER, bool OWN>
 __device__ __forceinline__ void stage_addr(const KArgs& a, const Group& gr, int c, bool valid,
                                            int wave, int lane, Addr& ad) {
   const int j = lane & 7;
-  const int q = 4 * j + wave;
+  const int q = OWN ? 8 * wave + j : 4 * j + wave;
   if (CONSUMER) {
     const int s = c * 32 + q;
     ad.raw = a.srow[static_cast<int64_t>(gr.t0) * a.cb_in + min(s, a.cb_in - 1)];
@@ -763,17 +766,18 @@ __device__ __forceinline__ void stage_load(const KArgs& a, int v, int lane, i32x
 
 // Into LDS: K tile rows with the XOR swizzle, scales of valid blocks (0xFFFF
 // halves mark a block without K rows).
+template <bool OWN>
 __device__ __forceinline__ void stage_store(int8_t* tile, uint16_t* ksc, const i32x4 (&kr)[8],
                                             const i32x4& sc, int v, int wave, int lane) {
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const int row = 8 * (4 * u + wave) + (lane >> 3);
+    const int row = 8 * (OWN ? 8 * wave + u : 4 * u + wave) + (lane >> 3);
     const int col = lane & 7;
     *reinterpret_cast<i32x4*>(tile + row * 128 + ((col ^ (row & 7)) << 4)) = kr[u];
   }
   if (lane < 8) {
     const i32x4 none = {-1, -1, -1, -1};
-    *reinterpret_cast<i32x4*>(ksc + 8 * (4 * lane + wave)) = v < 0 ? none : sc;
+    *reinterpret_cast<i32x4*>(ksc + 8 * (OWN ? 8 * wave + lane : 4 * lane + wave)) = v < 0 ? none : sc;
   }
 }
 
@@ -961,19 +965,19 @@ __device__ void run_multi(const KArgs& a, const ListView& L, Cursor cur, int hi,
   Cursor n1 = next_item(L, cur, hi);
   Cursor n2 = next_item(L, n1, hi);
   Addr ad;
-  stage_addr<CONSUMER>(a, cur.grp, cur.c, cur.valid, wave, lane, ad);
+  stage_addr<CONSUMER, false>(a, cur.grp, cur.c, cur.valid, wave, lane, ad);
   i32x4 kr[8];
   i32x4 sc;
   int v = resolve<CONSUMER>(a, ad, bad);
-  stage_addr<CONSUMER>(a, n1.grp, n1.c, n1.valid, wave, lane, ad);
+  stage_addr<CONSUMER, false>(a, n1.grp, n1.c, n1.valid, wave, lane, ad);
   stage_load<false>(a, v, lane, kr, sc);
   QState<NH, false> qs;
   qs.tok = -1;
   int buf = 0;
   while (cur.valid) {
-    stage_store(tile[buf], ksc[buf], kr, sc, v, wave, lane);
+    stage_store<false>(tile[buf], ksc[buf], kr, sc, v, wave, lane);
     v = resolve<CONSUMER>(a, ad, bad);
-    stage_addr<CONSUMER>(a, n2.grp, n2.c, n2.valid, wave, lane, ad);
+    stage_addr<CONSUMER, false>(a, n2.grp, n2.c, n2.valid, wave, lane, ad);
     stage_load<false>(a, v, lane, kr, sc);
     __syncthreads();
     const Group& gr = cur.grp;
@@ -995,10 +999,13 @@ __device__ void run_multi(const KArgs& a, const ListView& L, Cursor cur, int hi,
   }
 }
 
-// Single-token groups (decode shapes): wave w scores sub-tile w of every
-// item.  Per token segment the queries are loaded once; inside a segment the
-// loop body has a fixed set of memory operations and keeps two items of K in
-// flight (register sets A and B alternate; the body is unrolled twice).
+// Single-token groups (decode shapes): wave w stages and scores sub-tile w
+// of every item in its own LDS rows, so inside a token segment the waves
+// run independently (an LDS write and a later read of the same wave are
+// ordered without a barrier).  Per segment the queries are loaded once
+// (workgroup barriers); inside it the loop body has a fixed set of memory
+// operations and keeps two items of K in flight (register sets A and B
+// alternate; the body is unrolled twice).
 // Each step resolves the block rows looked up one step earlier, issues the
 // next lookup, then the K loads: with in-order memory counters a lookup is
 // always older than the K loads that must stay in flight.
@@ -1020,29 +1027,29 @@ __device__ void run_single(const KArgs& a, const ListView& L, Cursor cu, int hi,
     Addr ad;
     i32x4 krA[8], krB[8];
     i32x4 scA, scB;
-    stage_addr<CONSUMER>(a, gr, c0, true, wave, lane, ad);
+    stage_addr<CONSUMER, true>(a, gr, c0, true, wave, lane, ad);
     int vA = resolve<CONSUMER>(a, ad, bad);
-    stage_addr<CONSUMER>(a, gr, c0 + 1, c0 + 1 < c_end, wave, lane, ad);
+    stage_addr<CONSUMER, true>(a, gr, c0 + 1, c0 + 1 < c_end, wave, lane, ad);
     stage_load<true>(a, vA, lane, krA, scA);
     int vB = resolve<CONSUMER>(a, ad, bad);
-    stage_addr<CONSUMER>(a, gr, c0 + 2, c0 + 2 < c_end, wave, lane, ad);
+    stage_addr<CONSUMER, true>(a, gr, c0 + 2, c0 + 2 < c_end, wave, lane, ad);
     stage_load<true>(a, vB, lane, krB, scB);
     __syncthreads();  // queries in LDS
     for (int c = c0; c < c_end; c += 2) {
-      stage_store(tile[buf], ksc[buf], krA, scA, vA, wave, lane);
+      stage_store<true>(tile[buf], ksc[buf], krA, scA, vA, wave, lane);
       vA = resolve<CONSUMER>(a, ad, bad);
-      stage_addr<CONSUMER>(a, gr, c + 3, c + 3 < c_end, wave, lane, ad);
+      stage_addr<CONSUMER, true>(a, gr, c + 3, c + 3 < c_end, wave, lane, ad);
       stage_load<true>(a, vA, lane, krA, scA);
-      __syncthreads();
+      __builtin_amdgcn_wave_barrier();
       score_subtile<NH, MODE, DBG, true>(a, qs, tile[buf], ksc[buf], wave, t, c * kChunk + 64 * wave,
                                          n, lane, seed);
       buf ^= 1;
       if (c + 1 >= c_end) break;
-      stage_store(tile[buf], ksc[buf], krB, scB, vB, wave, lane);
+      stage_store<true>(tile[buf], ksc[buf], krB, scB, vB, wave, lane);
       vB = resolve<CONSUMER>(a, ad, bad);
-      stage_addr<CONSUMER>(a, gr, c + 4, c + 4 < c_end, wave, lane, ad);
+      stage_addr<CONSUMER, true>(a, gr, c + 4, c + 4 < c_end, wave, lane, ad);
       stage_load<true>(a, vB, lane, krB, scB);
-      __syncthreads();
+      __builtin_amdgcn_wave_barrier();
       score_subtile<NH, MODE, DBG, true>(a, qs, tile[buf], ksc[buf], wave, t,
                                          (c + 1) * kChunk + 64 * wave, n, lane, seed);
       buf ^= 1;
