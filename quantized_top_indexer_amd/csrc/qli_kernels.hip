@@ -187,11 +187,15 @@ __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uin
 
 // ReLU of two fp16 values given as bits: an fp16 is negative (or -0) exactly
 // when its bit pattern is a negative int16, so max(bits, 0) as int16 gives
-// x for x > 0 and +0 otherwise (no NaN can occur here).
+// x for x > 0 and +0 otherwise (no NaN can occur here).  Written as one
+// instruction in assembly: as a generic int16 max the compiler would pack
+// the two converted halves with an extra permute instead of converting the
+// second straight into the high half.  Its input is a VALU result, never an
+// MFMA result, so no MFMA wait states are involved.
 __device__ __forceinline__ uint32_t relu_h2(uint32_t v) {
-  const s2 x = __builtin_bit_cast(s2, v);
-  const s2 z = {0, 0};
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, z));
+  uint32_t r;
+  asm("v_pk_max_i16 %0, %1, 0" : "=v"(r) : "v"(v));
+  return r;
 }
 
 // Accumulator word holding the bits of 24576 + qk/512 (the MFMA accumulator
