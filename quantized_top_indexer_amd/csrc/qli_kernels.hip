@@ -1106,6 +1106,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(KArgs a) {
 // rows are processed chunk by chunk.  LDS: histogram (2048 bins) and scan
 // scratch.
 constexpr uint32_t kPinKey = 0xFFFFFFFFu;  // the forced block sorts above every score
+constexpr int kSelRank = 64;  // boundary bins this small are resolved by exact ranking (one wave)
 
 __host__ __device__ constexpr int sel_chunk(int bs) { return bs == 256 ? 4096 : 32 * bs; }
 
@@ -1258,7 +1259,55 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n, int cap
         hi = static_cast<uint32_t>(min(static_cast<uint64_t>(hi),
                                        static_cast<uint64_t>(blo) + (1ull << sft) - 1));
         bits = sft;
-        __syncthreads();  // misc is rewritten by the next pass
+        __syncthreads();  // misc is rewritten next
+        if (hb <= kSelRank) {
+          // few keys left in the boundary bin [lo, hi]: gather them with
+          // their indices and rank them exactly by (key desc, index asc);
+          // the key ranked krem-1 is the threshold
+          uint32_t* ck = hist;          // keys, then indices (hb <= kSelRank)
+          uint32_t* ci = hist + kSelRank;
+          uint32_t mine = 0;
+          for (int ch = 0; ch < nch; ++ch) {
+            if (MULTI && nch > 1) load(ch);
+#pragma unroll
+            for (int r = 0; r < 4 * VPT; ++r) mine += (kr[r] - lo <= hi - lo) ? 1u : 0u;
+          }
+          uint32_t mtot;
+          uint32_t at = block_exclusive_scan<BS>(mine, &mtot, sh);
+          for (int ch = 0; ch < nch; ++ch) {
+            if (MULTI && nch > 1) load(ch);
+#pragma unroll
+            for (int j = 0; j < VPT; ++j)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const uint32_t key = kr[4 * j + e];
+                if (key - lo <= hi - lo) {
+                  ck[at] = key;
+                  ci[at] = static_cast<uint32_t>(index_of(ch, j, e));
+                  ++at;
+                }
+              }
+          }
+          __syncthreads();
+          // lane q holds candidate q; wave w ranks candidates w, w + NW, ...
+          // with two ballots each
+          const bool has = static_cast<uint32_t>(lane) < mtot;
+          const uint32_t kq = has ? ck[lane] : 0u, iq = has ? ci[lane] : 0u;
+          for (uint32_t i = wave; i < mtot; i += NW) {
+            const uint32_t key = ck[i], idx = ci[i];
+            const uint32_t gt = static_cast<uint32_t>(__popcll(__ballot(has && kq > key)));
+            const uint32_t eqb =
+                static_cast<uint32_t>(__popcll(__ballot(has && kq == key && iq < idx)));
+            if (lane == 0 && gt + eqb == krem - 1) {
+              misc[0] = key;
+              misc[1] = eqb + 1;
+            }
+          }
+          __syncthreads();
+          thr = misc[0];
+          need = misc[1];
+          break;
+        }
       }
     }
   }

@@ -80,17 +80,19 @@ def test_edges(name):
     check_invariants(pb, gpu)
 
 
-@pytest.mark.parametrize("mode", [1, 2, 3])
-def test_heavy_ties(mode):
-    """K rows drawn from three patterns with one scale: each token sees at
-    most three distinct scores, so the selection is decided by position
-    among equal keys (score desc, position asc) almost everywhere."""
+@pytest.mark.parametrize("mode,patterns", [(1, 3), (2, 3), (3, 3), (1, 200), (2, 200), (3, 200)])
+def test_heavy_ties(mode, patterns):
+    """K rows drawn from a few patterns with one scale: each token sees at
+    most that many distinct scores, so the selection is decided by position
+    among equal keys (score desc, position asc).  With 3 patterns whole
+    histogram bins are ties; with 200 each value repeats ~15 times, so the
+    boundary falls inside a small run of equal keys."""
     pb = small_problem(310 + mode, ratio=1, N=32, mode=mode, topk=300, cb=64, cb_in=128,
                        requests=((2, 3000), (1, 1200), (1, 40)))
-    rng = np.random.default_rng(310 + mode)
-    pats = rng.integers(-128, 128, size=(3, 128), dtype=np.int64).astype(np.int8)
+    rng = np.random.default_rng(310 + mode + patterns)
+    pats = rng.integers(-128, 128, size=(patterns, 128), dtype=np.int64).astype(np.int8)
     P, R, _ = pb.k_pages.shape
-    pb.k_pages = pats[np.arange(P * R) % 3].reshape(P, R, 128).copy()
+    pb.k_pages = pats[rng.integers(0, patterns, size=P * R)].reshape(P, R, 128).copy()
     pb.s_pages = np.full((P, R), 0x3C00, dtype=np.uint16)
     gpu = run_gpu(pb, debug=True)
     orc = oracle_rows(pb, scores=True)
