@@ -1107,6 +1107,13 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(KArgs a) {
 // scratch.
 constexpr uint32_t kPinKey = 0xFFFFFFFFu;  // the forced block sorts above every score
 constexpr int kSelRank = 64;  // boundary bins this small are resolved by exact ranking (one wave)
+constexpr int kSelSampleMin = 12288;  // rows with fewer scores go straight to the radix passes
+// most keys gathered from a sampled bracket (an eighth of a chunk; the bracket
+// holds about 4 % of the row)
+__host__ __device__ constexpr int sel_cand(int bs) { return (bs == 256 ? 4096 : 32 * bs) / 8; }
+__host__ __device__ constexpr int sel_lds_words(int bs) {
+  return 2048 + 64 + 8 + 2 * sel_cand(bs) + 2 * kSelRank + QLI_MAX_TOPK;
+}
 
 __host__ __device__ constexpr int sel_chunk(int bs) { return bs == 256 ? 4096 : 32 * bs; }
 
@@ -1119,6 +1126,103 @@ struct MaxOp {
 struct AddOp {
   __device__ __forceinline__ uint32_t operator()(uint32_t x, uint32_t y) const { return x + y; }
 };
+
+// Threshold search among the keys that each(f) visits (f(key, index) for
+// this thread's share), restricted to [lo, hi], of which the best krem are
+// wanted: radix passes split the range 2048 ways until the boundary bin is
+// taken whole, is one key value, or holds at most kSelRank keys, which are
+// then ranked exactly by (key desc, index asc) with two ballots each.  On
+// return keys > thr are taken plus the first `need` keys == thr.
+template <int BS, class Each>
+__device__ __forceinline__ void refine_threshold(Each each, uint32_t lo, uint32_t hi, uint32_t krem,
+                                                 uint32_t& thr, uint32_t& need, uint32_t* hist,
+                                                 uint32_t* sh, uint32_t* misc, uint32_t* rk,
+                                                 uint32_t* ri) {
+  constexpr int NW = BS / 64;
+  constexpr int BPT = 2048 / BS;  // histogram bins per thread
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int bits = hi == lo ? 0 : 32 - __clz(static_cast<int>(hi - lo));
+#pragma unroll 1
+  while (true) {
+    const int sft = max(0, bits - 11);
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) hist[tid * BPT + j] = 0;
+    __syncthreads();
+    each([&](uint32_t key, int) {
+      if (key - lo <= hi - lo) atomicAdd(&hist[(key - lo) >> sft], 1u);
+    });
+    __syncthreads();
+    uint32_t c = 0;
+    uint32_t hv[BPT];
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      hv[j] = hist[tid * BPT + j];
+      c += hv[j];
+    }
+    uint32_t total;
+    const uint32_t excl = block_exclusive_scan<BS>(c, &total, sh);
+    const uint32_t above_t = total - excl - c;  // keys in higher bins
+    if (above_t < krem && above_t + c >= krem) {
+      uint32_t cum = above_t;
+      for (int j = BPT - 1; j >= 0; --j) {
+        if (cum + hv[j] >= krem) {
+          misc[0] = static_cast<uint32_t>(tid * BPT + j);
+          misc[1] = cum;
+          misc[2] = hv[j];
+          break;
+        }
+        cum += hv[j];
+      }
+    }
+    __syncthreads();
+    const uint32_t b = misc[0], above = misc[1], hb = misc[2];
+    krem -= above;
+    const uint32_t blo = lo + (b << sft);
+    if (hb == krem) {  // the whole boundary bin is taken
+      thr = blo - 1;
+      need = 0;
+      return;
+    }
+    if (sft == 0) {
+      thr = blo;
+      need = krem;
+      return;
+    }
+    lo = blo;
+    hi = static_cast<uint32_t>(min(static_cast<uint64_t>(hi),
+                                   static_cast<uint64_t>(blo) + (1ull << sft) - 1));
+    bits = sft;
+    if (tid == 0) misc[3] = 0;
+    __syncthreads();  // misc is rewritten next
+    if (hb <= static_cast<uint32_t>(kSelRank)) {
+      each([&](uint32_t key, int idx) {
+        if (key - lo <= hi - lo) {
+          const uint32_t slot = atomicAdd(&misc[3], 1u);
+          rk[slot] = key;
+          ri[slot] = static_cast<uint32_t>(idx);
+        }
+      });
+      __syncthreads();
+      // lane q holds candidate q; wave w ranks candidates w, w + NW, ...
+      const uint32_t m = hb;
+      const bool has = static_cast<uint32_t>(lane) < m;
+      const uint32_t kq = has ? rk[lane] : 0u, iq = has ? ri[lane] : 0u;
+      for (uint32_t i = wave; i < m; i += NW) {
+        const uint32_t key = rk[i], idx = ri[i];
+        const uint32_t gt = static_cast<uint32_t>(__popcll(__ballot(has && kq > key)));
+        const uint32_t eqb = static_cast<uint32_t>(__popcll(__ballot(has && kq == key && iq < idx)));
+        if (lane == 0 && gt + eqb == krem - 1) {
+          misc[0] = key;
+          misc[1] = eqb + 1;
+        }
+      }
+      __syncthreads();
+      thr = misc[0];
+      need = misc[1];
+      return;
+    }
+  }
+}
 
 // Select the best min(k, #nonzero) of keys[0..n) by (key desc, index asc)
 // and write map(index) for them in ascending index order to out[0..k),
@@ -1142,6 +1246,14 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n, int cap
   uint32_t* hist = lds;
   uint32_t* sh = lds + 2048;
   uint32_t* misc = lds + 2048 + 64;
+  uint32_t* ck = lds + 2048 + 64 + 8;   // bracket keys, then their indices
+  uint32_t* ci = ck + sel_cand(BS);
+  uint32_t* rk = ci + sel_cand(BS);     // boundary-bin keys for exact ranking, then indices
+  uint32_t* ri = rk + kSelRank;
+  int32_t* ol = reinterpret_cast<int32_t*>(ri + kSelRank);  // winners' key indices (<= 2048)
+  auto refine = [&](auto each, uint32_t lo, uint32_t hi, uint32_t kr_, uint32_t& t_, uint32_t& n_) {
+    refine_threshold<BS>(each, lo, hi, kr_, t_, n_, hist, sh, misc, rk, ri);
+  };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nch = MULTI ? (n + CHUNK - 1) / CHUNK : 1;
   uint32_t kr[4 * VPT];
@@ -1204,117 +1316,127 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n, int cap
     if (krem == 0) {
       thr = kPinKey - 1;
     } else {
-      uint32_t lo = mn, hi = mx;
-      int bits = hi == lo ? 0 : 32 - __clz(static_cast<int>(hi - lo));
-      constexpr int BPT = 2048 / BS;  // histogram bins per thread
-#pragma unroll 1
-      while (true) {
-        const int sft = max(0, bits - 11);
-#pragma unroll
-        for (int j = 0; j < BPT; ++j) hist[tid * BPT + j] = 0;
-        __syncthreads();
+      // the keys of this thread, as (key, index) pairs (reloading chunks)
+      auto each_reg = [&](auto f) {
         for (int ch = 0; ch < nch; ++ch) {
           if (MULTI && nch > 1) load(ch);
 #pragma unroll
-          for (int r = 0; r < 4 * VPT; ++r) {
-            const uint32_t key = kr[r];
-            if (key >= lo && key <= hi) atomicAdd(&hist[(key - lo) >> sft], 1u);
-            if ((r & 7) == 7) __builtin_amdgcn_sched_barrier(0);  // bounds live addresses
+          for (int j = 0; j < VPT; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f(kr[4 * j + e], index_of(ch, j, e));
+        }
+      };
+      bool done = false;
+      if (!MULTI && cnt >= static_cast<uint32_t>(kSelSampleMin)) {
+        // Bracket from a sample: two keys per thread go into a histogram
+        // over [mn, mx]; the bins around the sample's estimate of the
+        // threshold rank (+-3 sigma) give a key range [blo, bhi].  One
+        // counting sweep checks that the threshold lies inside; its keys
+        // (about 4 % of the row) are gathered and searched alone.
+        const int bits0 = mx == mn ? 0 : 32 - __clz(static_cast<int>(mx - mn));
+        const int sft0 = max(0, bits0 - 11);
+        constexpr int BPT = 2048 / BS;
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) hist[tid * BPT + j] = 0;
+        if (tid == 0) misc[4] = 0;
+        __syncthreads();
+        uint32_t ns = 0;
+#pragma unroll
+        for (int r = 0; r < 4 * VPT; r += 2 * VPT) {
+          const uint32_t key = kr[r];
+          if (key != 0 && key != kPinKey) {
+            atomicAdd(&hist[(key - mn) >> sft0], 1u);
+            ++ns;
           }
         }
+        ns = wave_allreduce(ns, AddOp{});
+        if (lane == 0) atomicAdd(&misc[4], ns);
         __syncthreads();
+        const uint32_t nsamp = misc[4];
+        // expected rank of the threshold among the samples, from the top
+        const float rexp = static_cast<float>(krem) * static_cast<float>(nsamp) / static_cast<float>(cnt);
+        const float dev = 3.0f * sqrtf(rexp) + 4.0f;
+        const uint32_t r_hi = static_cast<uint32_t>(max(0.0f, rexp - dev));      // keys above the bracket
+        const uint32_t r_lo = static_cast<uint32_t>(min(static_cast<float>(nsamp), rexp + dev));
         uint32_t c = 0;
+        uint32_t hv[BPT];
 #pragma unroll
-        for (int j = 0; j < BPT; ++j) c += hist[tid * BPT + j];
+        for (int j = 0; j < BPT; ++j) {
+          hv[j] = hist[tid * BPT + j];
+          c += hv[j];
+        }
         uint32_t total;
         const uint32_t excl = block_exclusive_scan<BS>(c, &total, sh);
-        const uint32_t above_t = total - excl - c;  // keys in higher bins
-        if (above_t < krem && above_t + c >= krem) {
-          uint32_t cum = above_t;
-          for (int j = BPT - 1; j >= 0; --j) {
-            const uint32_t h = hist[tid * BPT + j];
-            if (cum + h >= krem) {
-              misc[0] = static_cast<uint32_t>(tid * BPT + j);
-              misc[1] = cum;
-              misc[2] = h;
-              break;
+        const uint32_t above_t = total - excl - c;
+        // bin holding sample rank r (counted from the top, 0-based) -> misc[slot]
+        auto find = [&](uint32_t r, int slot) {
+          if (above_t <= r && r < above_t + c) {
+            uint32_t cum = above_t;
+            for (int j = BPT - 1; j >= 0; --j) {
+              if (cum + hv[j] > r) {
+                misc[slot] = static_cast<uint32_t>(tid * BPT + j);
+                break;
+              }
+              cum += hv[j];
             }
-            cum += h;
           }
+        };
+        if (tid == 0) {
+          misc[5] = 2047;  // r_hi above every sample: bracket reaches the top
+          misc[6] = 0;     // r_lo below every sample: bracket reaches mn
         }
         __syncthreads();
-        const uint32_t b = misc[0], above = misc[1], hb = misc[2];
-        krem -= above;
-        const uint32_t blo = lo + (b << sft);
-        if (hb == krem) {  // the whole boundary bin is taken
-          thr = blo - 1;
-          break;
+        if (r_hi < total) find(r_hi, 5);
+        if (r_lo < total) find(r_lo, 6);
+        __syncthreads();
+        const uint32_t b_top = r_hi < total ? misc[5] : 2047u;
+        const uint32_t b_bot = r_lo < total ? misc[6] : 0u;
+        const uint32_t blo = mn + (b_bot << sft0);
+        const uint32_t bhi = static_cast<uint32_t>(
+            min(static_cast<uint64_t>(mx), static_cast<uint64_t>(mn) + ((static_cast<uint64_t>(b_top) + 1) << sft0) - 1));
+        // keys above the bracket and inside it, packed above << 16 | inside
+        // (a chunk holds at most 32768 keys); the prefix places the gather
+        uint32_t cnt2 = 0;
+#pragma unroll
+        for (int r = 0; r < 4 * VPT; ++r) {
+          const uint32_t key = kr[r];
+          cnt2 += (key > bhi && key != kPinKey) ? (1u << 16) : 0u;
+          cnt2 += (key - blo <= bhi - blo) ? 1u : 0u;
         }
-        if (sft == 0) {
-          thr = blo;
-          need = krem;
-          break;
-        }
-        lo = blo;
-        hi = static_cast<uint32_t>(min(static_cast<uint64_t>(hi),
-                                       static_cast<uint64_t>(blo) + (1ull << sft) - 1));
-        bits = sft;
-        __syncthreads();  // misc is rewritten next
-        if (hb <= kSelRank) {
-          // few keys left in the boundary bin [lo, hi]: gather them with
-          // their indices and rank them exactly by (key desc, index asc);
-          // the key ranked krem-1 is the threshold
-          uint32_t* ck = hist;          // keys, then indices (hb <= kSelRank)
-          uint32_t* ci = hist + kSelRank;
-          uint32_t mine = 0;
-          for (int ch = 0; ch < nch; ++ch) {
-            if (MULTI && nch > 1) load(ch);
+        uint32_t tot2;
+        uint32_t at = block_exclusive_scan<BS>(cnt2, &tot2, sh) & 0xFFFFu;
+        const uint32_t n_above = tot2 >> 16, n_in = tot2 & 0xFFFFu;
+        if (n_above < krem && n_above + n_in >= krem && n_in <= static_cast<uint32_t>(sel_cand(BS))) {
+          // gather the bracket's keys and search them alone
 #pragma unroll
-            for (int r = 0; r < 4 * VPT; ++r) mine += (kr[r] - lo <= hi - lo) ? 1u : 0u;
-          }
-          uint32_t mtot;
-          uint32_t at = block_exclusive_scan<BS>(mine, &mtot, sh);
-          for (int ch = 0; ch < nch; ++ch) {
-            if (MULTI && nch > 1) load(ch);
+          for (int j = 0; j < VPT; ++j)
 #pragma unroll
-            for (int j = 0; j < VPT; ++j)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const uint32_t key = kr[4 * j + e];
-                if (key - lo <= hi - lo) {
-                  ck[at] = key;
-                  ci[at] = static_cast<uint32_t>(index_of(ch, j, e));
-                  ++at;
-                }
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t key = kr[4 * j + e];
+              if (key - blo <= bhi - blo) {
+                ck[at] = key;
+                ci[at] = static_cast<uint32_t>(index_of(0, j, e));
+                ++at;
               }
-          }
-          __syncthreads();
-          // lane q holds candidate q; wave w ranks candidates w, w + NW, ...
-          // with two ballots each
-          const bool has = static_cast<uint32_t>(lane) < mtot;
-          const uint32_t kq = has ? ck[lane] : 0u, iq = has ? ci[lane] : 0u;
-          for (uint32_t i = wave; i < mtot; i += NW) {
-            const uint32_t key = ck[i], idx = ci[i];
-            const uint32_t gt = static_cast<uint32_t>(__popcll(__ballot(has && kq > key)));
-            const uint32_t eqb =
-                static_cast<uint32_t>(__popcll(__ballot(has && kq == key && iq < idx)));
-            if (lane == 0 && gt + eqb == krem - 1) {
-              misc[0] = key;
-              misc[1] = eqb + 1;
             }
-          }
           __syncthreads();
-          thr = misc[0];
-          need = misc[1];
-          break;
+          auto each_cand = [&](auto f) {
+            for (uint32_t i = tid; i < n_in; i += BS) f(ck[i], static_cast<int>(ci[i]));
+          };
+          krem -= n_above;
+          refine(each_cand, blo, bhi, krem, thr, need);
+          done = true;
         }
+        __syncthreads();  // sh, misc and the candidate lists are reused
       }
+      if (!done) refine(each_reg, mn, mx, krem, thr, need);
     }
   }
 
   // ordered compaction: a key's output slot is (keys > thr before it) +
   // min(need, keys == thr before it), both counted in index order (packed
-  // as gt << 16 | eq; a chunk holds at most 32768 keys)
+  // as gt << 16 | eq; a chunk holds at most 32768 keys).  The winners' key
+  // indices are staged in LDS and written out in order.
   uint32_t run_gt = 0, run_eq = 0;
   for (int ch = 0; ch < nch; ++ch) {
     if (MULTI && nch > 1) load(ch);
@@ -1350,16 +1472,16 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n, int cap
         const uint32_t f = flag(kr[4 * j + e]);
         const uint32_t eq_rank = run_eq + (before & 0xFFFFu);
         const bool sel = f == (1u << 16) || (f == 1u && eq_rank < need);
-        if (sel) out[run_gt + (before >> 16) + min(need, eq_rank)] = map(index_of(ch, j, e));
+        if (sel) ol[run_gt + (before >> 16) + min(need, eq_rank)] = index_of(ch, j, e);
         before += f;
       }
-      __builtin_amdgcn_sched_barrier(0);  // bounds live addresses
     }
     run_gt += tot >> 16;
     run_eq += tot & 0xFFFFu;
   }
+  __syncthreads();
   const int count = static_cast<int>(run_gt + min(need, run_eq));
-  for (int i = count + tid; i < k; i += BS) out[i] = -1;
+  for (int i = tid; i < k; i += BS) out[i] = i < count ? map(ol[i]) : -1;
 }
 
 struct MapIdentity {
@@ -1373,7 +1495,7 @@ struct MapSlots {
 
 template <int BS, bool MULTI>
 __global__ __launch_bounds__(BS) void select_kernel(KArgs a) {
-  __shared__ uint32_t sel_lds[2048 + 64 + 8];
+  __shared__ uint32_t sel_lds[sel_lds_words(BS)];
   const int t = blockIdx.x;
   if (blockIdx.y == 0) {
     int32_t* out = a.topk_out + static_cast<int64_t>(t) * a.topk;
