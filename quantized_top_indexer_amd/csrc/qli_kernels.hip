@@ -865,79 +865,72 @@ __device__ __forceinline__ void load_q_lds(const KArgs& a, int t, i32x4* fr, uin
   }
 }
 
-// One (token, 64-slot sub-tile) of the current item: MFMA + epilogue.
+// Scoring of one (token, 64-slot sub-tile) of the current item, in 32-head
+// passes: mfma_pass, then epi_pass per pass, then finish_subtile.
 //
 // MFMA operands (v_mfma_i32_32x32x32_i8, 64 lanes): A = queries, lane l
 // supplies row l%32 of a 32-head tile, 16 bytes of the head dimension;
 // B = keys, lane l supplies column l%32 (one position), the same 16 bytes
 // (dim d = 64*(l/32) + 16*step + byte for both, so the reduction pairs
 // q[h,d] with k[j,d]).  C: lane l holds column l%32, rows 8*(i/4) +
-// 4*(l/32) + i%4.  With the A permutation, lanes 0..31 hold heads
-// 0..N/2-1 and lanes 32..63 heads N/2..N-1 of the same 64 positions, and
-// one v_permlane32_swap per register pair leaves each lane L with all N
-// heads of slot s0+L, summed in ascending head order.
-//
+// 4*(l/32) + i%4.  With the A permutation, lanes 0..31 hold heads 32p ..
+// 32p+15 and lanes 32..63 heads 32p+16 .. 32p+31 of the same 64 positions,
+// and one v_permlane32_swap per register pair leaves each lane L with all
+// 32 heads of the pass for slot s0+L, summed in ascending head order.
+template <class QSrc>
+__device__ __forceinline__ void mfma_pass(const QSrc& qs, const int8_t* tile, int sub, int ps, int lane,
+                                          const i32x16& seed, i32x16 (&acc)[2]) {
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int row = 64 * sub + 32 * n + (lane & 31);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int col = 4 * (lane >> 5) + s;
+      const i32x4 bk = *reinterpret_cast<const i32x4*>(tile + row * 128 + ((col ^ (row & 7)) << 4));
+      acc[n] = __builtin_amdgcn_mfma_i32_32x32x32_i8(qs.frag(ps, s, lane), bk, s == 0 ? seed : acc[n],
+                                                     0, 0, 0);
+    }
+  }
+}
+
+// x = fp16(qk/1024), ReLU, p = fp16(x * m) (packed two heads per word), then
+// the 32 heads of the pass added to sum in ascending order.
+template <class QSrc>
+__device__ __forceinline__ void epi_pass(const QSrc& qs, const i32x16 (&acc)[2], int ps, int lane,
+                                         float one, float& sum) {
+  uint32_t pk[2][8];
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const h2 x0 = {qk_to_half(acc[n][i]), qk_to_half(acc[n][i + 1])};
+      const h2 x = as_h2(relu_h2(as_u32(x0)));
+      pk[n][i >> 1] = as_u32(x * qs.mul(ps * 8 + (i >> 1), lane));
+    }
+  uint32_t hi[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const auto r = __builtin_amdgcn_permlane32_swap(pk[0][j], pk[1][j], false, false);
+    const h2 pl = as_h2(static_cast<uint32_t>(r[0]));
+    sum = add_h(sum, pl[0], one);
+    sum = add_h(sum, pl[1], one);
+    hi[j] = r[1];
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const h2 ph = as_h2(hi[j]);
+    sum = add_h(sum, ph[0], one);
+    sum = add_h(sum, ph[1], one);
+  }
+}
+
+// Score (× k_scale), key, block maximum and stores of slot s0 + lane.
 // Every store is unconditional (slots past n_i receive key 0, block maxima
 // are written by all 8 lanes of a block), so the memory operations of a
 // sub-tile are fixed.
-template <int NH, int MODE, bool DBG, bool SPLIT, class QSrc>
-__device__ __forceinline__ void score_subtile(const KArgs& a, const QSrc& qs,
-                                              const int8_t* tile, const uint16_t* ksc, int sub,
-                                              int t, int s0, int n_i, int lane, const i32x16& seed) {
-  constexpr int MT = NH / 32;
-  constexpr int PASSES = SPLIT ? MT : 1;     // head tiles scored one after the other
-  constexpr int TPP = SPLIT ? 1 : MT;        // head tiles per pass
-  constexpr int PAIRS = 8 * TPP;             // packed pairs per lane group per pass
-  const float one = a.one;
-  float sum = 0.0f;
-  // the passes stay a loop: overlapping them would keep two head tiles of
-  // accumulators live
-#pragma unroll 1
-  for (int ps = 0; ps < PASSES; ++ps) {
-    i32x16 acc[TPP][2];
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int row = 64 * sub + 32 * n + (lane & 31);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int col = 4 * (lane >> 5) + s;
-        const i32x4 bk = *reinterpret_cast<const i32x4*>(tile + row * 128 + ((col ^ (row & 7)) << 4));
-#pragma unroll
-        for (int m = 0; m < TPP; ++m)
-          acc[m][n] = __builtin_amdgcn_mfma_i32_32x32x32_i8(qs.frag(ps * TPP + m, s, lane), bk,
-                                                           s == 0 ? seed : acc[m][n], 0, 0, 0);
-      }
-    }
-    // x = fp16(qk/1024), ReLU, p = fp16(x * m), packed two heads per word
-    uint32_t pk[2][PAIRS];
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int m = 0; m < TPP; ++m)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          const int32_t a0 = acc[m][n][i], a1 = acc[m][n][i + 1];
-          const h2 x0 = {qk_to_half(a0), qk_to_half(a1)};
-          const h2 x = as_h2(relu_h2(as_u32(x0)));
-          pk[n][(16 * m + i) >> 1] = as_u32(x * qs.mul(ps * PAIRS + ((16 * m + i) >> 1), lane));
-        }
-    uint32_t hi[PAIRS];
-#pragma unroll
-    for (int j = 0; j < PAIRS; ++j) {
-      const auto r = __builtin_amdgcn_permlane32_swap(pk[0][j], pk[1][j], false, false);
-      const uint32_t lo = r[0];
-      const h2 pl = as_h2(lo);
-      sum = add_h(sum, pl[0], one);
-      sum = add_h(sum, pl[1], one);
-      hi[j] = r[1];
-    }
-#pragma unroll
-    for (int j = 0; j < PAIRS; ++j) {
-      const h2 ph = as_h2(hi[j]);
-      sum = add_h(sum, ph[0], one);
-      sum = add_h(sum, ph[1], one);
-    }
-  }
+template <int MODE, bool DBG>
+__device__ __forceinline__ void finish_subtile(const KArgs& a, const uint16_t* ksc, int sub, int t, int s0,
+                                               int n_i, int lane, float sum) {
   const int slot = s0 + lane;
   const uint16_t kb = ksc[64 * sub + lane];
   const bool valid = slot < n_i && kb != 0xFFFFu;
@@ -959,42 +952,75 @@ __device__ __forceinline__ void score_subtile(const KArgs& a, const QSrc& qs,
   }
 }
 
-// Multi groups (prefill shapes): each item is 256 slots for up to 4 tokens;
-// wave w scores the (token, sub-tile) pairs w, w+4, ... so that with 4
-// tokens every wave keeps one token's queries.  One item of K in flight.
+// One sub-tile, the passes one after the other (a loop: overlapping them
+// would keep two head tiles of accumulators live).
+template <int NH, int MODE, bool DBG, class QSrc>
+__device__ __forceinline__ void score_subtile(const KArgs& a, const QSrc& qs,
+                                              const int8_t* tile, const uint16_t* ksc, int sub,
+                                              int t, int s0, int n_i, int lane, const i32x16& seed) {
+  float sum = 0.0f;
+#pragma unroll 1
+  for (int ps = 0; ps < NH / 32; ++ps) {
+    i32x16 acc[2];
+    mfma_pass(qs, tile, sub, ps, lane, seed, acc);
+    epi_pass(qs, acc, ps, lane, a.one, sum);
+  }
+  finish_subtile<MODE, DBG>(a, ksc, sub, t, s0, n_i, lane, sum);
+}
+
+// Multi groups (prefill shapes): each item is 256 slots for 4 consecutive
+// tokens of one request; wave w scores the four 64-slot sub-tiles of token
+// t0 + w, keeping its queries in registers.  The item's (sub-tile, pass)
+// units form a software pipeline: the MFMAs of unit u + 1 are issued
+// before the epilogue of unit u, so the matrix core runs under the VALU
+// epilogue (two accumulator sets alternate).  One item of K in flight.
 template <int NH, int MODE, bool DBG>
 __device__ void run_multi(const KArgs& a, const ListView& L, Cursor cur, int hi, int8_t (*tile)[kChunk * 128],
                           uint16_t (*ksc)[kChunk], int wave, int lane, const i32x16& seed, bool& bad) {
-  constexpr bool CONSUMER = MODE == QLI_MODE_CONSUMER;
+  constexpr int P = NH / 32;   // passes per sub-tile
+  constexpr int NU = 4 * P;    // (sub-tile, pass) units per item
   Cursor n1 = next_item(L, cur, hi);
   Cursor n2 = next_item(L, n1, hi);
   Addr ad;
-  stage_addr<CONSUMER, false>(a, cur.grp, cur.c, cur.valid, wave, lane, ad);
+  stage_addr<false, false>(a, cur.grp, cur.c, cur.valid, wave, lane, ad);
   i32x4 kr[8];
   i32x4 sc;
-  int v = resolve<CONSUMER>(a, ad, bad);
-  stage_addr<CONSUMER, false>(a, n1.grp, n1.c, n1.valid, wave, lane, ad);
+  int v = resolve<false>(a, ad, bad);
+  stage_addr<false, false>(a, n1.grp, n1.c, n1.valid, wave, lane, ad);
   stage_load<false>(a, v, lane, kr, sc);
-  QState<NH, false> qs;
+  QState<NH, true> qs;
   qs.tok = -1;
   int buf = 0;
+  const float one = a.one;
   while (cur.valid) {
     stage_store<false>(tile[buf], ksc[buf], kr, sc, v, wave, lane);
-    v = resolve<CONSUMER>(a, ad, bad);
-    stage_addr<CONSUMER, false>(a, n2.grp, n2.c, n2.valid, wave, lane, ad);
+    v = resolve<false>(a, ad, bad);
+    stage_addr<false, false>(a, n2.grp, n2.c, n2.valid, wave, lane, ad);
     stage_load<false>(a, v, lane, kr, sc);
     __syncthreads();
-    const Group& gr = cur.grp;
-    const int np = 4 * gr.ntok;
-    for (int q = wave; q < np; q += 4) {
-      const int sub = q / gr.ntok, ti = q - sub * gr.ntok;
-      const int t = gr.t0 + ti;
-      const int n_i = CONSUMER ? gr.n0 : visible(a, static_cast<int64_t>(gr.p0) + ti, gr.L);
-      const int s0 = cur.c * kChunk + 64 * sub;
-      if (s0 >= n_i) continue;
-      if (t != qs.tok) load_q<NH, false>(a, t, lane, qs);
-      score_subtile<NH, MODE, DBG, false>(a, QRegs<NH, false>{qs}, tile[buf], ksc[buf], sub, t, s0,
-                                          n_i, lane, seed);
+    const Group& gr = cur.grp;  // multi groups hold kGroupTokens tokens
+    const int t = gr.t0 + wave;
+    const int n_i = visible(a, static_cast<int64_t>(gr.p0) + wave, gr.L);
+    if (t != qs.tok) load_q<NH, true>(a, t, lane, qs);
+    const QRegs<NH, true> q{qs};
+    const int8_t* tl = tile[buf];
+    i32x16 accA[2], accB[2];
+    float sum = 0.0f;
+    mfma_pass(q, tl, 0, 0, lane, seed, accA);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      if (u + 1 < NU) {
+        if (u & 1) mfma_pass(q, tl, (u + 1) / P, (u + 1) % P, lane, seed, accA);
+        else mfma_pass(q, tl, (u + 1) / P, (u + 1) % P, lane, seed, accB);
+      }
+      epi_pass(q, (u & 1) ? accB : accA, u % P, lane, one, sum);
+      if (u % P == P - 1) {
+        finish_subtile<MODE, DBG>(a, ksc[buf], u / P, t, cur.c * kChunk + 64 * (u / P), n_i, lane, sum);
+        sum = 0.0f;
+      }
+      // each step schedules one unit's MFMAs against the previous unit's
+      // epilogue, no further (bounds the live registers)
+      __builtin_amdgcn_sched_barrier(0);
     }
     cur = n1;
     n1 = n2;
@@ -1045,7 +1071,7 @@ __device__ void run_single(const KArgs& a, const ListView& L, Cursor cu, int hi,
       stage_addr<CONSUMER, true>(a, gr, c + 3, c + 3 < c_end, wave, lane, ad);
       stage_load<true>(a, vA, lane, krA, scA);
       __builtin_amdgcn_wave_barrier();
-      score_subtile<NH, MODE, DBG, true>(a, qs, tile[buf], ksc[buf], wave, t, c * kChunk + 64 * wave,
+      score_subtile<NH, MODE, DBG>(a, qs, tile[buf], ksc[buf], wave, t, c * kChunk + 64 * wave,
                                          n, lane, seed);
       buf ^= 1;
       if (c + 1 >= c_end) break;
@@ -1054,7 +1080,7 @@ __device__ void run_single(const KArgs& a, const ListView& L, Cursor cu, int hi,
       stage_addr<CONSUMER, true>(a, gr, c + 4, c + 4 < c_end, wave, lane, ad);
       stage_load<true>(a, vB, lane, krB, scB);
       __builtin_amdgcn_wave_barrier();
-      score_subtile<NH, MODE, DBG, true>(a, qs, tile[buf], ksc[buf], wave, t,
+      score_subtile<NH, MODE, DBG>(a, qs, tile[buf], ksc[buf], wave, t,
                                          (c + 1) * kChunk + 64 * wave, n, lane, seed);
       buf ^= 1;
     }
@@ -1091,8 +1117,11 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(KArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) seed[i] = kSeedBits;
   bool bad = false;
-  if (l == 0) run_multi<NH, MODE, DBG>(a, L, cu, st.hi, tile, ksc, wave, lane, seed, bad);
-  else run_single<NH, MODE, DBG>(a, L, cu, st.hi, tile, ksc, qfr, qml, wave, lane, seed, bad);
+  // consumer tokens are always single groups
+  if (MODE != QLI_MODE_CONSUMER && l == 0)
+    run_multi<NH, MODE, DBG>(a, L, cu, st.hi, tile, ksc, wave, lane, seed, bad);
+  else
+    run_single<NH, MODE, DBG>(a, L, cu, st.hi, tile, ksc, qfr, qml, wave, lane, seed, bad);
   if (bad) raise_flag(a, QLI_DEV_BAD_PAGE);
 }
 
