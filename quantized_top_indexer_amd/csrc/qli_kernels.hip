@@ -201,13 +201,25 @@ __device__ __forceinline__ uint32_t relu_h2(uint32_t v) {
 // Accumulator word holding the bits of 24576 + qk/512 (the MFMA accumulator
 // is seeded with the bits of 24576.0f, whose ulp is 2^-9, so the integer sum
 // of the seed and qk is exactly that float for |qk| < 2^22) -> fp16(qk/1024):
-// 0.5*F - 12288 is exact, and the conversion rounds it once (RNE).  Written
-// as an fma so that it becomes one v_fma_mixlo_f16 (an fma by 1.0 would be
-// folded into an add); no inline assembly touches MFMA results, so the
-// compiler inserts the MFMA-to-VALU wait states.
+// 0.5*F - 12288 is exact, and the conversion rounds it once (RNE).  Two
+// forms, same bits:
+//  - qk_to_half: one fma written so that it becomes one v_fma_mixlo/hi_f16
+//    (fewest instructions and registers);
+//  - qk_over_1024 + a packed conversion of two values: an FP32 fma per
+//    value and one v_cvt_pk_f16_f32 per pair, faster where the VALU is the
+//    bound (the mixed-precision conversions issue at half rate).  The empty
+//    assembly statement keeps the compiler from fusing the two back into
+//    the mixed form; it emits no instruction.
+// No inline assembly touches MFMA results, so the compiler inserts the
+// MFMA-to-VALU wait states.
 constexpr int32_t kSeedBits = 0x46C00000;  // 24576.0f
 __device__ __forceinline__ _Float16 qk_to_half(int32_t acc) {
   return static_cast<_Float16>(__builtin_fmaf(__int_as_float(acc), 0.5f, -12288.0f));
+}
+__device__ __forceinline__ float qk_over_1024(int32_t acc) {
+  float y = __builtin_fmaf(__int_as_float(acc), 0.5f, -12288.0f);
+  asm volatile("" : "+v"(y));
+  return y;
 }
 
 // s + float(h) with one FP32 rounding: fma(h, one, s) with one == 1.0 held
@@ -895,7 +907,7 @@ __device__ __forceinline__ void mfma_pass(const QSrc& qs, const int8_t* tile, in
 
 // x = fp16(qk/1024), ReLU, p = fp16(x * m) (packed two heads per word), then
 // the 32 heads of the pass added to sum in ascending order.
-template <class QSrc>
+template <bool PACKED_CVT, class QSrc>
 __device__ __forceinline__ void epi_pass(const QSrc& qs, const i32x16 (&acc)[2], int ps, int lane,
                                          float one, float& sum) {
   uint32_t pk[2][8];
@@ -903,7 +915,9 @@ __device__ __forceinline__ void epi_pass(const QSrc& qs, const i32x16 (&acc)[2],
   for (int n = 0; n < 2; ++n)
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
-      const h2 x0 = {qk_to_half(acc[n][i]), qk_to_half(acc[n][i + 1])};
+      const h2 x0 = PACKED_CVT ? h2{static_cast<_Float16>(qk_over_1024(acc[n][i])),
+                                    static_cast<_Float16>(qk_over_1024(acc[n][i + 1]))}
+                               : h2{qk_to_half(acc[n][i]), qk_to_half(acc[n][i + 1])};
       const h2 x = as_h2(relu_h2(as_u32(x0)));
       pk[n][i >> 1] = as_u32(x * qs.mul(ps * 8 + (i >> 1), lane));
     }
@@ -963,7 +977,7 @@ __device__ __forceinline__ void score_subtile(const KArgs& a, const QSrc& qs,
   for (int ps = 0; ps < NH / 32; ++ps) {
     i32x16 acc[2];
     mfma_pass(qs, tile, sub, ps, lane, seed, acc);
-    epi_pass(qs, acc, ps, lane, a.one, sum);
+    epi_pass<false>(qs, acc, ps, lane, a.one, sum);
   }
   finish_subtile<MODE, DBG>(a, ksc, sub, t, s0, n_i, lane, sum);
 }
@@ -1013,13 +1027,25 @@ __device__ void run_multi(const KArgs& a, const ListView& L, Cursor cur, int hi,
         if (u & 1) mfma_pass(q, tl, (u + 1) / P, (u + 1) % P, lane, seed, accA);
         else mfma_pass(q, tl, (u + 1) / P, (u + 1) % P, lane, seed, accB);
       }
-      epi_pass(q, (u & 1) ? accB : accA, u % P, lane, one, sum);
+      epi_pass<true>(q, (u & 1) ? accB : accA, u % P, lane, one, sum);
       if (u % P == P - 1) {
         finish_subtile<MODE, DBG>(a, ksc[buf], u / P, t, cur.c * kChunk + 64 * (u / P), n_i, lane, sum);
         sum = 0.0f;
       }
       // each step schedules one unit's MFMAs against the previous unit's
-      // epilogue, no further (bounds the live registers)
+      // epilogue, no further (bounds the live registers): the K fragment
+      // reads first, then one MFMA every dozen VALU instructions, so each
+      // MFMA finds the matrix core free and its chain predecessor done
+#ifdef QLI_SCHED_GROUPS
+      if (u + 1 < NU) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+        }
+      }
+#endif
       __builtin_amdgcn_sched_barrier(0);
     }
     cur = n1;
