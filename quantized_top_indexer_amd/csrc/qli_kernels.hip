@@ -1309,8 +1309,12 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n, int cap
   auto refine = [&](auto each, uint32_t lo, uint32_t hi, uint32_t kr_, uint32_t& t_, uint32_t& n_) {
     refine_threshold<BS>(each, lo, hi, kr_, t_, n_, hist, sh, misc, rk, ri);
   };
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nch = MULTI ? (n + CHUNK - 1) / CHUNK : 1;
+  // vectors of this wave that hold any index below n (one chunk): the
+  // others are all zero and their work is skipped as a whole
+  const int nvec = MULTI ? VPT : min(VPT, max(0, (n - wave * KPW + 255) >> 8));
   uint32_t kr[4 * VPT];
   auto index_of = [&](int ch, int j, int e) {
     return ch * CHUNK + wave * KPW + 256 * j + 4 * lane + e;
@@ -1335,12 +1339,16 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n, int cap
   for (int ch = 0; ch < nch; ++ch) {
     load(ch);
 #pragma unroll
-    for (int r = 0; r < 4 * VPT; ++r) {
-      const uint32_t v = kr[r];
-      const bool s = v != 0 && v != kPinKey;
-      mn = s ? min(mn, v) : mn;
-      mx = s ? max(mx, v) : mx;
-      cnt += s ? 1u : 0u;
+    for (int j = 0; j < VPT; ++j) {
+      if (j >= nvec) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t v = kr[4 * j + e];
+        const bool s = v != 0 && v != kPinKey;
+        mn = s ? min(mn, v) : mn;
+        mx = s ? max(mx, v) : mx;
+        cnt += s ? 1u : 0u;
+      }
     }
   }
   mn = wave_allreduce(mn, MinOp{});
@@ -1376,9 +1384,11 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n, int cap
         for (int ch = 0; ch < nch; ++ch) {
           if (MULTI && nch > 1) load(ch);
 #pragma unroll
-          for (int j = 0; j < VPT; ++j)
+          for (int j = 0; j < VPT; ++j) {
+            if (j >= nvec) continue;
 #pragma unroll
             for (int e = 0; e < 4; ++e) f(kr[4 * j + e], index_of(ch, j, e));
+          }
         }
       };
       bool done = false;
@@ -1502,6 +1512,8 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n, int cap
     uint32_t wsum = 0;   // running wave total over the vectors
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
+      excl[j] = wsum;
+      if (j >= nvec) continue;
       uint32_t c = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) c += flag(kr[4 * j + e]);
@@ -1521,6 +1533,7 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n, int cap
     __syncthreads();  // sh is reused
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
+      if (j >= nvec) continue;
       uint32_t before = wbase + excl[j];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
