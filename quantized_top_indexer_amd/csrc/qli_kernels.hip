@@ -567,15 +567,24 @@ __device__ __forceinline__ void plan_body(const KArgs& a, const Meta& m, uint32_
   const int t_lo = min(T, tid * per);
   const int t_hi = min(T, t_lo + per);
   uint32_t cnt[4] = {0, 0, 0, 0};  // groups and units of list 0, then of list 1
+  // with one token per thread (T <= 1024) the second pass reuses the first's
+  // results instead of looking the request up again
+  int kind1 = 0, tv1 = 0;
+  Group g1c{};
   if (t_lo < t_hi) {
     int b = request_of(m, a.B, t_lo);
     ReqView r = request_view(a, m, b, true);
     for (int t = t_lo; t < t_hi; ++t) {
       while (t >= r.q1 && b + 1 < a.B) r = request_view(a, m, ++b, true);
       if (t < r.q0 || t >= r.q1) continue;
+      if (per == 1) tv1 = visible(a, r.S - (r.q1 - r.q0) + (t - r.q0), r.L);
       const int kind = group_kind(a, r, t);
       if (kind == 0) continue;
       const Group g = make_group(a, b, r, t, kind == 1 ? kGroupTokens : 1);
+      if (per == 1) {
+        kind1 = kind;
+        g1c = g;
+      }
       const uint32_t units = static_cast<uint32_t>(g.nch * g.ntok);
       if (kind == 1) {
         cnt[0] += 1;
@@ -603,7 +612,19 @@ __device__ __forceinline__ void plan_body(const KArgs& a, const Meta& m, uint32_
     return sp;
   };
   const Split sp0 = split(0), sp1 = split(1);
-  if (t_lo < t_hi) {
+  if (per == 1 && t_lo < t_hi) {
+    a.tokv[t_lo] = tv1;
+    if (kind1 != 0) {
+      const int l = kind1 - 1;
+      const uint32_t gi = l == 0 ? cnt[0] : cnt[2], ui = l == 0 ? cnt[1] : cnt[3];
+      a.groups[l * T + gi] = g1c;
+      a.ustart[l * (T + 1) + gi] = static_cast<int32_t>(ui);
+      if (g1c.nch > 0) {
+        if (l == 0) write_starts(a, sp0, static_cast<int>(gi), g1c, static_cast<int>(ui));
+        else write_starts(a, sp1, static_cast<int>(gi), g1c, static_cast<int>(ui));
+      }
+    }
+  } else if (t_lo < t_hi) {
     // running group index and first unit of list 0, then of list 1
     uint32_t g0 = cnt[0], u0 = cnt[1], g1 = cnt[2], u1 = cnt[3];
     int b = request_of(m, a.B, t_lo);
