@@ -13,6 +13,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qli_oracle.c")
+_SRC_QUANT = os.path.join(_HERE, "qli_quant_oracle.c")
 _LIB = os.path.join(_HERE, "libqli_oracle.so")
 # an alternative build (used by the tests that plant mistakes in a copy)
 _LOAD = os.environ.get("QLI_ORACLE_LIB", _LIB)
@@ -24,7 +25,7 @@ def build(force: bool = True) -> str:
     """Compile the oracle with gcc (no GPU toolchain involved)."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
-        subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        subprocess.run(["gcc", *CFLAGS, _SRC, _SRC_QUANT, "-o", tmp, "-lm"], check=True)
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -169,3 +170,61 @@ def f16_value(h):
     out = np.empty(h.shape, np.float64)
     lib().oracle_f16_value_array(h.ctypes.data, out.ctypes.data, h.size)
     return out
+
+
+# ---- query quantization and index-K cache write (qli_quant_oracle.c) ----
+
+DTYPE_F32, DTYPE_BF16 = 0, 1
+
+
+def _dtype_code(a):
+    if a.dtype == np.float32:
+        return DTYPE_F32
+    if a.dtype == np.uint16:  # bfloat16 bit patterns
+        return DTYPE_BF16
+    raise TypeError("rows must be float32 or bfloat16 bits (uint16)")
+
+
+def quantize_rows(x):
+    """Symmetric INT8 quantization of rows of 128 values with an FP16 scale.
+    x: float32 or bfloat16 bits (uint16), shape [..., 128].  Returns
+    (q int8 [..., 128], scale fp16 bits uint16 [...])."""
+    x = np.ascontiguousarray(x)
+    assert x.shape[-1] == 128
+    rows = int(np.prod(x.shape[:-1], dtype=np.int64))
+    q = np.zeros(x.shape, np.int8)
+    sc = np.zeros(x.shape[:-1], np.uint16)
+    L = lib()
+    L.oracle_quantize_rows.restype = None
+    L.oracle_quantize_rows.argtypes = [C.c_void_p, C.c_int, C.c_int64, C.c_void_p, C.c_void_p]
+    L.oracle_quantize_rows(_ptr(x), C.c_int(_dtype_code(x)), C.c_int64(rows), _ptr(q), _ptr(sc))
+    return q, sc
+
+
+def round_weights(w):
+    """FP16 (RNE) bits of float32 or bfloat16-bit values."""
+    w = np.ascontiguousarray(w)
+    out = np.zeros(w.shape, np.uint16)
+    L = lib()
+    L.oracle_round_weights.restype = None
+    L.oracle_round_weights.argtypes = [C.c_void_p, C.c_int, C.c_int64, C.c_void_p]
+    L.oracle_round_weights(_ptr(w), C.c_int(_dtype_code(w)), C.c_int64(w.size), _ptr(out))
+    return out
+
+
+def write_k(x, slot, kpages, spages):
+    """Quantize K rows x [M, 128] and scatter them into copies of the compact
+    pool (kpages [P, R, 128] int8, spages [P, R] fp16 bits) at flat slots
+    page * R + row (negative or out of range: skipped).  Returns the copies."""
+    x = np.ascontiguousarray(x)
+    slot = np.ascontiguousarray(slot, dtype=np.int64)
+    kp = np.array(kpages, dtype=np.int8, copy=True, order="C")
+    sp = np.array(spages, dtype=np.uint16, copy=True, order="C")
+    P, R = sp.shape
+    L = lib()
+    L.oracle_write_k.restype = None
+    L.oracle_write_k.argtypes = [C.c_void_p, C.c_int, C.c_void_p, C.c_int64, C.c_int, C.c_int64,
+                                 C.c_void_p, C.c_void_p]
+    L.oracle_write_k(_ptr(x), C.c_int(_dtype_code(x)), _ptr(slot), C.c_int64(slot.size),
+                     C.c_int(R), C.c_int64(P), _ptr(kp), _ptr(sp))
+    return kp, sp
