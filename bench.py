@@ -14,7 +14,9 @@ kernel against its roofline (algorithmic bytes per launch over its average
 duration, measured with HIP events on the launch stream), and the oracle
 timed on the host cores on a bounded sample.  Secondary workloads (the
 8192-token prefill chunk against the INT8 MFMA peak, the 1M-context
-consumer against HBM) are reported under "other_workloads".
+consumer against HBM) are reported under "other_workloads", and the two
+producers of the indexer's inputs (query quantization, index-K cache
+write) at decode and prefill shapes under "producers".
 """
 from __future__ import annotations
 
@@ -36,13 +38,13 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def recorded_traffic(workload, kernel):
+def recorded_traffic(workload, kernel, source="qli_kernels.hip"):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (profiles/traffic.json), or None when the kernel source changed
     since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
-    src = os.path.join(ROOT, "quantized_top_indexer_amd", "csrc", "qli_kernels.hip")
+    src = os.path.join(ROOT, "quantized_top_indexer_amd", "csrc", source)
     if not os.path.exists(path):
         return None, None
     h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
@@ -204,6 +206,101 @@ def measure(pb, steps, warmup, copies=1, cand_sets=None, bound="hbm"):
             "keys_per_s": keys / (ms * 1e-3)}
 
 
+def measure_producers(steps, warmup, copies=2):
+    """Query quantization and the index-K write at the shapes of the decode
+    and prefill workloads: each launch timed with HIP events on its stream
+    (the library's timing facility), against HBM.  Algorithmic bytes: per
+    row, its 128 values in + 128 INT8 codes + one FP16 scale out; per head
+    weight, its value in + 2 bytes out; per K row also its 8-byte slot.
+    ``copies`` rotated input/output sets keep the previous launch's data out
+    of the last-level cache."""
+    import numpy as np
+    import torch
+
+    import quantized_top_indexer_amd as Q
+    import qli_workloads as W
+    Q.load_library()
+    out = {}
+
+    def timed(launch, kernel_id):
+        for i in range(warmup):
+            launch(i)
+        torch.cuda.synchronize()
+        Q.qli_timing_read(reset=True)
+        Q.qli_timing_enable(True)
+        try:
+            for i in range(steps):
+                launch(i)
+            ms, cnt = Q.qli_timing_read(reset=True)
+        finally:
+            Q.qli_timing_enable(False)
+        return ms[kernel_id] / cnt[kernel_id]
+
+    # query quantization: T tokens x N heads of bfloat16, bfloat16 weights
+    for name, T, N in (("quantize_query_prefill", 8192, 64), ("quantize_query_decode", 64, 64)):
+        rows = T * N
+        x = W.make_activations(7, 0, rows, "bf16").view(np.int16)
+        w = W.make_head_weights(7, 0, rows, "bf16").view(np.int16)
+        sets = []
+        for c in range(copies):
+            xt = torch.from_numpy(x).cuda().view(torch.bfloat16).view(T, N, 128)
+            wt = torch.from_numpy(w).cuda().view(torch.bfloat16).view(T, N)
+            sets.append((xt, wt, torch.empty((T, N, 128), dtype=torch.int8, device="cuda"),
+                         torch.empty((T, N), dtype=torch.float16, device="cuda"),
+                         torch.empty((T, N), dtype=torch.float16, device="cuda")))
+
+        def launch(i, sets=sets):
+            xt, wt, q, qs, wo = sets[i % len(sets)]
+            Q.quantize_query(xt, wt, q=q, q_scale=qs, w_out=wo)
+        kms = timed(launch, Q.QLI_KERNEL_QUANTIZE)
+        nbytes = rows * (256 + 128 + 2) + rows * (2 + 2)
+        out[name] = _producer_line(name, "quantize_kernel", kms, nbytes, rows,
+                                   {"tokens": T, "heads": N, "x": "bf16", "weights": "bf16"})
+        del sets
+        torch.cuda.empty_cache()
+
+    # index-K write: the compressed K rows of one prefill chunk (8192 raw
+    # tokens at ratio 2 -> 4096 rows, 64-row pages at 131072 B) and of one
+    # decode step (64 requests x 1 row, 128-row pages at 147712 B)
+    for name, ratio, rows, pages in (("write_k_prefill", 2, 4096, 157 * 4),
+                                     ("write_k_decode", 1, 64, 16384)):
+        R, stride, koff, soff = W.page_layout(ratio)
+        pool = torch.empty((pages, stride), dtype=torch.uint8, device="cuda")
+        kv = pool[:, koff:koff + R * 128].view(torch.int8).view(pages, R, 128)
+        sv = pool[:, soff:soff + R * 2].view(torch.int16)
+        rng = np.random.default_rng(9)
+        if rows == 64:   # one new row per request, each in its own page
+            slot = rng.permutation(pages)[:rows].astype(np.int64) * R + rng.integers(0, R, rows)
+        else:            # consecutive positions of one request over shuffled pages
+            pg = rng.permutation(pages)[:rows // R].astype(np.int64)
+            slot = (pg[:, None] * R + np.arange(R)[None, :]).reshape(-1)
+        x = W.make_activations(8, ratio, rows, "bf16", which="k").view(np.int16)
+        sets = [(torch.from_numpy(x).cuda().view(torch.bfloat16),
+                 torch.from_numpy(slot).cuda()) for _ in range(copies)]
+
+        def launch(i, sets=sets, kv=kv, sv=sv):
+            xt, st = sets[i % len(sets)]
+            Q.write_index_k(xt, st, kv, sv)
+        kms = timed(launch, Q.QLI_KERNEL_WRITE_K)
+        nbytes = rows * (256 + 8 + 128 + 2)
+        out[name] = _producer_line(name, "write_k_kernel", kms, nbytes, rows,
+                                   {"rows": rows, "ratio": ratio, "page_rows": R,
+                                    "page_stride_bytes": stride, "x": "bf16"})
+        del sets, pool, kv, sv
+        torch.cuda.empty_cache()
+    return out
+
+
+def _producer_line(name, kernel, kms, nbytes, rows, config):
+    achieved = nbytes / (kms * 1e-3) / 1e9
+    traffic, summary = recorded_traffic(name, kernel, source="qli_quant.hip")
+    return {"config": config, "kernel_ms": round(kms, 5), "rows_per_s": round(rows / (kms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                         "traffic_summary": summary, "alg_bytes_per_launch": nbytes}}
+
+
 def cpu_baseline(pb, budget_tokens=None):
     """The oracle as it stands, on the host cores, on a bounded sample of the
     workload's tokens."""
@@ -239,6 +336,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--others", default="prefill_chunk,decode_consumer_1m",
                     help="comma list of secondary workloads ('' for none)")
+    ap.add_argument("--no-producers", action="store_true",
+                    help="skip the query-quantization and index-K write measurements")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MIB",
                     help="only run a plain device copy kernel of this many MiB (5 launches), "
                          "to scale HBM byte counters")
@@ -295,6 +394,13 @@ def main():
                         "roofline": m["roofline"]}
         del opb
 
+    producers = {}
+    if not args.no_producers:
+        log("producers: query quantization and index-K write")
+        producers = measure_producers(args.steps, args.warmup)
+        for k, v in producers.items():
+            log(f"{k}: {v['kernel_ms']:.5f} ms {v['roofline']['achieved']} GB/s")
+
     cpu = None
     if not args.no_cpu_baseline and pb.mode != 3:
         log("cpu baseline: oracle on the host")
@@ -324,6 +430,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels_ms": main_m["kernels_ms"],
         "other_workloads": others,
+        "producers": producers,
     }
     print(json.dumps(line), flush=True)
 

@@ -181,12 +181,79 @@ int qli_score_topk(const qli_params* p, void* stream);
 /* Static, human-readable name of a status code. */
 const char* qli_status_string(int status);
 
-/* Kernels of one call, in launch order (for the timing facility below). */
+/* ---- Producers of the indexer's inputs --------------------------------
+ *
+ * Query quantization (DeepSeek V4.1 QLI developer guide, "数据流": every
+ * query head becomes INT8 with a representable FP16 scale, the head weights
+ * are FP16; "当前 A3 契约": per-head Q scale, quantization mode 2) and the
+ * index-K cache write (the same guide: paged INT8 index K with one FP16
+ * scale per compressed position, in 64-row pages at a 131072-byte stride or
+ * 128-row pages at 147712 bytes).  The guide gives no formula; this library
+ * implements, for one row x[0..127] of query head or K position:
+ *   amax = max_d |x_d|;  s = fp16(fp32(amax / 127)) saturated to 65504;
+ *   q_d  = clamp(rint(fp32(x_d / s)), -127, 127)   (q = 0 when s == 0)
+ * with IEEE round-to-nearest-even everywhere (rint: ties to even), and
+ * weights = fp16(w) (RNE, overflow to infinity).  Inputs are FP32 or
+ * bfloat16 and must be finite. */
+#define QLI_DTYPE_F32 0
+#define QLI_DTYPE_BF16 1
+
+typedef struct qli_quant_params {
+  int32_t struct_size;  /* sizeof(qli_quant_params) */
+  int32_t num_rows;     /* query heads to quantize (T * N), >= 0 */
+  int32_t head_dim;     /* must be 128 */
+  int32_t x_dtype;      /* QLI_DTYPE_* of x */
+  int32_t num_weights;  /* head weights to round (T * N), >= 0 (0: none) */
+  int32_t w_dtype;      /* QLI_DTYPE_* of w */
+  const void* x;        /* [num_rows, 128] (16-B aligned), read */
+  int8_t* q;            /* [num_rows, 128] (16-B aligned), written */
+  void* q_scale;        /* fp16 [num_rows] (2-B aligned), written */
+  const void* w;        /* [num_weights], read (may be NULL when num_weights == 0) */
+  void* w_out;          /* fp16 [num_weights], written */
+} qli_quant_params;
+
+/* Enqueue the quantization of num_rows query heads and the rounding of
+ * num_weights head weights on `stream`; no allocation, no synchronisation.
+ * Validation runs first; num_rows == num_weights == 0 is a no-op.
+ * Returns a qli_status. */
+int qli_quantize_query(const qli_quant_params* p, void* stream);
+
+typedef struct qli_kwrite_params {
+  int32_t struct_size;    /* sizeof(qli_kwrite_params) */
+  int32_t num_rows;       /* new K rows, >= 0 */
+  int32_t head_dim;       /* must be 128 */
+  int32_t x_dtype;        /* QLI_DTYPE_* of x */
+  int32_t page_rows;      /* rows per page: 128 (ratio 1) or 64 (ratio 2) */
+  int32_t reserved0;      /* must be 0 */
+  int64_t num_pages;      /* pages of the pool, >= 1 */
+  int64_t k_page_stride;  /* bytes between pages of the K view, multiple of 16, >= page_rows * 128 */
+  int64_t s_page_stride;  /* bytes between pages of the scale view, even, >= page_rows * 2 */
+  const void* x;          /* [num_rows, 128] new K rows (16-B aligned), read */
+  const int64_t* slot;    /* [num_rows] destination page * page_rows + row; < 0: no
+                             slot (row skipped); >= num_pages * page_rows: skipped
+                             and flagged */
+  int8_t* k_cache;        /* row 0 of page 0 of the index-K view (16-B aligned) */
+  void* k_scale;          /* fp16 row 0 of page 0 of the scale view (2-B aligned) */
+  uint32_t* status_out;   /* optional device word: QLI_DEV_BAD_PAGE is ORed in for a
+                             slot beyond the pool (NULL: not reported) */
+} qli_kwrite_params;
+
+/* Enqueue the quantization of num_rows K rows and their scatter into the
+ * paged index-K cache on `stream`: row i's INT8 values go to
+ * k_cache + page * k_page_stride + row * 128 and its FP16 scale to
+ * k_scale + page * s_page_stride + row * 2, with page, row = divmod(slot[i],
+ * page_rows).  Slots must be distinct (two rows writing one slot race).
+ * No allocation, no synchronisation; num_rows == 0 is a no-op.
+ * Returns a qli_status. */
+int qli_write_index_k(const qli_kwrite_params* p, void* stream);
+
+/* Kernels, in launch order within a call (for the timing facility below). */
 enum qli_kernel { QLI_KERNEL_CONSUMER_PREP = 0, QLI_KERNEL_PLAN = 1, QLI_KERNEL_SCORE = 2,
-                  QLI_KERNEL_SELECT = 3, QLI_NUM_KERNELS = 4 };
+                  QLI_KERNEL_SELECT = 3, QLI_KERNEL_QUANTIZE = 4, QLI_KERNEL_WRITE_K = 5,
+                  QLI_NUM_KERNELS = 6 };
 
 /* Optional per-kernel timing (off by default; process-wide, not thread
- * safe).  While enabled, every qli_score_topk() call records a HIP event
+ * safe).  While enabled, every call of this library records a HIP event
  * before and after each kernel it launches, on the call's stream.
  * qli_timing_read() waits for the recorded events, adds each kernel's
  * elapsed milliseconds to ms[kernel] and its launch count to count[kernel]

@@ -38,7 +38,8 @@ POISON_K = np.int8(127)
 POISON_S = np.float16(60000.0).view(np.uint16)
 
 # tensor ids for independent streams
-_TID_Q, _TID_QS, _TID_W, _TID_K, _TID_KS, _TID_BT, _TID_CAND, _TID_REQ = range(8)
+_TID_Q, _TID_QS, _TID_W, _TID_K, _TID_KS, _TID_BT, _TID_CAND, _TID_REQ, _TID_XQ, _TID_XK, \
+    _TID_WF, _TID_SLOT = range(12)
 
 
 def page_layout(ratio: int):
@@ -359,3 +360,54 @@ WORKLOADS = {
     "prefill_chunk": prefill_chunk,
     "decode_consumer_1m": decode_consumer_1m,
 }
+
+
+# ---------------------------------------------------------------------------
+# Un-quantized activations (inputs of query quantization and the K write)
+# ---------------------------------------------------------------------------
+
+def bf16_bits(x):
+    """bfloat16 bit patterns (uint16) of float32 values, rounded to nearest
+    even: the storage encoding of the activations, not indexer arithmetic."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_to_f32(b):
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def make_activations(seed: int, layer: int, rows: int, dtype: str = "bf16", which: str = "q"):
+    """Rows of 128 un-quantized values (query heads or new K positions).
+
+    Each row is N(0, 1) times a per-row magnitude log-uniform on [0.05, 20]
+    (heads and tokens differ in scale), with 1% of the values multiplied by
+    8 (outlier channels).  Returns float32 [rows, 128] or bfloat16 bits
+    (uint16) [rows, 128]."""
+    rng = _rng(seed, _TID_XQ if which == "q" else _TID_XK, layer)
+    mag = np.exp(rng.uniform(math.log(0.05), math.log(20.0), size=(rows, 1)))
+    x = rng.normal(0.0, 1.0, size=(rows, HEAD_DIM)) * mag
+    x = np.where(rng.random((rows, HEAD_DIM)) < 0.01, x * 8.0, x).astype(np.float32)
+    return bf16_bits(x) if dtype == "bf16" else x
+
+
+def make_head_weights(seed: int, layer: int, n: int, dtype: str = "bf16"):
+    """Un-rounded head weights, N(0, 0.1): float32 [n] or bfloat16 bits."""
+    w = _rng(seed, _TID_WF, layer).normal(0.0, 0.1, size=n).astype(np.float32)
+    return bf16_bits(w) if dtype == "bf16" else w
+
+
+def request_slots(block_table, k_lens, ratio: int, positions=None):
+    """Flat cache slots (page * page_rows + row) of compressed positions.
+
+    ``positions``: per request, an array of positions (default: all
+    [0, k_lens[b])).  Input construction for the K write: where each new
+    row of a request lands in the paged pool."""
+    R = page_layout(ratio)[0]
+    out = []
+    for b, L in enumerate(np.asarray(k_lens)):
+        j = np.arange(int(L), dtype=np.int64) if positions is None else \
+            np.asarray(positions[b], dtype=np.int64)
+        out.append(block_table[b, j // R].astype(np.int64) * R + j % R)
+    return np.concatenate(out) if out else np.zeros(0, np.int64)

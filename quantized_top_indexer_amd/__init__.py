@@ -7,9 +7,11 @@ library is not built, importing the entry points raises.
 
 Entry points (same names as the C ABI): ``qli_score_topk``,
 ``qli_workspace_bytes``, ``qli_validate``, ``qli_status_string``,
-``qli_abi_version``; plus ``score_topk``, a convenience wrapper that
-allocates the outputs and the workspace with torch and runs one call on the
-current stream, and ``output_shapes`` (shapes of a call's outputs).
+``qli_abi_version``, ``qli_quantize_query``, ``qli_write_index_k``; plus
+``score_topk``, ``quantize_query`` and ``write_index_k``, convenience
+wrappers that allocate the outputs (and the workspace) with torch and run
+one call on the current stream, and ``output_shapes`` (shapes of a call's
+outputs).
 """
 from __future__ import annotations
 
@@ -46,11 +48,37 @@ class qli_params(C.Structure):
     ]
 
 
+QLI_DTYPE_F32, QLI_DTYPE_BF16 = 0, 1
+
+
+class qli_quant_params(C.Structure):
+    """Mirror of ``struct qli_quant_params`` in include/qli.h."""
+    _fields_ = [
+        ("struct_size", C.c_int32), ("num_rows", C.c_int32), ("head_dim", C.c_int32),
+        ("x_dtype", C.c_int32), ("num_weights", C.c_int32), ("w_dtype", C.c_int32),
+        ("x", C.c_void_p), ("q", C.c_void_p), ("q_scale", C.c_void_p),
+        ("w", C.c_void_p), ("w_out", C.c_void_p),
+    ]
+
+
+class qli_kwrite_params(C.Structure):
+    """Mirror of ``struct qli_kwrite_params`` in include/qli.h."""
+    _fields_ = [
+        ("struct_size", C.c_int32), ("num_rows", C.c_int32), ("head_dim", C.c_int32),
+        ("x_dtype", C.c_int32), ("page_rows", C.c_int32), ("reserved0", C.c_int32),
+        ("num_pages", C.c_int64), ("k_page_stride", C.c_int64), ("s_page_stride", C.c_int64),
+        ("x", C.c_void_p), ("slot", C.c_void_p), ("k_cache", C.c_void_p),
+        ("k_scale", C.c_void_p), ("status_out", C.c_void_p),
+    ]
+
+
 EXPORTS = ("qli_abi_version", "qli_validate", "qli_workspace_bytes", "qli_score_topk",
-           "qli_status_string", "qli_timing_enable", "qli_timing_read")
+           "qli_status_string", "qli_timing_enable", "qli_timing_read", "qli_quantize_query",
+           "qli_write_index_k")
 QLI_KERNEL_CONSUMER_PREP, QLI_KERNEL_PLAN, QLI_KERNEL_SCORE, QLI_KERNEL_SELECT, \
-    QLI_NUM_KERNELS = 0, 1, 2, 3, 4
-KERNEL_NAMES = ("consumer_prep_kernel", "plan_kernel", "score_kernel", "select_kernel")
+    QLI_KERNEL_QUANTIZE, QLI_KERNEL_WRITE_K, QLI_NUM_KERNELS = range(7)
+KERNEL_NAMES = ("consumer_prep_kernel", "plan_kernel", "score_kernel", "select_kernel",
+                "quantize_kernel", "write_k_kernel")
 
 _lib = None
 
@@ -82,6 +110,10 @@ def load_library(path: str = LIB_PATH):
     L.qli_timing_enable.argtypes = [C.c_int]
     L.qli_timing_read.restype = C.c_int
     L.qli_timing_read.argtypes = [C.c_void_p, C.c_void_p, C.c_int]
+    L.qli_quantize_query.restype = C.c_int
+    L.qli_quantize_query.argtypes = [C.POINTER(qli_quant_params), C.c_void_p]
+    L.qli_write_index_k.restype = C.c_int
+    L.qli_write_index_k.argtypes = [C.POINTER(qli_kwrite_params), C.c_void_p]
     if path == LIB_PATH:
         _lib = L
     return L
@@ -106,6 +138,90 @@ def qli_score_topk(p: qli_params, stream=None) -> int:
         import torch
         stream = torch.cuda.current_stream().cuda_stream
     return load_library().qli_score_topk(C.byref(p), C.c_void_p(stream))
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    return C.c_void_p(stream)
+
+
+def qli_quantize_query(p: qli_quant_params, stream=None) -> int:
+    """Enqueue query quantization + weight rounding on ``stream``."""
+    return load_library().qli_quantize_query(C.byref(p), _stream(stream))
+
+
+def qli_write_index_k(p: qli_kwrite_params, stream=None) -> int:
+    """Enqueue the quantization and paged scatter of new index-K rows."""
+    return load_library().qli_write_index_k(C.byref(p), _stream(stream))
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return QLI_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return QLI_DTYPE_BF16
+    raise ValueError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def quantize_query(x, weights=None, *, q=None, q_scale=None, w_out=None, stream=None):
+    """Quantize query heads x [..., 128] (float32 or bfloat16, contiguous) to
+    INT8 with one FP16 scale per head, and round ``weights`` to FP16.
+
+    Returns ``(q int8 [..., 128], q_scale fp16 [...], weights fp16 or None)``;
+    outputs are allocated with torch unless given.
+    """
+    import torch
+    if x.shape[-1] != 128 or not x.is_contiguous():
+        raise ValueError("x must be contiguous with a last dimension of 128")
+    lead = x.shape[:-1]
+    rows = x.numel() // 128
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    if q_scale is None:
+        q_scale = torch.empty(lead, dtype=torch.float16, device=x.device)
+    p = qli_quant_params()
+    p.struct_size = C.sizeof(qli_quant_params)
+    p.num_rows, p.head_dim, p.x_dtype = rows, 128, _dtype_code(x)
+    p.x, p.q, p.q_scale = x.data_ptr(), q.data_ptr(), q_scale.data_ptr()
+    p.w_dtype = QLI_DTYPE_F32
+    if weights is not None:
+        if not weights.is_contiguous():
+            raise ValueError("weights must be contiguous")
+        if w_out is None:
+            w_out = torch.empty(weights.shape, dtype=torch.float16, device=weights.device)
+        p.num_weights, p.w_dtype = weights.numel(), _dtype_code(weights)
+        p.w, p.w_out = weights.data_ptr(), w_out.data_ptr()
+    rc = qli_quantize_query(p, stream)
+    if rc != QLI_OK:
+        raise RuntimeError(qli_status_string(rc))
+    return q, q_scale, w_out
+
+
+def write_index_k(x, slot, k_cache, k_scale, *, status_out=None, stream=None):
+    """Quantize new index-K rows x [rows, 128] (float32 or bfloat16) and
+    scatter them into the paged cache: k_cache is an int8 view
+    [num_pages, page_rows, 128] (rows of 128 contiguous bytes, any page
+    stride), k_scale an fp16 view [num_pages, page_rows] (any page stride);
+    slot int64 [rows] holds page * page_rows + row, negative to skip."""
+    if x.shape[-1] != 128 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [rows, 128] tensor")
+    if k_cache.stride(1) != 128 or k_cache.stride(2) != 1 or k_scale.stride(1) != 1:
+        raise ValueError("k_cache rows must be 128 contiguous bytes, k_scale rows 2 bytes")
+    p = qli_kwrite_params()
+    p.struct_size = C.sizeof(qli_kwrite_params)
+    p.num_rows, p.head_dim, p.x_dtype = x.shape[0], 128, _dtype_code(x)
+    p.page_rows, p.num_pages = k_cache.shape[1], k_cache.shape[0]
+    p.k_page_stride = k_cache.stride(0) * k_cache.element_size()
+    p.s_page_stride = k_scale.stride(0) * k_scale.element_size()
+    p.x, p.slot = x.data_ptr(), slot.data_ptr()
+    p.k_cache, p.k_scale = k_cache.data_ptr(), k_scale.data_ptr()
+    p.status_out = _ptr(status_out)
+    rc = qli_write_index_k(p, stream)
+    if rc != QLI_OK:
+        raise RuntimeError(qli_status_string(rc))
 
 
 def qli_status_string(code: int) -> str:

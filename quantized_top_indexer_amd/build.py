@@ -10,7 +10,8 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libqli.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = [os.path.join(CSRC, "qli_api.cpp"), os.path.join(CSRC, "qli_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "qli_api.cpp"), os.path.join(CSRC, "qli_kernels.hip"),
+           os.path.join(CSRC, "qli_quant.hip")]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -44,9 +44,62 @@ int check_scalars(const qli_params* p) {
   return QLI_OK;
 }
 
+bool dtype_ok(int32_t d) { return d == QLI_DTYPE_F32 || d == QLI_DTYPE_BF16; }
+
+int check_quant(const qli_quant_params* p) {
+  if (!p || p->struct_size != sizeof(qli_quant_params)) return QLI_ERR_INVALID_ARG;
+  if (p->head_dim != 128) return QLI_ERR_UNSUPPORTED;
+  if (!dtype_ok(p->x_dtype) || !dtype_ok(p->w_dtype)) return QLI_ERR_UNSUPPORTED;
+  if (p->num_rows < 0 || p->num_weights < 0) return QLI_ERR_INVALID_ARG;
+  if (p->num_rows > 0) {
+    if (!p->x || !p->q || !p->q_scale) return QLI_ERR_INVALID_ARG;
+    if (!aligned(p->x, 16) || !aligned(p->q, 16) || !aligned(p->q_scale, 2)) return QLI_ERR_INVALID_ARG;
+  }
+  if (p->num_weights > 0) {
+    if (!p->w || !p->w_out) return QLI_ERR_INVALID_ARG;
+    if (!aligned(p->w, p->w_dtype == QLI_DTYPE_F32 ? 4 : 2) || !aligned(p->w_out, 2))
+      return QLI_ERR_INVALID_ARG;
+  }
+  return QLI_OK;
+}
+
+int check_kwrite(const qli_kwrite_params* p) {
+  if (!p || p->struct_size != sizeof(qli_kwrite_params)) return QLI_ERR_INVALID_ARG;
+  if (p->head_dim != 128) return QLI_ERR_UNSUPPORTED;
+  if (!dtype_ok(p->x_dtype)) return QLI_ERR_UNSUPPORTED;
+  if (p->num_rows < 0 || p->reserved0 != 0) return QLI_ERR_INVALID_ARG;
+  if (p->page_rows != 64 && p->page_rows != 128) return QLI_ERR_INVALID_ARG;
+  // pool rows (num_pages * page_rows) must not overflow a 64-bit slot
+  if (p->num_pages < 1 || p->num_pages > (int64_t(1) << 40)) return QLI_ERR_INVALID_ARG;
+  if (p->k_page_stride < static_cast<int64_t>(p->page_rows) * 128 || p->k_page_stride % 16)
+    return QLI_ERR_INVALID_ARG;
+  if (p->s_page_stride < static_cast<int64_t>(p->page_rows) * 2 || p->s_page_stride % 2)
+    return QLI_ERR_INVALID_ARG;
+  if (p->num_rows == 0) return QLI_OK;
+  if (!p->x || !p->slot || !p->k_cache || !p->k_scale) return QLI_ERR_INVALID_ARG;
+  if (!aligned(p->x, 16) || !aligned(p->slot, 8) || !aligned(p->k_cache, 16) ||
+      !aligned(p->k_scale, 2) || !aligned(p->status_out, 4))
+    return QLI_ERR_INVALID_ARG;
+  return QLI_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int qli_quantize_query(const qli_quant_params* p, void* stream) {
+  const int rc = check_quant(p);
+  if (rc != QLI_OK) return rc;
+  if (p->num_rows == 0 && p->num_weights == 0) return QLI_OK;
+  return qli::launch_quantize(p, stream);
+}
+
+int qli_write_index_k(const qli_kwrite_params* p, void* stream) {
+  const int rc = check_kwrite(p);
+  if (rc != QLI_OK) return rc;
+  if (p->num_rows == 0) return QLI_OK;
+  return qli::launch_write_k(p, stream);
+}
 
 int qli_abi_version(void) { return QLI_ABI_VERSION; }
 

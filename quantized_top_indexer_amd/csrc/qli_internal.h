@@ -87,4 +87,27 @@ int launch(const qli_params* p, const WsLayout& w, void* stream);
 int timing_enable(int on);
 int timing_read(double* ms, int64_t* count, int reset);
 
+// While timing is enabled, records a HIP event on `stream` at construction
+// and another at destruction, queued for timing_read() under `kernel`.
+class Stamp {
+ public:
+  Stamp(int kernel, void* stream);
+  ~Stamp();
+  Stamp(const Stamp&) = delete;
+  Stamp& operator=(const Stamp&) = delete;
+
+ private:
+  int kernel_;
+  void* st_;
+  void* start_ = nullptr;
+  void* stop_ = nullptr;
+};
+
+// Compute units of the current device (cached per device).
+int cu_count();
+
+// Enqueue the quantization / K-write kernels (arguments already validated).
+int launch_quantize(const qli_quant_params* p, void* stream);
+int launch_write_k(const qli_kwrite_params* p, void* stream);
+
 }  // namespace qli

@@ -1619,24 +1619,29 @@ std::vector<Timed> g_pending;
 double g_ms[QLI_NUM_KERNELS];
 int64_t g_count[QLI_NUM_KERNELS];
 
-struct Stamp {
-  int kernel;
-  hipStream_t st;
-  hipEvent_t start = nullptr, stop = nullptr;
-  Stamp(int k, hipStream_t s) : kernel(k), st(s) {
-    if (!g_timing_on) return;
-    if (hipEventCreate(&start) != hipSuccess || hipEventCreate(&stop) != hipSuccess) return;
-    (void)hipEventRecord(start, st);
-  }
-  ~Stamp() {
-    if (!start || !stop) return;
-    (void)hipEventRecord(stop, st);
-    std::lock_guard<std::mutex> g(g_timing_mu);
-    g_pending.push_back({kernel, start, stop});
-  }
-};
-
 int g_cu_count[64];
+}  // namespace
+
+Stamp::Stamp(int k, void* s) : kernel_(k), st_(s) {
+  if (!g_timing_on) return;
+  hipEvent_t a = nullptr, b = nullptr;
+  if (hipEventCreate(&a) != hipSuccess) return;
+  if (hipEventCreate(&b) != hipSuccess) {
+    (void)hipEventDestroy(a);
+    return;
+  }
+  start_ = a;
+  stop_ = b;
+  (void)hipEventRecord(a, static_cast<hipStream_t>(st_));
+}
+
+Stamp::~Stamp() {
+  if (!start_ || !stop_) return;
+  (void)hipEventRecord(static_cast<hipEvent_t>(stop_), static_cast<hipStream_t>(st_));
+  std::lock_guard<std::mutex> g(g_timing_mu);
+  g_pending.push_back({kernel_, static_cast<hipEvent_t>(start_), static_cast<hipEvent_t>(stop_)});
+}
+
 int cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -1648,7 +1653,6 @@ int cu_count() {
   }
   return g_cu_count[dev];
 }
-}  // namespace
 
 int timing_enable(int on) {
   std::lock_guard<std::mutex> g(g_timing_mu);

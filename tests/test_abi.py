@@ -44,12 +44,14 @@ def test_abi_version(lib):
     assert Q.qli_abi_version() == 1
 
 
-def test_struct_layout_matches_header(tmp_path):
-    fields = [f[0] for f in Q.qli_params._fields_]
+@pytest.mark.parametrize("struct", ["qli_params", "qli_quant_params", "qli_kwrite_params"])
+def test_struct_layout_matches_header(tmp_path, struct):
+    cls = getattr(Q, struct)
+    fields = [f[0] for f in cls._fields_]
     prog = tmp_path / "layout.c"
-    body = "\n".join(f'  printf("{f} %zu\\n", offsetof(qli_params, {f}));' for f in fields)
+    body = "\n".join(f'  printf("{f} %zu\\n", offsetof({struct}, {f}));' for f in fields)
     prog.write_text(f'#include <stdio.h>\n#include <stddef.h>\n#include "qli.h"\n'
-                    f'int main(void) {{\n{body}\n  printf("sizeof %zu\\n", sizeof(qli_params));\n'
+                    f'int main(void) {{\n{body}\n  printf("sizeof %zu\\n", sizeof({struct}));\n'
                     f'  return 0;\n}}\n')
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), str(prog), "-o", str(exe)],
@@ -57,8 +59,8 @@ def test_struct_layout_matches_header(tmp_path):
     got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
                                                        check=True).stdout.splitlines())
     for f in fields:
-        assert int(got[f]) == getattr(Q.qli_params, f).offset, f
-    assert int(got["sizeof"]) == C.sizeof(Q.qli_params)
+        assert int(got[f]) == getattr(cls, f).offset, f
+    assert int(got["sizeof"]) == C.sizeof(cls)
 
 
 def base_params(mode=2, ratio=2, T=4):
@@ -189,3 +191,91 @@ def test_one_hip_runtime_per_process():
     out = subprocess.run(["python", "-c", code], capture_output=True, text=True, check=True,
                          cwd=ROOT).stdout.strip()
     assert out == "1"
+
+
+FAKE = 0x7F0000000000
+
+
+def quant_params(rows=8, nw=8):
+    p = Q.qli_quant_params()
+    p.struct_size = C.sizeof(Q.qli_quant_params)
+    p.num_rows, p.head_dim, p.x_dtype, p.num_weights, p.w_dtype = rows, 128, Q.QLI_DTYPE_BF16, nw, \
+        Q.QLI_DTYPE_F32
+    p.x, p.q, p.q_scale, p.w, p.w_out = FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288, FAKE + 16384
+    return p
+
+
+def kwrite_params(rows=8):
+    p = Q.qli_kwrite_params()
+    p.struct_size = C.sizeof(Q.qli_kwrite_params)
+    p.num_rows, p.head_dim, p.x_dtype, p.page_rows = rows, 128, Q.QLI_DTYPE_F32, 64
+    p.num_pages, p.k_page_stride, p.s_page_stride = 16, 131072, 131072
+    p.x, p.slot, p.k_cache, p.k_scale = FAKE, FAKE + 4096, FAKE + 8192, FAKE + 8192 + 73728
+    return p
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("struct_size", 4, Q.QLI_ERR_INVALID_ARG),
+    ("head_dim", 64, Q.QLI_ERR_UNSUPPORTED),
+    ("x_dtype", 2, Q.QLI_ERR_UNSUPPORTED),
+    ("w_dtype", -1, Q.QLI_ERR_UNSUPPORTED),
+    ("num_rows", -1, Q.QLI_ERR_INVALID_ARG),
+    ("num_weights", -3, Q.QLI_ERR_INVALID_ARG),
+    ("x", None, Q.QLI_ERR_INVALID_ARG),
+    ("q", None, Q.QLI_ERR_INVALID_ARG),
+    ("q_scale", None, Q.QLI_ERR_INVALID_ARG),
+    ("w", None, Q.QLI_ERR_INVALID_ARG),
+    ("w_out", None, Q.QLI_ERR_INVALID_ARG),
+    ("x", FAKE + 8, Q.QLI_ERR_INVALID_ARG),
+    ("q", FAKE + 4096 + 4, Q.QLI_ERR_INVALID_ARG),
+    ("q_scale", FAKE + 8192 + 1, Q.QLI_ERR_INVALID_ARG),
+    ("w", FAKE + 12288 + 2, Q.QLI_ERR_INVALID_ARG),  # f32 weights need 4-byte alignment
+])
+def test_quantize_rejections(lib, field, value, code):
+    p = quant_params()
+    setattr(p, field, value)
+    assert Q.qli_quantize_query(p, 0) == code
+
+
+def test_quantize_noop_and_optional_weights(lib):
+    p = quant_params(rows=0, nw=0)
+    p.x = p.q = p.q_scale = p.w = p.w_out = None
+    assert Q.qli_quantize_query(p, 0) == Q.QLI_OK  # nothing to do: no launch
+    p = quant_params(rows=0, nw=5)
+    p.w = None
+    assert Q.qli_quantize_query(p, 0) == Q.QLI_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("struct_size", 8, Q.QLI_ERR_INVALID_ARG),
+    ("head_dim", 256, Q.QLI_ERR_UNSUPPORTED),
+    ("x_dtype", 5, Q.QLI_ERR_UNSUPPORTED),
+    ("num_rows", -2, Q.QLI_ERR_INVALID_ARG),
+    ("reserved0", 1, Q.QLI_ERR_INVALID_ARG),
+    ("page_rows", 32, Q.QLI_ERR_INVALID_ARG),
+    ("num_pages", 0, Q.QLI_ERR_INVALID_ARG),
+    ("k_page_stride", 64 * 128 - 16, Q.QLI_ERR_INVALID_ARG),
+    ("k_page_stride", 131072 + 8, Q.QLI_ERR_INVALID_ARG),
+    ("s_page_stride", 127, Q.QLI_ERR_INVALID_ARG),
+    ("s_page_stride", 131073, Q.QLI_ERR_INVALID_ARG),
+    ("x", None, Q.QLI_ERR_INVALID_ARG),
+    ("slot", None, Q.QLI_ERR_INVALID_ARG),
+    ("k_cache", None, Q.QLI_ERR_INVALID_ARG),
+    ("k_scale", None, Q.QLI_ERR_INVALID_ARG),
+    ("slot", FAKE + 4096 + 4, Q.QLI_ERR_INVALID_ARG),
+    ("k_cache", FAKE + 8192 + 8, Q.QLI_ERR_INVALID_ARG),
+    ("k_scale", FAKE + 8192 + 73728 + 1, Q.QLI_ERR_INVALID_ARG),
+    ("status_out", FAKE + 2, Q.QLI_ERR_INVALID_ARG),
+])
+def test_write_k_rejections(lib, field, value, code):
+    p = kwrite_params()
+    setattr(p, field, value)
+    assert Q.qli_write_index_k(p, 0) == code
+
+
+def test_write_k_noop(lib):
+    p = kwrite_params(rows=0)
+    p.x = p.slot = p.k_cache = p.k_scale = None
+    assert Q.qli_write_index_k(p, 0) == Q.QLI_OK
+    p.page_rows = 100  # scalars are still checked with no rows
+    assert Q.qli_write_index_k(p, 0) == Q.QLI_ERR_INVALID_ARG
