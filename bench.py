@@ -338,6 +338,8 @@ def main():
                     help="comma list of secondary workloads ('' for none)")
     ap.add_argument("--no-producers", action="store_true",
                     help="skip the query-quantization and index-K write measurements")
+    ap.add_argument("--producers-only", action="store_true",
+                    help="only measure the producers (one JSON object, for profiling runs)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MIB",
                     help="only run a plain device copy kernel of this many MiB (5 launches), "
                          "to scale HBM byte counters")
@@ -364,6 +366,9 @@ def main():
         return
     import quantized_top_indexer_amd as Q
     Q.load_library()
+    if args.producers_only:
+        print(json.dumps({"producers": measure_producers(args.steps, args.warmup)}), flush=True)
+        return
 
     def run_workload(name, steps, copies):
         log(f"{name}: generating")

@@ -40,6 +40,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kQuantThreads = 256;
 constexpr int kRowLanes = 16;                          // lanes per 128-value row
 constexpr int kRowsPerWG = kQuantThreads / kRowLanes;  // 16
+constexpr int kQuantPasses = 4;  // row passes per workgroup on large inputs (1 on small ones)
 
 // Eight consecutive values of one row, as FP32 (bfloat16 widens exactly).
 template <int DT>
@@ -140,24 +141,36 @@ struct QuantArgs {
   int64_t nw;
 };
 
-// Block b quantizes rows [16b, 16b+16) and rounds weights [256b, 256b+256).
-template <int XDT, int WDT>
+// Block b quantizes rows [16*PASSES*b, 16*PASSES*(b+1)) in PASSES passes of
+// 16 consecutive rows (the loads of every pass issued before the first is
+// used) and rounds weights b*256 + tid, b*256 + tid + 256*grid, ...
+template <int XDT, int WDT, int PASSES>
 __global__ void __launch_bounds__(kQuantThreads) quantize_kernel(QuantArgs a) {
+  constexpr int kQuantRowsPerWG = kRowsPerWG * PASSES;
   const int64_t b = blockIdx.x;
   const int tid = threadIdx.x;
-  const int64_t wi = b * kQuantThreads + tid;
-  if (wi < a.nw)
+  for (int64_t wi = b * kQuantThreads + tid; wi < a.nw; wi += static_cast<int64_t>(gridDim.x) * kQuantThreads)
     a.wo[wi] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(load_weight<WDT>(a.w, wi)));
-  const int64_t row = b * kRowsPerWG + tid / kRowLanes;
-  if (b * kRowsPerWG >= a.rows) return;  // whole block past the rows (uniform)
+  const int64_t row0 = b * kQuantRowsPerWG + tid / kRowLanes;
+  if (b * kQuantRowsPerWG >= a.rows) return;  // whole block past the rows (uniform)
   const int part = tid % kRowLanes;
-  // rows of a partial last block: a 16-lane group either has its row or not
-  if (row >= a.rows) return;
-  float v[8];
-  load8<XDT>(a.x, row, part, v);
-  const RowCodes c = quantize8(v);
-  __builtin_nontemporal_store(c.q, reinterpret_cast<u32x2*>(a.q + row * 128 + part * 8));
-  if (part == 0) a.qs[row] = c.scale;
+  // a 16-lane group either has its row or not: the DPP row maximum needs
+  // all 16 lanes of the row, and never mixes rows
+  float v[PASSES][8];
+#pragma unroll
+  for (int i = 0; i < PASSES; ++i) {
+    // rows past the end load the last row (in bounds, never stored)
+    const int64_t row = row0 + i * kRowsPerWG;
+    load8<XDT>(a.x, row < a.rows ? row : a.rows - 1, part, v[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < PASSES; ++i) {
+    const int64_t row = row0 + i * kRowsPerWG;
+    if (row >= a.rows) break;
+    const RowCodes c = quantize8(v[i]);
+    __builtin_nontemporal_store(c.q, reinterpret_cast<u32x2*>(a.q + row * 128 + part * 8));
+    if (part == 0) a.qs[row] = c.scale;
+  }
 }
 
 struct KWriteArgs {
@@ -195,10 +208,25 @@ __global__ void __launch_bounds__(kQuantThreads) write_k_kernel(KWriteArgs a) {
   if (part == 0) *reinterpret_cast<uint16_t*>(a.ks + page * a.sstride + r * 2) = c.scale;
 }
 
+template <int XDT, int PASSES>
+void launch_quantize_xp(int wdt, hipStream_t st, const QuantArgs& a) {
+  const int64_t gr = (a.rows + kRowsPerWG * PASSES - 1) / (kRowsPerWG * PASSES);
+  const int64_t gw = (a.nw + kQuantThreads - 1) / kQuantThreads;
+  const unsigned grid = static_cast<unsigned>(gr > gw ? gr : gw);
+  if (wdt == QLI_DTYPE_BF16)
+    quantize_kernel<XDT, QLI_DTYPE_BF16, PASSES><<<grid, kQuantThreads, 0, st>>>(a);
+  else
+    quantize_kernel<XDT, QLI_DTYPE_F32, PASSES><<<grid, kQuantThreads, 0, st>>>(a);
+}
+
+// Four passes per workgroup once that still leaves two workgroups per CU;
+// smaller inputs spread one pass per workgroup over more CUs.
 template <int XDT>
-void launch_quantize_x(int wdt, unsigned grid, hipStream_t st, const QuantArgs& a) {
-  if (wdt == QLI_DTYPE_BF16) quantize_kernel<XDT, QLI_DTYPE_BF16><<<grid, kQuantThreads, 0, st>>>(a);
-  else quantize_kernel<XDT, QLI_DTYPE_F32><<<grid, kQuantThreads, 0, st>>>(a);
+void launch_quantize_x(int wdt, hipStream_t st, const QuantArgs& a) {
+  if (a.rows >= static_cast<int64_t>(kRowsPerWG) * kQuantPasses * 2 * cu_count())
+    launch_quantize_xp<XDT, kQuantPasses>(wdt, st, a);
+  else
+    launch_quantize_xp<XDT, 1>(wdt, st, a);
 }
 
 }  // namespace
@@ -214,13 +242,10 @@ int launch_quantize(const qli_quant_params* p, void* stream) {
   a.wo = static_cast<uint16_t*>(p->w_out);
   a.rows = p->num_rows;
   a.nw = p->num_weights;
-  const int64_t gr = (a.rows + kRowsPerWG - 1) / kRowsPerWG;
-  const int64_t gw = (a.nw + kQuantThreads - 1) / kQuantThreads;
-  const unsigned grid = static_cast<unsigned>(gr > gw ? gr : gw);
   {
     Stamp s(QLI_KERNEL_QUANTIZE, st);
-    if (p->x_dtype == QLI_DTYPE_BF16) launch_quantize_x<QLI_DTYPE_BF16>(p->w_dtype, grid, st, a);
-    else launch_quantize_x<QLI_DTYPE_F32>(p->w_dtype, grid, st, a);
+    if (p->x_dtype == QLI_DTYPE_BF16) launch_quantize_x<QLI_DTYPE_BF16>(p->w_dtype, st, a);
+    else launch_quantize_x<QLI_DTYPE_F32>(p->w_dtype, st, a);
   }
   return hipGetLastError() == hipSuccess ? QLI_OK : QLI_ERR_HIP;
 }

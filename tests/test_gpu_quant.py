@@ -72,11 +72,13 @@ def special_rows():
     return np.concatenate([x, r[None]])
 
 
-@pytest.mark.parametrize("dtype,wdtype", [("bf16", "bf16"), ("f32", "f32"), ("bf16", "f32"),
-                                          ("f32", "bf16")])
-def test_quantize_parity(dtype, wdtype):
-    rows = 3001                      # 188 workgroups of 16 rows, ragged last one
-    nw = 5000                        # more weights than rows: extra workgroups
+@pytest.mark.parametrize("dtype,wdtype,rows,nw", [
+    ("bf16", "bf16", 3001, 5000),     # one pass per workgroup, ragged; more weights than rows
+    ("f32", "f32", 3001, 5000),
+    ("bf16", "f32", 40007, 40007),    # four passes per workgroup, ragged last workgroup
+    ("f32", "bf16", 40007, 1000),     # fewer weights than rows
+])
+def test_quantize_parity(dtype, wdtype, rows, nw):
     say(f"quantize {dtype}/{wdtype} rows={rows} weights={nw}")
     x = W.make_activations(11, 0, rows, dtype)
     w = W.make_head_weights(11, 0, nw, wdtype)
