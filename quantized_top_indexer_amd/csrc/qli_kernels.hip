@@ -959,14 +959,18 @@ __device__ __forceinline__ void epi_pass(const QSrc& qs, const i32x16 (&acc)[2],
   }
 }
 
-// Score (× k_scale), key, block maximum and stores of slot s0 + lane.
-// Every store is unconditional (slots past n_i receive key 0, block maxima
-// are written by all 8 lanes of a block), so the memory operations of a
-// sub-tile are fixed.
+// Score (× k_scale), key, block maximum and stores of slot s0 + lane, whose
+// place in its 256-slot item is 64 * sub + lane: the key goes to
+// kp[64 * sub + lane] and the block maximum to bp[(64 * sub + lane) / 8]
+// (kp and bp point at the item's keys, in global memory or in an LDS
+// staging entry).  Every store is unconditional (slots past n_i receive key
+// 0, block maxima are written by all 8 lanes of a block), so the memory
+// operations of a sub-tile are fixed.
 template <int MODE, bool DBG>
 __device__ __forceinline__ void finish_subtile(const KArgs& a, const uint16_t* ksc, int sub, int t, int s0,
-                                               int n_i, int lane, float sum) {
+                                               int n_i, int lane, float sum, uint32_t* kp, uint32_t* bp) {
   const int slot = s0 + lane;
+  const int local = 64 * sub + lane;
   const uint16_t kb = ksc[64 * sub + lane];
   const bool valid = slot < n_i && kb != 0xFFFFu;
   const float score = sum * static_cast<float>(__builtin_bit_cast(_Float16, kb));
@@ -977,13 +981,13 @@ __device__ __forceinline__ void finish_subtile(const KArgs& a, const uint16_t* k
                         : slot;
     a.dbg[static_cast<int64_t>(t) * a.max_k_len + pos] = score;
   }
-  a.keys[static_cast<int64_t>(t) * a.ncap + slot] = key;
+  kp[local] = key;
   if (MODE == QLI_MODE_SOURCE) {
     uint32_t bk = key;
     bk = max(bk, static_cast<uint32_t>(__shfl_xor(static_cast<int>(bk), 1)));
     bk = max(bk, static_cast<uint32_t>(__shfl_xor(static_cast<int>(bk), 2)));
     bk = max(bk, static_cast<uint32_t>(__shfl_xor(static_cast<int>(bk), 4)));
-    a.bkeys[static_cast<int64_t>(t) * a.nbcap + (slot >> 3)] = bk;
+    bp[local >> 3] = bk;
   }
 }
 
@@ -992,7 +996,8 @@ __device__ __forceinline__ void finish_subtile(const KArgs& a, const uint16_t* k
 template <int NH, int MODE, bool DBG, class QSrc>
 __device__ __forceinline__ void score_subtile(const KArgs& a, const QSrc& qs,
                                               const int8_t* tile, const uint16_t* ksc, int sub,
-                                              int t, int s0, int n_i, int lane, const i32x16& seed) {
+                                              int t, int s0, int n_i, int lane, const i32x16& seed,
+                                              uint32_t* kp, uint32_t* bp) {
   float sum = 0.0f;
 #pragma unroll 1
   for (int ps = 0; ps < NH / 32; ++ps) {
@@ -1000,7 +1005,7 @@ __device__ __forceinline__ void score_subtile(const KArgs& a, const QSrc& qs,
     mfma_pass(qs, tile, sub, ps, lane, seed, acc);
     epi_pass<false>(qs, acc, ps, lane, a.one, sum);
   }
-  finish_subtile<MODE, DBG>(a, ksc, sub, t, s0, n_i, lane, sum);
+  finish_subtile<MODE, DBG>(a, ksc, sub, t, s0, n_i, lane, sum, kp, bp);
 }
 
 // Multi groups (prefill shapes): each item is 256 slots for 4 consecutive
@@ -1050,7 +1055,11 @@ __device__ void run_multi(const KArgs& a, const ListView& L, Cursor cur, int hi,
       }
       epi_pass<true>(q, (u & 1) ? accB : accA, u % P, lane, one, sum);
       if (u % P == P - 1) {
-        finish_subtile<MODE, DBG>(a, ksc[buf], u / P, t, cur.c * kChunk + 64 * (u / P), n_i, lane, sum);
+        finish_subtile<MODE, DBG>(a, ksc[buf], u / P, t, cur.c * kChunk + 64 * (u / P), n_i, lane, sum,
+                                  a.keys + static_cast<int64_t>(t) * a.ncap + cur.c * kChunk,
+                                  MODE == QLI_MODE_SOURCE
+                                      ? a.bkeys + static_cast<int64_t>(t) * a.nbcap + cur.c * (kChunk / 8)
+                                      : nullptr);
         sum = 0.0f;
       }
       // each step schedules one unit's MFMAs against the previous unit's
@@ -1079,20 +1088,62 @@ __device__ void run_multi(const KArgs& a, const ListView& L, Cursor cur, int hi,
 // Single-token groups (decode shapes): wave w stages and scores sub-tile w
 // of every item in its own LDS rows, so inside a token segment the waves
 // run independently (an LDS write and a later read of the same wave are
-// ordered without a barrier).  Per segment the queries are loaded once
-// (workgroup barriers); inside it the loop body has a fixed set of memory
-// operations and keeps two items of K in flight (register sets A and B
-// alternate; the body is unrolled twice).
+// ordered without a barrier, which also lets one K buffer serve every item:
+// a wave's next stores follow its previous reads).  Per segment the queries
+// are loaded once (workgroup barriers); inside it the loop body has a fixed
+// set of memory operations and keeps two items of K in flight (register
+// sets A and B alternate; the body is unrolled twice).
 // Each step resolves the block rows looked up one step earlier, issues the
 // next lookup, then the K loads: with in-order memory counters a lookup is
 // always older than the K loads that must stay in flight.
+// The keys (and block maxima) of up to kKeyStage items are staged in LDS
+// (the second K buffer, unused here) and written out together when the
+// stage is full and at the end of the range: HBM writes spread through the
+// K stream cost far more read bandwidth than the same bytes in bursts.
+constexpr int kKeyStage = 24;                  // staged items
+constexpr int kKeyEntry = kChunk + kChunk / 8;  // u32 words per staged item (keys, block maxima)
+static_assert(kKeyStage * kKeyEntry * 4 + kKeyStage * 8 <= kChunk * 128, "key stage exceeds a K buffer");
+
+template <int MODE>
+__device__ __forceinline__ void flush_keys(const KArgs& a, const uint32_t* stage, const int32_t* meta,
+                                           int n) {
+  __syncthreads();  // every wave's keys of the staged items are in LDS
+  const int tid = threadIdx.x;
+  for (int e = 0; e < n; ++e) {
+    const int t = meta[2 * e], c = meta[2 * e + 1];
+    __builtin_nontemporal_store(stage[e * kKeyEntry + tid],
+                                a.keys + static_cast<int64_t>(t) * a.ncap + c * kChunk + tid);
+    if (MODE == QLI_MODE_SOURCE && tid < kChunk / 8)
+      __builtin_nontemporal_store(stage[e * kKeyEntry + kChunk + tid],
+                                  a.bkeys + static_cast<int64_t>(t) * a.nbcap + c * (kChunk / 8) + tid);
+  }
+  __syncthreads();  // the stage is free again
+}
+
 template <int NH, int MODE, bool DBG>
 __device__ void run_single(const KArgs& a, const ListView& L, Cursor cu, int hi,
                            int8_t (*tile)[kChunk * 128], uint16_t (*ksc)[kChunk], i32x4* qfr,
                            uint32_t* qml, int wave, int lane, const i32x16& seed, bool& bad) {
+  static_assert(kScoreThreads == kChunk, "one staged key per thread and item");
   constexpr bool CONSUMER = MODE == QLI_MODE_CONSUMER;
-  int buf = 0;
-  const QLds<NH> qs{qfr, qml};
+  uint32_t* stage = reinterpret_cast<uint32_t*>(tile[1]);
+  int32_t* meta = reinterpret_cast<int32_t*>(stage + kKeyStage * kKeyEntry);
+  int ne = 0;  // staged items (the same in every wave)
+  // score item c of token t into staged entry ne, flushing a full stage
+  auto score_item = [&](int t, int c, int n) {
+    if (ne == kKeyStage) {
+      flush_keys<MODE>(a, stage, meta, ne);
+      ne = 0;
+    }
+    if (wave == 0 && lane == 0) {
+      meta[2 * ne] = t;
+      meta[2 * ne + 1] = c;
+    }
+    uint32_t* kp = stage + ne * kKeyEntry;
+    score_subtile<NH, MODE, DBG>(a, QLds<NH>{qfr, qml}, tile[0], ksc[0], wave, t, c * kChunk + 64 * wave,
+                                 n, lane, seed, kp, kp + kChunk);
+    ++ne;
+  };
   while (cu.valid) {
     const Group gr = cu.grp;
     const int c0 = cu.c;
@@ -1113,29 +1164,26 @@ __device__ void run_single(const KArgs& a, const ListView& L, Cursor cu, int hi,
     stage_load<true>(a, vB, lane, krB, scB);
     __syncthreads();  // queries in LDS
     for (int c = c0; c < c_end; c += 2) {
-      stage_store<true>(tile[buf], ksc[buf], krA, scA, vA, wave, lane);
+      stage_store<true>(tile[0], ksc[0], krA, scA, vA, wave, lane);
       vA = resolve<CONSUMER>(a, ad, bad);
       stage_addr<CONSUMER, true>(a, gr, c + 3, c + 3 < c_end, wave, lane, ad);
       stage_load<true>(a, vA, lane, krA, scA);
       __builtin_amdgcn_wave_barrier();
-      score_subtile<NH, MODE, DBG>(a, qs, tile[buf], ksc[buf], wave, t, c * kChunk + 64 * wave,
-                                         n, lane, seed);
-      buf ^= 1;
+      score_item(t, c, n);
       if (c + 1 >= c_end) break;
-      stage_store<true>(tile[buf], ksc[buf], krB, scB, vB, wave, lane);
+      stage_store<true>(tile[0], ksc[0], krB, scB, vB, wave, lane);
       vB = resolve<CONSUMER>(a, ad, bad);
       stage_addr<CONSUMER, true>(a, gr, c + 4, c + 4 < c_end, wave, lane, ad);
       stage_load<true>(a, vB, lane, krB, scB);
       __builtin_amdgcn_wave_barrier();
-      score_subtile<NH, MODE, DBG>(a, qs, tile[buf], ksc[buf], wave, t,
-                                         (c + 1) * kChunk + 64 * wave, n, lane, seed);
-      buf ^= 1;
+      score_item(t, c + 1, n);
     }
     // next token segment
     cu.c = c_end - 1;
     cu.unit += (c_end - 1 - c0);
     cu = next_item(L, cu, hi);
   }
+  if (ne > 0) flush_keys<MODE>(a, stage, meta, ne);
 }
 
 // Each workgroup takes its list, first item and unit range from the plan.
