@@ -104,7 +104,7 @@ struct KArgs {
   int32_t* slots;
   int32_t* srow;
   int32_t* ncount;
-  int32_t* tokv;    // [T] visible compressed count per token (plan)
+  int32_t* tokv;    // [T] visible compressed count per token (plan), | kTokBad (score)
 };
 
 __device__ __forceinline__ void raise_flag(const KArgs& a, uint32_t bit) {
@@ -748,13 +748,20 @@ __device__ Cursor next_item(const ListView& L, Cursor cu, int hi) {
 struct Addr {
   int raw;   // loaded block-table entry / prepared page row
   int meta;  // bit 31: block wanted; bit 30: table index in range; low bits: row in page
+  int t0, ntok;  // the tokens sharing the block (marked when its page is out of contract)
 };
+
+// Set in a token's visible count (tokv) when some block it may read had an
+// out-of-contract page: its selection then takes the general path.
+constexpr int32_t kTokBad = 1 << 30;
 
 template <bool CONSUMER, bool OWN>
 __device__ __forceinline__ void stage_addr(const KArgs& a, const Group& gr, int c, bool valid,
                                            int wave, int lane, Addr& ad) {
   const int j = lane & 7;
   const int q = OWN ? 8 * wave + j : 4 * j + wave;
+  ad.t0 = gr.t0;
+  ad.ntok = gr.ntok;
   if (CONSUMER) {
     const int s = c * 32 + q;
     ad.raw = a.srow[static_cast<int64_t>(gr.t0) * a.cb_in + min(s, a.cb_in - 1)];
@@ -774,7 +781,10 @@ __device__ __forceinline__ int resolve(const KArgs& a, const Addr& ad, bool& bad
   const bool want = ad.meta < 0;  // bit 31
   if (CONSUMER) return want && ad.raw >= 0 ? ad.raw : -1;
   const bool ok = want && (ad.meta & (1 << 30)) && ad.raw >= 0 && ad.raw < a.num_pages;
-  bad |= want && !ok;
+  if (want && !ok) {  // rare: mark every token of the group
+    bad = true;
+    for (int i = 0; i < ad.ntok; ++i) atomicOr(&a.tokv[ad.t0 + i], kTokBad);
+  }
   return ok ? ad.raw * a.R + (ad.meta & (a.R - 1)) : -1;
 }
 
@@ -1634,6 +1644,12 @@ template <int BS, bool MULTI>
 __global__ __launch_bounds__(BS) void select_kernel(KArgs a) {
   __shared__ uint32_t sel_lds[sel_lds_words(BS)];
   const int t = blockIdx.x;
+  // plain/source: every position below V and every block below ceil(V/8) is
+  // eligible unless a page was out of contract, so when they all fit the
+  // selection is all of them, in order (no keys needed)
+  auto all_of = [](int32_t* out, int n, int k) {
+    for (int i = threadIdx.x; i < k; i += BS) out[i] = i < n ? i : -1;
+  };
   if (blockIdx.y == 0) {
     int32_t* out = a.topk_out + static_cast<int64_t>(t) * a.topk;
     const uint32_t* keys = a.keys + static_cast<int64_t>(t) * a.ncap;
@@ -1642,12 +1658,18 @@ __global__ __launch_bounds__(BS) void select_kernel(KArgs a) {
       select_topk<BS, MULTI>(keys, a.ncount[t], cap, a.topk, -1, out,
                       MapSlots{a.slots + static_cast<int64_t>(t) * a.cb_in}, sel_lds);
     } else {
-      select_topk<BS, MULTI>(keys, a.tokv[t], cap, a.topk, -1, out, MapIdentity{}, sel_lds);
+      const int32_t tv = a.tokv[t];
+      const int V = tv & ~kTokBad;
+      if (!(tv & kTokBad) && V <= a.topk) all_of(out, V, a.topk);
+      else select_topk<BS, MULTI>(keys, V, cap, a.topk, -1, out, MapIdentity{}, sel_lds);
     }
   } else {
-    const int nb = (a.tokv[t] + 7) / 8;
-    select_topk<BS, MULTI>(a.bkeys + static_cast<int64_t>(t) * a.nbcap, nb, static_cast<int>(a.nbcap), a.cb,
-                    nb - 1, a.cand_out + static_cast<int64_t>(t) * a.cb, MapIdentity{}, sel_lds);
+    const int32_t tv = a.tokv[t];
+    const int nb = ((tv & ~kTokBad) + 7) / 8;
+    int32_t* out = a.cand_out + static_cast<int64_t>(t) * a.cb;
+    if (!(tv & kTokBad) && nb <= a.cb) all_of(out, nb, a.cb);
+    else select_topk<BS, MULTI>(a.bkeys + static_cast<int64_t>(t) * a.nbcap, nb, static_cast<int>(a.nbcap), a.cb,
+                           nb - 1, out, MapIdentity{}, sel_lds);
   }
 }
 

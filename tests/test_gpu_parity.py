@@ -5,7 +5,8 @@ ragged tails, plus the edge cases of the method."""
 import numpy as np
 import pytest
 
-from gpu_check import (check_invariants, compare, oracle_rows, run_gpu, say, small_problem)
+from gpu_check import (check_invariants, compare, oracle_rows, run_gpu, say, small_problem,
+                       visible)
 
 pytestmark = pytest.mark.gpu
 
@@ -180,6 +181,39 @@ def test_device_status_flags():
     torch.cuda.synchronize()
     assert int(status.item()) & Q.QLI_DEV_BAD_LENGTH
     assert torch.all(idx == -1)
+
+
+def test_bad_page_when_everything_fits():
+    """When top-k and the candidate width cover every visible position and
+    block, the selection is everything visible; a block-table entry past the
+    pool must still take its positions and blocks out (the general path)."""
+    import torch
+
+    import quantized_top_indexer_amd as Q
+    pb = small_problem(306, ratio=2, N=32, mode=2, topk=2048, cb=512, requests=((3, 1200), (2, 700)))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    clean = run_gpu(pb)
+    vis = visible(pb)
+    for t, V in enumerate(vis):   # everything fits: all positions / blocks in order
+        assert np.array_equal(clean["topk"][t, :V], np.arange(V))
+        assert np.all(clean["topk"][t, V:] == -1)
+        nb = -(-int(V) // 8)
+        assert np.array_equal(clean["cand"][t, :nb], np.arange(nb))
+    pb.block_table = pb.block_table.copy()
+    pb.block_table[0, 1] = pb.num_pages + 7          # positions 64..127 of request 0
+    res = run_gpu(pb, status=status)
+    assert int(status.item()) & Q.QLI_DEV_BAD_PAGE
+    for t in range(3):                                # request 0's tokens
+        V = int(vis[t])
+        want = np.array([j for j in range(V) if not 64 <= j < 128])
+        assert np.array_equal(res["topk"][t, :len(want)], want)
+        assert np.all(res["topk"][t, len(want):] == -1)
+        nb = -(-V // 8)
+        wb = np.array([c for c in range(nb) if not 8 <= c < 16])
+        assert np.array_equal(res["cand"][t, :len(wb)], wb)
+    for t in range(3, 5):                             # request 1 is untouched
+        assert np.array_equal(res["topk"][t], clean["topk"][t])
+        assert np.array_equal(res["cand"][t], clean["cand"][t])
 
 
 def test_zero_tokens():
