@@ -68,6 +68,9 @@ EDGES = {
                            cand_policy="messy"),
     "consumer_ratio1_full": dict(ratio=1, N=64, mode=3, topk=2048, cb_in=64,
                                  requests=((2, 600), (1, 1))),
+    # rows longer than one select chunk (32768 keys): the chunked selection
+    "long_rows_chunked": dict(ratio=1, N=32, mode=2, topk=2048, cb=1024,
+                              requests=((2, 45000), (1, 33000))),
 }
 
 
@@ -89,7 +92,7 @@ def test_heavy_ties(mode, patterns):
     histogram bins are ties; with 200 each value repeats ~15 times, so the
     boundary falls inside a small run of equal keys."""
     pb = small_problem(310 + mode, ratio=1, N=32, mode=mode, topk=300, cb=64, cb_in=128,
-                       requests=((2, 3000), (1, 1200), (1, 40)))
+                       requests=((2, 3000), (1, 1200), (1, 40), (1, 36000) if mode != 3 else (1, 60)))
     rng = np.random.default_rng(310 + mode + patterns)
     pats = rng.integers(-128, 128, size=(patterns, 128), dtype=np.int64).astype(np.int8)
     P, R, _ = pb.k_pages.shape
