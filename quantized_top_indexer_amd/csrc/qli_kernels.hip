@@ -1391,12 +1391,14 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n, int cap
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nch = MULTI ? (n + CHUNK - 1) / CHUNK : 1;
-  // vectors of this wave that hold any index below n (one chunk): the
-  // others are all zero and their work is skipped as a whole
-  const int nvec = MULTI ? VPT : min(VPT, max(0, (n - wave * KPW + 255) >> 8));
+  // one chunk: the row is spread evenly over the waves in whole vectors
+  // (kpw keys per wave), so that a short row keeps every wave busy; the
+  // vectors of a wave past its nvec are all zero and their work is skipped
+  const int kpw = MULTI ? KPW : min(KPW, ((n + NW - 1) / NW + 255) & ~255);
+  const int nvec = MULTI ? VPT : min(min(VPT, max(0, (n - wave * kpw + 255) >> 8)), kpw >> 8);
   uint32_t kr[4 * VPT];
   auto index_of = [&](int ch, int j, int e) {
-    return ch * CHUNK + wave * KPW + 256 * j + 4 * lane + e;
+    return ch * CHUNK + wave * kpw + 256 * j + 4 * lane + e;
   };
   auto load = [&](int ch) {  // every load is issued before the first use
     i32x4 x[VPT];
@@ -1407,9 +1409,11 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n, int cap
     for (int j = 0; j < VPT; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
+        // vectors past nvec may reach into the next wave's keys: zero
         const int idx = index_of(ch, j, e);
-        const uint32_t v = idx < n ? static_cast<uint32_t>(x[j][e]) : 0u;
-        kr[4 * j + e] = idx == pin ? kPinKey : v;
+        const bool own = j < nvec && idx < n;
+        const uint32_t v = own ? static_cast<uint32_t>(x[j][e]) : 0u;
+        kr[4 * j + e] = own && idx == pin ? kPinKey : v;
       }
   };
 
