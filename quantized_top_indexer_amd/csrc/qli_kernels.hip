@@ -329,17 +329,33 @@ __device__ __forceinline__ void prep_write(const KArgs& a, int t, int b, int V, 
   }
 }
 
+// In consumer mode one launch prepares the tokens and plans the score work:
+// block 0 runs the plan (it needs no prepared data: a consumer token's work
+// is bounded by min(cb_in, visible blocks) * 8 slots, and the score kernel
+// reads the exact eligible count), blocks 1..T prepare token blockIdx.x - 1.
+// Both roles carve their LDS from one buffer.
+__device__ void plan_role(const KArgs& a, uint32_t* lds);
+constexpr int kPlanLdsRequests = 4096;  // metadata of up to this many requests is staged in LDS
+constexpr int kPlanLdsWords = 3 * kPlanLdsRequests + 1 + 64;
+constexpr int kPrepLdsWords = kPrepBitmapWords + QLI_MAX_CAND_BLOCKS + 64 + 1;
+constexpr int kConsumerLdsWords = kPrepLdsWords > kPlanLdsWords ? kPrepLdsWords : kPlanLdsWords;
+
 // Sorted unique visible incoming block ids per token, through a bitmap of
 // the visible block ids: duplicates merge, and a prefix count of set bits
 // places every id (contexts of up to 2^18 blocks).
 __global__ __launch_bounds__(kPrepThreads) void consumer_prep_kernel(KArgs a) {
-  __shared__ uint32_t bm[kPrepBitmapWords];
-  __shared__ int32_t sl[QLI_MAX_CAND_BLOCKS];
-  __shared__ uint32_t sh[64];
-  __shared__ int s_req;
-  const int t = blockIdx.x;
+  __shared__ uint32_t lds[kConsumerLdsWords];
+  if (blockIdx.x == 0) {
+    plan_role(a, lds);
+    return;
+  }
+  uint32_t* bm = lds;
+  int32_t* sl = reinterpret_cast<int32_t*>(lds + kPrepBitmapWords);
+  uint32_t* sh = lds + kPrepBitmapWords + QLI_MAX_CAND_BLOCKS;
+  int* s_req = reinterpret_cast<int*>(sh + 64);
+  const int t = blockIdx.x - 1;
   const int tid = threadIdx.x;
-  const int b = prep_request(a, t, &s_req);
+  const int b = prep_request(a, t, s_req);
   const ReqView r = request_view(a, global_meta(a), b, tid == 0);
   const int V = (t >= r.q0 && t < r.q1)
                     ? visible(a, r.S - (r.q1 - r.q0) + (t - r.q0), r.L) : 0;
@@ -373,13 +389,18 @@ __global__ __launch_bounds__(kPrepThreads) void consumer_prep_kernel(KArgs a) {
 
 // The same by a bitonic sort of the incoming ids (any context length).
 __global__ __launch_bounds__(kPrepThreads) void consumer_prep_sort_kernel(KArgs a) {
-  __shared__ int32_t v[QLI_MAX_CAND_BLOCKS];
-  __shared__ int32_t sl[QLI_MAX_CAND_BLOCKS];
-  __shared__ uint32_t sh[64];
-  __shared__ int s_req;
-  const int t = blockIdx.x;
+  __shared__ uint32_t lds[kConsumerLdsWords];
+  if (blockIdx.x == 0) {
+    plan_role(a, lds);
+    return;
+  }
+  int32_t* v = reinterpret_cast<int32_t*>(lds);
+  int32_t* sl = v + QLI_MAX_CAND_BLOCKS;
+  uint32_t* sh = lds + 2 * QLI_MAX_CAND_BLOCKS;
+  int* s_req = reinterpret_cast<int*>(sh + 64);
+  const int t = blockIdx.x - 1;
   const int tid = threadIdx.x;
-  const int b = prep_request(a, t, &s_req);
+  const int b = prep_request(a, t, s_req);
   const ReqView r = request_view(a, global_meta(a), b, tid == 0);
   const int V = (t >= r.q0 && t < r.q1)
                     ? visible(a, r.S - (r.q1 - r.q0) + (t - r.q0), r.L) : 0;
@@ -452,7 +473,10 @@ __device__ __forceinline__ Group make_group(const KArgs& a, int b, const ReqView
   const int64_t p0 = r.S - (r.q1 - r.q0) + (t - r.q0);
   g.p0 = static_cast<int>(p0);
   if (a.mode == QLI_MODE_CONSUMER) {
-    g.n0 = a.ncount[t];
+    // a bound on the eligible slots (the prepared count may not exist yet):
+    // every kept block is an incoming id below ceil(V / 8)
+    const int64_t nb = (static_cast<int64_t>(visible(a, p0, r.L)) + 7) / 8;
+    g.n0 = static_cast<int>(8 * min(nb, static_cast<int64_t>(a.cb_in)));
     g.nlast = g.n0;
   } else {
     g.n0 = visible(a, p0, r.L);
@@ -557,7 +581,6 @@ __device__ void write_starts(const KArgs& a, const Split& sp, int gidx, const Gr
   }
 }
 
-constexpr int kPlanLdsRequests = 4096;  // metadata of up to this many requests is staged in LDS
 
 // The plan proper, on request metadata m (an LDS copy or global memory).
 __device__ __forceinline__ void plan_body(const KArgs& a, const Meta& m, uint32_t* sh) {
@@ -664,11 +687,13 @@ __device__ __forceinline__ void plan_body(const KArgs& a, const Meta& m, uint32_
   }
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(KArgs a) {
-  __shared__ uint32_t sh[64];
-  __shared__ int32_t s_qsl[kPlanLdsRequests + 1];
-  __shared__ int32_t s_klen[kPlanLdsRequests];
-  __shared__ int32_t s_smod[kPlanLdsRequests];
+static_assert(kPlanThreads == kPrepThreads, "the plan role runs in a consumer-prep workgroup");
+
+__device__ void plan_role(const KArgs& a, uint32_t* lds) {
+  int32_t* s_qsl = reinterpret_cast<int32_t*>(lds);
+  int32_t* s_klen = s_qsl + kPlanLdsRequests + 1;
+  int32_t* s_smod = s_klen + kPlanLdsRequests;
+  uint32_t* sh = reinterpret_cast<uint32_t*>(s_smod + kPlanLdsRequests);
   const int tid = threadIdx.x;
   // every start entry begins as "no work" (the barriers below order these
   // stores before the ones the plan writes); workgroups whose range starts
@@ -691,6 +716,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KArgs a) {
   } else {
     plan_body(a, global_meta(a), sh);
   }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(KArgs a) {
+  __shared__ uint32_t lds[kPlanLdsWords];
+  plan_role(a, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1155,10 +1185,13 @@ __device__ void run_single(const KArgs& a, const ListView& L, Cursor cu, int hi,
     ++ne;
   };
   while (cu.valid) {
-    const Group gr = cu.grp;
+    Group gr = cu.grp;
     const int c0 = cu.c;
     const int c_end = min(gr.nch, c0 + (hi - cu.unit));
     const int t = gr.t0;
+    // consumer: the plan's bound covers the work; the eligible slots are the
+    // prepared count (slots past it are not read and score as not eligible)
+    if (CONSUMER) gr.n0 = a.ncount[t];
     const int n = gr.n0;
     __syncthreads();  // the previous segment's last item is scored
     load_q_lds<NH>(a, t, qfr, qml);
@@ -1829,14 +1862,14 @@ int launch(const qli_params* p, const WsLayout& w, void* stream) {
 
   const unsigned T = static_cast<unsigned>(p->num_tokens);
   if (consumer) {
+    // block 0 plans, blocks 1..T prepare the tokens
     Stamp s(QLI_KERNEL_CONSUMER_PREP, st);
     const int64_t max_blocks = (static_cast<int64_t>(p->max_k_len) + 7) / 8;
     if (max_blocks <= 32 * static_cast<int64_t>(kPrepBitmapWords))
-      consumer_prep_kernel<<<T, kPrepThreads, 0, st>>>(a);
+      consumer_prep_kernel<<<T + 1, kPrepThreads, 0, st>>>(a);
     else
-      consumer_prep_sort_kernel<<<T, kPrepThreads, 0, st>>>(a);
-  }
-  {
+      consumer_prep_sort_kernel<<<T + 1, kPrepThreads, 0, st>>>(a);
+  } else {
     Stamp s(QLI_KERNEL_PLAN, st);
     plan_kernel<<<1, kPlanThreads, 0, st>>>(a);
   }
