@@ -334,6 +334,7 @@ __device__ __forceinline__ void prep_write(const KArgs& a, int t, int b, int V, 
 // is bounded by min(cb_in, visible blocks) * 8 slots, and the score kernel
 // reads the exact eligible count), blocks 1..T prepare token blockIdx.x - 1.
 // Both roles carve their LDS from one buffer.
+template <int PT>
 __device__ void plan_role(const KArgs& a, uint32_t* lds);
 constexpr int kPlanLdsRequests = 4096;  // metadata of up to this many requests is staged in LDS
 constexpr int kPlanLdsWords = 3 * kPlanLdsRequests + 1 + 64;
@@ -346,7 +347,7 @@ constexpr int kConsumerLdsWords = kPrepLdsWords > kPlanLdsWords ? kPrepLdsWords 
 __global__ __launch_bounds__(kPrepThreads) void consumer_prep_kernel(KArgs a) {
   __shared__ uint32_t lds[kConsumerLdsWords];
   if (blockIdx.x == 0) {
-    plan_role(a, lds);
+    plan_role<kPrepThreads>(a, lds);
     return;
   }
   uint32_t* bm = lds;
@@ -391,7 +392,7 @@ __global__ __launch_bounds__(kPrepThreads) void consumer_prep_kernel(KArgs a) {
 __global__ __launch_bounds__(kPrepThreads) void consumer_prep_sort_kernel(KArgs a) {
   __shared__ uint32_t lds[kConsumerLdsWords];
   if (blockIdx.x == 0) {
-    plan_role(a, lds);
+    plan_role<kPrepThreads>(a, lds);
     return;
   }
   int32_t* v = reinterpret_cast<int32_t*>(lds);
@@ -582,11 +583,13 @@ __device__ void write_starts(const KArgs& a, const Split& sp, int gidx, const Gr
 }
 
 
-// The plan proper, on request metadata m (an LDS copy or global memory).
+// The plan proper, on request metadata m (an LDS copy or global memory), by
+// PT threads.
+template <int PT>
 __device__ __forceinline__ void plan_body(const KArgs& a, const Meta& m, uint32_t* sh) {
   const int tid = threadIdx.x;
   const int T = a.T;
-  const int per = (T + kPlanThreads - 1) / kPlanThreads;
+  const int per = (T + PT - 1) / PT;
   const int t_lo = min(T, tid * per);
   const int t_hi = min(T, t_lo + per);
   uint32_t cnt[4] = {0, 0, 0, 0};  // groups and units of list 0, then of list 1
@@ -619,7 +622,7 @@ __device__ __forceinline__ void plan_body(const KArgs& a, const Meta& m, uint32_
     }
   }
   uint32_t tot[4];
-  block_exclusive_scan_n<kPlanThreads, 4>(cnt, tot, sh);  // also orders the clears below
+  block_exclusive_scan_n<PT, 4>(cnt, tot, sh);  // also orders the clears below
   const int W = a.score_grid;
   const int Wm = multi_workgroups(W, static_cast<int>(tot[1]), static_cast<int>(tot[3]));
   auto split = [&](int l) {
@@ -687,8 +690,9 @@ __device__ __forceinline__ void plan_body(const KArgs& a, const Meta& m, uint32_
   }
 }
 
-static_assert(kPlanThreads == kPrepThreads, "the plan role runs in a consumer-prep workgroup");
-
+// PT threads (a consumer-prep workgroup, a plan workgroup, or one wave for
+// small batches, where no cross-wave barrier is needed).
+template <int PT>
 __device__ void plan_role(const KArgs& a, uint32_t* lds) {
   int32_t* s_qsl = reinterpret_cast<int32_t*>(lds);
   int32_t* s_klen = s_qsl + kPlanLdsRequests + 1;
@@ -698,13 +702,13 @@ __device__ void plan_role(const KArgs& a, uint32_t* lds) {
   // every start entry begins as "no work" (the barriers below order these
   // stores before the ones the plan writes); workgroups whose range starts
   // past the last item of their list keep it
-  for (int w = tid; w < a.score_grid; w += kPlanThreads) {
+  for (int w = tid; w < a.score_grid; w += PT) {
     WgStart st = {};
     st.g = -1;
     a.wgs[w] = st;
   }
   if (a.B <= kPlanLdsRequests) {
-    for (int i = tid; i <= a.B; i += kPlanThreads) {
+    for (int i = tid; i <= a.B; i += PT) {
       s_qsl[i] = a.qsl[i];
       if (i < a.B) {
         s_klen[i] = a.klen[i];
@@ -712,15 +716,16 @@ __device__ void plan_role(const KArgs& a, uint32_t* lds) {
       }
     }
     __syncthreads();
-    plan_body(a, Meta{s_qsl, s_klen, a.smod ? s_smod : nullptr}, sh);
+    plan_body<PT>(a, Meta{s_qsl, s_klen, a.smod ? s_smod : nullptr}, sh);
   } else {
-    plan_body(a, global_meta(a), sh);
+    plan_body<PT>(a, global_meta(a), sh);
   }
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(KArgs a) {
+template <int PT>
+__global__ __launch_bounds__(PT) void plan_kernel(KArgs a) {
   __shared__ uint32_t lds[kPlanLdsWords];
-  plan_role(a, lds);
+  plan_role<PT>(a, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1871,7 +1876,9 @@ int launch(const qli_params* p, const WsLayout& w, void* stream) {
       consumer_prep_sort_kernel<<<T + 1, kPrepThreads, 0, st>>>(a);
   } else {
     Stamp s(QLI_KERNEL_PLAN, st);
-    plan_kernel<<<1, kPlanThreads, 0, st>>>(a);
+    // a decode-sized batch is planned by one wave
+    if (p->num_tokens <= 64 && p->batch <= 256) plan_kernel<64><<<1, 64, 0, st>>>(a);
+    else plan_kernel<kPlanThreads><<<1, kPlanThreads, 0, st>>>(a);
   }
   if (w.ncap > 0) {
     Stamp s(QLI_KERNEL_SCORE, st);
