@@ -1108,19 +1108,9 @@ __device__ void run_multi(const KArgs& a, const ListView& L, Cursor cur, int hi,
         sum = 0.0f;
       }
       // each step schedules one unit's MFMAs against the previous unit's
-      // epilogue, no further (bounds the live registers): the K fragment
-      // reads first, then one MFMA every dozen VALU instructions, so each
-      // MFMA finds the matrix core free and its chain predecessor done
-#ifdef QLI_SCHED_GROUPS
-      if (u + 1 < NU) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
-        }
-      }
-#endif
+      // epilogue, no further (bounds the live registers); inside the step
+      // the compiler's own order measured faster than forced interleavings
+      // of one to four MFMAs per 12 to 48 VALU instructions
       __builtin_amdgcn_sched_barrier(0);
     }
     cur = n1;
