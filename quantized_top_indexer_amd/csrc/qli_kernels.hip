@@ -1,27 +1,29 @@
 // HIP kernels of the quantized lightning indexer for CDNA4 (gfx950).
 //
-// One call = up to four kernels (DeepSeek V4.1 QLI developer guide, "数据流"
+// One call = three launches (DeepSeek V4.1 QLI developer guide, "数据流"
 // and "当前 A3 契约"):
-//   consumer_prep  (consumer mode) one workgroup per token: sort and
-//                  de-duplicate the incoming candidate block ids, drop ids
-//                  without a visible position, resolve each kept block to its
-//                  page row -> dense slot list + eligible count.
-//   plan           one workgroup: cut the batch into groups (up to 4
-//                  consecutive query tokens of one request in plain/source
-//                  mode, one token in consumer mode) and prefix-sum their
-//                  256-slot work units, so that a persistent kernel can split
-//                  any mix of decode tokens and prefill chunks evenly.
+//   plan           one workgroup (one wave for decode-sized batches): cut the
+//                  batch into groups (up to 4 consecutive query tokens of one
+//                  request in plain/source mode, one token in consumer mode)
+//                  and prefix-sum their 256-slot work units, so that a
+//                  persistent kernel can split any mix of decode tokens and
+//                  prefill chunks evenly.  In consumer mode it is block 0 of
+//   consumer_prep  (consumer mode) one workgroup per token: de-duplicate the
+//                  incoming candidate block ids, drop ids without a visible
+//                  position, resolve each kept block to its page row -> dense
+//                  slot list + eligible count.
 //   score          persistent, two workgroups per CU.  Each workgroup walks a
 //                  contiguous range of work items (group, 256-slot chunk) with
-//                  a three-stage software pipeline: page lookup two items
-//                  ahead, K + scale loads one item ahead (registers), and for
-//                  the current item an LDS tile shared by the group's tokens,
-//                  INT8 MFMA (v_mfma_i32_32x32x32_i8, queries x keys), the
-//                  golden FP16/FP32 epilogue, block maxima and order keys.
+//                  a software pipeline: page lookup ahead, K + scale loads one
+//                  item ahead (registers), and for the current item an LDS
+//                  tile (shared by a group's 4 tokens, or each wave's own rows
+//                  for single tokens), INT8 MFMA (v_mfma_i32_32x32x32_i8,
+//                  queries x keys), the golden FP16/FP32 epilogue, block
+//                  maxima and order keys.
 //   select         one workgroup per (token, positions|blocks): keys held in
-//                  registers, radix select on 11/11/10-bit digits, then one
-//                  block scan for an ordered compaction that emits the winners
-//                  already in ascending order, -1 tail.
+//                  registers, range-adaptive radix select (2048-bin digits),
+//                  then an ordered compaction that emits the winners already
+//                  in ascending order, -1 tail.
 //
 // Exactness: the epilogue applies one IEEE round-to-nearest-even per golden
 // step and sums heads in ascending order from +0.0f in a single lane, so the
