@@ -219,6 +219,22 @@ def test_bad_page_when_everything_fits():
         assert np.array_equal(res["cand"][t], clean["cand"][t])
 
 
+def test_consumer_mostly_invalid_candidates():
+    """Consumer tokens whose incoming lists are mostly -1: the plan bounds the
+    work by the list width, the prepared eligible count is far smaller, and
+    the items past it must load nothing and score as not eligible."""
+    import qli_workloads as W
+    req = W.Requests(n=np.array([2, 1, 3]), S=np.array([9000, 300, 20000]))
+    pb = W.build_problem("consumer_sparse_in", 320, req, ratio=2, num_heads=64, mode=3, topk=500,
+                         cand_in_blocks=512, p_invalid=0.9)
+    say(f"consumer sparse: T={pb.num_tokens} valid ids per token "
+        f"{[int((pb.cand_in[t, 0] >= 0).sum()) for t in range(pb.num_tokens)]}")
+    gpu = run_gpu(pb, debug=True)
+    orc = oracle_rows(pb, scores=True)
+    compare(pb, gpu, orc)
+    check_invariants(pb, gpu)
+
+
 def test_zero_tokens():
     import torch
 
