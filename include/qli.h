@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define QLI_ABI_VERSION 1
+#define QLI_ABI_VERSION 2
 
 /* Status codes returned by the host entry points. */
 enum qli_status {
@@ -149,6 +149,10 @@ typedef struct qli_params {
   float* dbg_scores;    /* optional (NULL in production): [T, max_k_len]
                            FP32 scores by position, written only where a
                            position is eligible */
+  int32_t* dbg_qk;      /* optional (NULL in production), needs dbg_scores:
+                           [T, N, max_k_len] exact INT32 q.k by token, head
+                           and position, written only where the position is
+                           eligible */
   uint32_t* status_out; /* optional device word receiving QLI_DEV_* bits
                            (never cleared by the library) */
 

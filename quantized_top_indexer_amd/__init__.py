@@ -43,7 +43,7 @@ class qli_params(C.Structure):
         ("query_start_loc", C.c_void_p), ("k_lens", C.c_void_p), ("seq_mod", C.c_void_p),
         ("cand_in", C.c_void_p),
         ("topk_out", C.c_void_p), ("cand_out", C.c_void_p), ("dbg_scores", C.c_void_p),
-        ("status_out", C.c_void_p),
+        ("dbg_qk", C.c_void_p), ("status_out", C.c_void_p),
         ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
     ]
 
@@ -262,7 +262,8 @@ def _ptr(t):
 
 def make_params(*, q, q_scale, weights, k_cache, k_scale, block_table, query_start_loc, k_lens,
                 seq_mod=None, cand_in=None, ratio, mode, topk, cand_blocks=0, max_k_len,
-                topk_out=None, cand_out=None, dbg_scores=None, status_out=None, workspace=None):
+                topk_out=None, cand_out=None, dbg_scores=None, dbg_qk=None, status_out=None,
+                workspace=None):
     """Fill qli_params from torch tensors.
 
     k_cache: int8 view [num_pages, page_rows, 128] of the paged index K (row
@@ -292,7 +293,7 @@ def make_params(*, q, q_scale, weights, k_cache, k_scale, block_table, query_sta
         _ptr(k_lens)
     p.seq_mod, p.cand_in = _ptr(seq_mod), _ptr(cand_in)
     p.topk_out, p.cand_out = _ptr(topk_out), _ptr(cand_out)
-    p.dbg_scores, p.status_out = _ptr(dbg_scores), _ptr(status_out)
+    p.dbg_scores, p.dbg_qk, p.status_out = _ptr(dbg_scores), _ptr(dbg_qk), _ptr(status_out)
     if workspace is not None:
         p.workspace, p.workspace_bytes = _ptr(workspace), workspace.numel()
     return p
@@ -300,12 +301,14 @@ def make_params(*, q, q_scale, weights, k_cache, k_scale, block_table, query_sta
 
 def score_topk(*, q, q_scale, weights, k_cache, k_scale, block_table, query_start_loc, k_lens,
                seq_mod=None, cand_in=None, ratio, mode, topk, cand_blocks=0, max_k_len,
-               debug_scores=False, status_out=None, workspace=None, stream=None):
+               debug_scores=False, dbg_qk=None, status_out=None, workspace=None, stream=None):
     """One indexer call on torch device tensors.
 
     Returns ``(indices [T,1,topk] int32, candidates [T,1,cb] int32 or None,
-    dbg_scores [T, max_k_len] float32 or None)``.  Raises RuntimeError with
-    the library's status string on a rejected call.
+    dbg_scores [T, max_k_len] float32 or None)``.  ``dbg_qk`` (optional, with
+    ``debug_scores``): an int32 tensor [T, N, max_k_len] that receives the
+    exact q.k of every eligible (token, head, position).  Raises RuntimeError
+    with the library's status string on a rejected call.
     """
     import torch
     dev = q.device
@@ -320,7 +323,7 @@ def score_topk(*, q, q_scale, weights, k_cache, k_scale, block_table, query_star
                     block_table=block_table, query_start_loc=query_start_loc, k_lens=k_lens,
                     seq_mod=seq_mod, cand_in=cand_in, ratio=ratio, mode=mode, topk=topk,
                     cand_blocks=cand_blocks, max_k_len=max_k_len, topk_out=topk_out,
-                    cand_out=cand_out, dbg_scores=dbg, status_out=status_out)
+                    cand_out=cand_out, dbg_scores=dbg, dbg_qk=dbg_qk, status_out=status_out)
     need = qli_workspace_bytes(p)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)

@@ -115,6 +115,7 @@ int qli_validate(const qli_params* p) {
       !p->query_start_loc || !p->k_lens || !p->topk_out)
     return QLI_ERR_INVALID_ARG;
   if (p->mode == QLI_MODE_SOURCE && !p->cand_out) return QLI_ERR_INVALID_ARG;
+  if (p->dbg_qk && (!p->dbg_scores || !aligned(p->dbg_qk, 4))) return QLI_ERR_INVALID_ARG;
   if (!aligned(p->q, 16) || !aligned(p->k_cache, 16) || !aligned(p->k_scale, 16) ||
       !aligned(p->q_scale, 2) || !aligned(p->weights, 2) || !aligned(p->block_table, 4) ||
       !aligned(p->query_start_loc, 4) || !aligned(p->k_lens, 4) || !aligned(p->topk_out, 4))

@@ -96,6 +96,7 @@ struct KArgs {
   int32_t* topk_out;
   int32_t* cand_out;
   float* dbg;
+  int32_t* dbg_qk;  // [T, NH, max_k_len] exact q.k (debug only)
   uint32_t* status;
   uint32_t* keys;
   uint32_t* bkeys;
@@ -1038,6 +1039,30 @@ __device__ __forceinline__ void finish_subtile(const KArgs& a, const uint16_t* k
   }
 }
 
+// Debug only: the exact q.k of one pass's accumulators (lane l holds heads
+// 32 ps + 16 (l / 32) + i, i < 16, for slot s0 + 32 n + l % 32 of accumulator
+// n; the accumulator holds the seed plus q.k), stored where the slot is
+// eligible.
+template <int NH, int MODE>
+__device__ __forceinline__ void dbg_store_qk(const KArgs& a, const i32x16 (&acc)[2], int ps, int t,
+                                             int s0, int n_i, const uint16_t* ksc, int sub, int lane) {
+  if (!a.dbg_qk) return;
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int in_tile = 32 * n + (lane & 31);
+    const int slot = s0 + in_tile;
+    if (slot >= n_i || ksc[64 * sub + in_tile] == 0xFFFFu) continue;
+    const int pos = MODE == QLI_MODE_CONSUMER
+                        ? a.slots[static_cast<int64_t>(t) * a.cb_in + (slot >> 3)] * 8 + (slot & 7)
+                        : slot;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int head = 32 * ps + 16 * (lane >> 5) + i;
+      a.dbg_qk[(static_cast<int64_t>(t) * NH + head) * a.max_k_len + pos] = acc[n][i] - kSeedBits;
+    }
+  }
+}
+
 // One sub-tile, the passes one after the other (a loop: overlapping them
 // would keep two head tiles of accumulators live).
 template <int NH, int MODE, bool DBG, class QSrc>
@@ -1050,6 +1075,7 @@ __device__ __forceinline__ void score_subtile(const KArgs& a, const QSrc& qs,
   for (int ps = 0; ps < NH / 32; ++ps) {
     i32x16 acc[2];
     mfma_pass(qs, tile, sub, ps, lane, seed, acc);
+    if (DBG) dbg_store_qk<NH, MODE>(a, acc, ps, t, s0, n_i, ksc, sub, lane);
     epi_pass<false>(qs, acc, ps, lane, a.one, sum);
   }
   finish_subtile<MODE, DBG>(a, ksc, sub, t, s0, n_i, lane, sum, kp, bp);
@@ -1100,6 +1126,9 @@ __device__ void run_multi(const KArgs& a, const ListView& L, Cursor cur, int hi,
         if (u & 1) mfma_pass(q, tl, (u + 1) / P, (u + 1) % P, lane, seed, accA);
         else mfma_pass(q, tl, (u + 1) / P, (u + 1) % P, lane, seed, accB);
       }
+      if (DBG)
+        dbg_store_qk<NH, MODE>(a, (u & 1) ? accB : accA, u % P, t, cur.c * kChunk + 64 * (u / P), n_i,
+                               ksc[buf], u / P, lane);
       epi_pass<true>(q, (u & 1) ? accB : accA, u % P, lane, one, sum);
       if (u % P == P - 1) {
         finish_subtile<MODE, DBG>(a, ksc[buf], u / P, t, cur.c * kChunk + 64 * (u / P), n_i, lane, sum,
@@ -1841,6 +1870,7 @@ int launch(const qli_params* p, const WsLayout& w, void* stream) {
   a.topk_out = p->topk_out;
   a.cand_out = p->cand_out;
   a.dbg = p->dbg_scores;
+  a.dbg_qk = p->dbg_qk;
   a.status = p->status_out;
   char* ws = static_cast<char*>(p->workspace);
   const bool consumer = p->mode == QLI_MODE_CONSUMER;

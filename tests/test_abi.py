@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert Q.qli_abi_version() == 1
+    assert Q.qli_abi_version() == 2
 
 
 @pytest.mark.parametrize("struct", ["qli_params", "qli_quant_params", "qli_kwrite_params"])
@@ -91,6 +91,7 @@ def test_valid_params_pass(lib):
 
 
 @pytest.mark.parametrize("field,value,code", [
+    ("dbg_qk", 0x7F0000100000, Q.QLI_ERR_INVALID_ARG),  # debug q.k without debug scores
     ("struct_size", 8, Q.QLI_ERR_INVALID_ARG),
     ("head_dim", 64, Q.QLI_ERR_UNSUPPORTED),
     ("quant_mode", 1, Q.QLI_ERR_UNSUPPORTED),
@@ -279,3 +280,12 @@ def test_write_k_noop(lib):
     assert Q.qli_write_index_k(p, 0) == Q.QLI_OK
     p.page_rows = 100  # scalars are still checked with no rows
     assert Q.qli_write_index_k(p, 0) == Q.QLI_ERR_INVALID_ARG
+
+
+def test_debug_qk_alignment(lib):
+    p = base_params(mode=2, ratio=2)
+    p.dbg_scores = 0x7F0000200000
+    p.dbg_qk = 0x7F0000100002
+    assert Q.qli_validate(p) == Q.QLI_ERR_INVALID_ARG
+    p.dbg_qk = 0x7F0000100000
+    assert Q.qli_validate(p) == Q.QLI_OK

@@ -235,6 +235,41 @@ def test_consumer_mostly_invalid_candidates():
     check_invariants(pb, gpu)
 
 
+@pytest.mark.parametrize("mode,ratio,N", [(2, 2, 64), (1, 1, 32), (3, 2, 64)])
+def test_debug_qk_matches_oracle(mode, ratio, N):
+    """The debug output of the exact INT32 q.k (both score paths: a request
+    with 8 queries forms 4-token groups, the others are single tokens) at
+    sampled (token, position) pairs, every head; positions that are not
+    eligible keep the caller's fill."""
+    import torch
+
+    import oracle
+    import quantized_top_indexer_amd as Q
+    from qli_workloads.device import call_kwargs, to_device
+    pb = small_problem(330 + mode, ratio=ratio, N=N, mode=mode, topk=64, cb=64, cb_in=64,
+                       requests=((8, 1500), (1, 700), (2, 300)))
+    dev = to_device(pb, "cuda")
+    kw = call_kwargs(pb, dev)
+    L = pb.max_k_len
+    fill = -(2 ** 31) + 7
+    dq = torch.full((pb.num_tokens, N, L), fill, dtype=torch.int32, device="cuda")
+    _, _, dbg = Q.score_topk(**kw, debug_scores=True, dbg_qk=dq)
+    torch.cuda.synchronize()
+    got = dq.cpu().numpy()
+    scores = dbg.cpu().numpy()
+    o = oracle.OracleProblem(pb)
+    rng = np.random.default_rng(5)
+    checked = 0
+    for t in range(pb.num_tokens):
+        elig = np.flatnonzero(~np.isnan(scores[t]))
+        assert np.all(got[t][:, np.isnan(scores[t])] == fill)  # nothing written elsewhere
+        for j in rng.choice(elig, size=min(12, len(elig)), replace=False) if len(elig) else []:
+            want = o.terms(t, int(j))["qk"]
+            assert np.array_equal(got[t, :, j], want), (t, j)
+            checked += 1
+    assert checked > 50
+
+
 def test_zero_tokens():
     import torch
 
