@@ -291,6 +291,57 @@ def measure_producers(steps, warmup, copies=2):
     return out
 
 
+def measure_ceilings():
+    """What this GPU sustains: a 2 GiB streaming read with 16-byte
+    non-temporal loads (GB/s) and back-to-back independent INT8 MFMAs on
+    every SIMD (TOP/s), each the best of 10 timed launches after 3 warm-ups
+    (include/qli_probe.h)."""
+    import torch
+
+    import quantized_top_indexer_amd as Q
+    sink = torch.zeros(65536, dtype=torch.int32, device="cuda")
+    buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+
+    def best(launch):
+        for _ in range(3):
+            launch()
+        t = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            launch()
+            e1.record()
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1) * 1e-3)
+        return min(t)
+
+    def read():
+        rc = Q.qli_probe_hbm_read(buf.data_ptr(), buf.numel(), 4096, sink.data_ptr())
+        assert rc == Q.QLI_OK, Q.qli_status_string(rc)
+
+    grid, iters = 2048, 20000
+
+    def mfma():
+        rc = Q.qli_probe_int8_mfma(grid, iters, sink.data_ptr())
+        assert rc == Q.QLI_OK, Q.qli_status_string(rc)
+    hbm = buf.numel() / best(read) / 1e9
+    tops = Q.qli_probe_int8_mfma_ops(grid, iters) / best(mfma) / 1e12
+    del buf
+    torch.cuda.empty_cache()
+    return {"hbm_read_GBps": round(hbm, 1), "int8_mfma_TOPs": round(tops, 1)}
+
+
+def with_measured(roof, ceilings):
+    """Add the measured ceiling of the roofline's unit and the fraction of it."""
+    if not ceilings:
+        return roof
+    peak = ceilings["hbm_read_GBps"] if roof["unit"] == "GB/s" else ceilings["int8_mfma_TOPs"]
+    roof["measured_peak"] = peak
+    roof["frac_of_measured"] = round(roof["achieved"] / peak, 4)
+    return roof
+
+
 def _producer_line(name, kernel, kms, nbytes, rows, config):
     achieved = nbytes / (kms * 1e-3) / 1e9
     traffic, summary = recorded_traffic(name, kernel, source="qli_quant.hip")
@@ -338,6 +389,8 @@ def main():
                     help="comma list of secondary workloads ('' for none)")
     ap.add_argument("--no-producers", action="store_true",
                     help="skip the query-quantization and index-K write measurements")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured HBM-read and INT8-MFMA ceilings")
     ap.add_argument("--producers-only", action="store_true",
                     help="only measure the producers (one JSON object, for profiling runs)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MIB",
@@ -406,6 +459,15 @@ def main():
         for k, v in producers.items():
             log(f"{k}: {v['kernel_ms']:.5f} ms {v['roofline']['achieved']} GB/s")
 
+    ceilings = None
+    if not args.no_ceilings:
+        log("ceilings: streaming read and INT8 MFMA probes")
+        ceilings = measure_ceilings()
+        log(f"ceilings: {ceilings}")
+        with_measured(main_m["roofline"], ceilings)
+        for v in list(others.values()) + list(producers.values()):
+            with_measured(v["roofline"], ceilings)
+
     cpu = None
     if not args.no_cpu_baseline and pb.mode != 3:
         log("cpu baseline: oracle on the host")
@@ -436,6 +498,7 @@ def main():
         "kernels_ms": main_m["kernels_ms"],
         "other_workloads": others,
         "producers": producers,
+        "measured_ceilings": ceilings,
     }
     print(json.dumps(line), flush=True)
 

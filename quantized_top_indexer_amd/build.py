@@ -11,7 +11,7 @@ OUT = os.path.join(HERE, "libqli.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = [os.path.join(CSRC, "qli_api.cpp"), os.path.join(CSRC, "qli_kernels.hip"),
-           os.path.join(CSRC, "qli_quant.hip")]
+           os.path.join(CSRC, "qli_quant.hip"), os.path.join(CSRC, "qli_probe.hip")]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

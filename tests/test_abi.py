@@ -24,7 +24,7 @@ def lib():
 
 
 def declared_functions():
-    src = open(HEADER).read()
+    src = open(HEADER).read() + open(os.path.join(ROOT, "include", "qli_probe.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(qli_\w+)\s*\(", src, flags=re.M)
 
@@ -289,3 +289,14 @@ def test_debug_qk_alignment(lib):
     assert Q.qli_validate(p) == Q.QLI_ERR_INVALID_ARG
     p.dbg_qk = 0x7F0000100000
     assert Q.qli_validate(p) == Q.QLI_OK
+
+
+def test_probe_rejections(lib):
+    fake = 0x7F0000000000
+    assert Q.qli_probe_hbm_read(fake, 1 << 20, 64, None, 0) == Q.QLI_ERR_INVALID_ARG   # no sink
+    assert Q.qli_probe_hbm_read(fake, 100, 64, fake, 0) == Q.QLI_ERR_INVALID_ARG       # not x16 bytes
+    assert Q.qli_probe_hbm_read(fake + 8, 1 << 20, 64, fake, 0) == Q.QLI_ERR_INVALID_ARG
+    assert Q.qli_probe_hbm_read(fake, 1 << 20, 0, fake, 0) == Q.QLI_ERR_INVALID_ARG
+    assert Q.qli_probe_int8_mfma(0, 10, fake, 0) == Q.QLI_ERR_INVALID_ARG
+    assert Q.qli_probe_int8_mfma(16, 0, fake, 0) == Q.QLI_ERR_INVALID_ARG
+    assert Q.qli_probe_int8_mfma_ops(2, 3) == 2 * 4 * 3 * 4 * 32 * 32 * 32 * 2
