@@ -78,3 +78,38 @@ def test_mixed_source_then_consumer():
         compare(con, cres, corc, tokens=tok, scores=False)
         del gpu_cand
         _free()
+
+
+def test_longest_context_source():
+    """One query at the longest supported context (2^24 compressed positions,
+    ratio 2): the chunked selection over 512 chunks of keys.  Scores at
+    sampled positions equal the oracle's, and the returned positions and
+    blocks are exactly the best ones by the GPU's own scores (properties that
+    hold at any size; the oracle's full row would take minutes)."""
+    import torch
+
+    import oracle
+    import quantized_top_indexer_amd as Q
+    L = 1 << 24
+    assert L == 16777216  # QLI_MAX_K_LEN
+    req = W.Requests(n=np.array([1]), S=np.array([2 * L]))
+    pb = W.build_problem("longest", 9, req, ratio=2, num_heads=32, mode=2, topk=2048,
+                         cand_blocks=2048, extra_pages=0)
+    say(f"longest context: L={pb.max_k_len} pages={pb.num_pages}")
+    res = run_gpu(pb, debug=True)
+    sc = res["scores"][0]
+    assert not np.any(np.isnan(sc))
+    o = oracle.OracleProblem(pb)
+    rng = np.random.default_rng(9)
+    for j in np.concatenate([rng.integers(0, L, 150), [0, L - 1, 32767, 32768]]):
+        assert sc[j] == o.terms(0, int(j))["score"], j
+    # positions: the top 2048 by (score desc, position asc), ascending
+    order = np.lexsort((np.arange(L), -sc.astype(np.float64)))
+    assert np.array_equal(res["topk"][0], np.sort(order[:2048]))
+    # blocks: the last block pinned plus the best 2047 others by (max desc, id asc)
+    bm = sc.reshape(-1, 8).max(axis=1)
+    nb = L // 8
+    others = np.lexsort((np.arange(nb - 1), -bm[:-1].astype(np.float64)))[:2047]
+    assert np.array_equal(res["cand"][0], np.sort(np.concatenate([others, [nb - 1]])))
+    del res, sc
+    _free()
