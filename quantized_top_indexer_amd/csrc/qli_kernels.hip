@@ -1404,14 +1404,22 @@ __device__ __forceinline__ void refine_threshold(Each each, uint32_t lo, uint32_
         const uint32_t key = rk[i], idx = ri[i];
         const uint32_t gt = static_cast<uint32_t>(__popcll(__ballot(has && kq > key)));
         const uint32_t eqb = static_cast<uint32_t>(__popcll(__ballot(has && kq == key && iq < idx)));
+        const uint32_t eqall = static_cast<uint32_t>(__popcll(__ballot(has && kq == key)));
         if (lane == 0 && gt + eqb == krem - 1) {
           misc[0] = key;
           misc[1] = eqb + 1;
+          misc[2] = eqall;
         }
       }
       __syncthreads();
       thr = misc[0];
       need = misc[1];
+      // every key equal to the threshold is taken: the same set is "keys >
+      // thr - 1" (keys are non-zero), with no tie to resolve
+      if (misc[2] == need) {
+        thr -= 1;
+        need = 0;
+      }
       return;
     }
   }
@@ -1645,7 +1653,56 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n, int cap
   // as gt << 16 | eq; a chunk holds at most 32768 keys).  The winners' key
   // indices are staged in LDS and written out in order.
   uint32_t run_gt = 0, run_eq = 0;
-  for (int ch = 0; ch < nch; ++ch) {
+  static_assert(4 * VPT <= 32, "one winner bit per key of a chunk");
+  if (need == 0) {
+    // no tie at the threshold: the winners are the keys > thr; one mask bit
+    // per key (vector j, element e -> bit 4j + e) is computed once
+    for (int ch = 0; ch < nch; ++ch) {
+      if (MULTI && nch > 1) load(ch);
+      uint32_t gm = 0;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        if (j >= nvec) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gm |= (kr[4 * j + e] > thr ? 1u : 0u) << (4 * j + e);
+      }
+      uint32_t excl[VPT];
+      uint32_t wsum = 0;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        excl[j] = wsum;
+        if (j >= nvec) continue;
+        const uint32_t c = static_cast<uint32_t>(__popc((gm >> (4 * j)) & 0xFu));
+        const uint32_t inc = wave_inclusive_scan(c);
+        excl[j] = wsum + inc - c;
+        wsum += static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(inc), 63));
+      }
+      if (lane == 0) sh[wave] = wsum;
+      __syncthreads();
+      uint32_t wbase = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const uint32_t x = sh[w];
+        wbase += w < wave ? x : 0u;
+        tot += x;
+      }
+      __syncthreads();  // sh is reused
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        if (j >= nvec) continue;
+        uint32_t at = run_gt + wbase + excl[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if ((gm >> (4 * j + e)) & 1u) {
+            ol[at] = index_of(ch, j, e);
+            ++at;
+          }
+        }
+      }
+      run_gt += tot;
+    }
+  }
+  for (int ch = 0; ch < (need == 0 ? 0 : nch); ++ch) {
     if (MULTI && nch > 1) load(ch);
     auto flag = [&](uint32_t key) {
       return key > thr ? (1u << 16) : ((key == thr && need != 0) ? 1u : 0u);
