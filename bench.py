@@ -379,8 +379,10 @@ def cpu_baseline(pb, budget_tokens=None):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps first: the GPU reaches its sustained clocks only after "
+                         "some milliseconds of continuous work")
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--workload", default="decode_source",
                     help="main workload (decode_source is the headline configuration)")
