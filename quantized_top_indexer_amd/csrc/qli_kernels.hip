@@ -35,6 +35,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "qli.h"
@@ -224,6 +225,21 @@ __device__ __forceinline__ float qk_over_1024(int32_t acc) {
   asm volatile("" : "+v"(y));
   return y;
 }
+
+// Scaled form of the same step with the ReLU folded in: y = qk * 2^-21 =
+// 2^-12 * F - 6 (exact), clamped to [0, 1] by the fma's clamp bit, gives
+// max(qk, 0) * 2^-21, and fp16(y) = fp16(qk/1024) * 2^-11 exactly (for
+// qk < 128, y is an fp16 subnormal on the 2^-21 grid; above, scaling by a
+// power of two commutes with rounding), so fp16(fp16(y) * m * 2^11) equals
+// the golden fp16(relu(fp16(qk/1024)) * m) whenever m * 2^11 is still a
+// finite fp16 (|m| < 32).  One clamped fma per value instead of an fma
+// plus half a packed max.
+__device__ __forceinline__ float qk_relu_scaled(int32_t acc) {
+  float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(__int_as_float(acc), 0x1p-12f, -6.0f), 0.0f, 1.0f);
+  asm volatile("" : "+v"(y));
+  return y;
+}
+constexpr uint32_t kHalfAbs32 = 0x5000u;  // fp16 bits of 32.0
 
 // s + float(h) with one FP32 rounding: fma(h, one, s) with one == 1.0 held
 // in a kernel argument (opaque to constant folding) selects v_fma_mix_f32.
@@ -878,6 +894,7 @@ struct QState {
   i32x4 qa[NH / 32][4];
   h2 mh[NH / 4];  // pairs of multipliers in the order the epilogue consumes them
   int tok;
+  bool scaled;    // mh holds m * 2^11 (every |m| < 32): the scaled epilogue applies
 };
 
 template <int NH, bool SPLIT>
@@ -899,6 +916,20 @@ __device__ __forceinline__ void load_q(const KArgs& a, int t, int lane, QState<N
     // pair j covers heads (SPLIT) 32*(j/8) + 16g + 2*(j%8) or (else) g*N/2 + 2j
     const int h0 = SPLIT ? 32 * (j >> 3) + 16 * g + 2 * (j & 7) : g * HALF + 2 * j;
     qs.mh[j] = as_h2(wr[h0 >> 1]) * as_h2(qr[h0 >> 1]);  // fp16 RNE
+  }
+  // the scaled epilogue needs m * 2^11 finite for every head of the token
+  // (NaN and infinite multipliers fail the test as well)
+  bool small = true;
+#pragma unroll
+  for (int j = 0; j < HALF / 2; ++j) {
+    const uint32_t u = as_u32(qs.mh[j]);
+    small = small && (u & 0x7FFFu) < kHalfAbs32 && ((u >> 16) & 0x7FFFu) < kHalfAbs32;
+  }
+  qs.scaled = __builtin_amdgcn_ballot_w64(!small) == 0;
+  if (qs.scaled) {
+    const h2 k2048 = {static_cast<_Float16>(2048.0f), static_cast<_Float16>(2048.0f)};
+#pragma unroll
+    for (int j = 0; j < HALF / 2; ++j) qs.mh[j] = qs.mh[j] * k2048;  // exact
   }
   qs.tok = t;
 }
@@ -976,7 +1007,9 @@ __device__ __forceinline__ void mfma_pass(const QSrc& qs, const int8_t* tile, in
 
 // x = fp16(qk/1024), ReLU, p = fp16(x * m) (packed two heads per word), then
 // the 32 heads of the pass added to sum in ascending order.
-template <bool PACKED_CVT, class QSrc>
+// SCALED: the multipliers are m * 2^11 and the ReLU rides on the clamp
+// (qk_relu_scaled); same products bit for bit.
+template <bool PACKED_CVT, bool SCALED, class QSrc>
 __device__ __forceinline__ void epi_pass(const QSrc& qs, const i32x16 (&acc)[2], int ps, int lane,
                                          float one, float& sum) {
   uint32_t pk[2][8];
@@ -984,10 +1017,16 @@ __device__ __forceinline__ void epi_pass(const QSrc& qs, const i32x16 (&acc)[2],
   for (int n = 0; n < 2; ++n)
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
-      const h2 x0 = PACKED_CVT ? h2{static_cast<_Float16>(qk_over_1024(acc[n][i])),
-                                    static_cast<_Float16>(qk_over_1024(acc[n][i + 1]))}
-                               : h2{qk_to_half(acc[n][i]), qk_to_half(acc[n][i + 1])};
-      const h2 x = as_h2(relu_h2(as_u32(x0)));
+      h2 x;
+      if (SCALED) {
+        x = h2{static_cast<_Float16>(qk_relu_scaled(acc[n][i])),
+               static_cast<_Float16>(qk_relu_scaled(acc[n][i + 1]))};
+      } else {
+        const h2 x0 = PACKED_CVT ? h2{static_cast<_Float16>(qk_over_1024(acc[n][i])),
+                                      static_cast<_Float16>(qk_over_1024(acc[n][i + 1]))}
+                                 : h2{qk_to_half(acc[n][i]), qk_to_half(acc[n][i + 1])};
+        x = as_h2(relu_h2(as_u32(x0)));
+      }
       pk[n][i >> 1] = as_u32(x * qs.mul(ps * 8 + (i >> 1), lane));
     }
   uint32_t hi[8];
@@ -1076,7 +1115,7 @@ __device__ __forceinline__ void score_subtile(const KArgs& a, const QSrc& qs,
     i32x16 acc[2];
     mfma_pass(qs, tile, sub, ps, lane, seed, acc);
     if (DBG) dbg_store_qk<NH, MODE>(a, acc, ps, t, s0, n_i, ksc, sub, lane);
-    epi_pass<false>(qs, acc, ps, lane, a.one, sum);
+    epi_pass<false, false>(qs, acc, ps, lane, a.one, sum);
   }
   finish_subtile<MODE, DBG>(a, ksc, sub, t, s0, n_i, lane, sum, kp, bp);
 }
@@ -1117,32 +1156,56 @@ __device__ void run_multi(const KArgs& a, const ListView& L, Cursor cur, int hi,
     if (t != qs.tok) load_q<NH, true>(a, t, lane, qs);
     const QRegs<NH, true> q{qs};
     const int8_t* tl = tile[buf];
-    i32x16 accA[2], accB[2];
-    float sum = 0.0f;
-    mfma_pass(q, tl, 0, 0, lane, seed, accA);
+    if (qs.scaled) {
+      // the item's units, pipelined, with the scaled epilogue
+      i32x16 accA[2], accB[2];
+      float sum = 0.0f;
+      mfma_pass(q, tl, 0, 0, lane, seed, accA);
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      if (u + 1 < NU) {
-        if (u & 1) mfma_pass(q, tl, (u + 1) / P, (u + 1) % P, lane, seed, accA);
-        else mfma_pass(q, tl, (u + 1) / P, (u + 1) % P, lane, seed, accB);
+      for (int u = 0; u < NU; ++u) {
+        if (u + 1 < NU) {
+          if (u & 1) mfma_pass(q, tl, (u + 1) / P, (u + 1) % P, lane, seed, accA);
+          else mfma_pass(q, tl, (u + 1) / P, (u + 1) % P, lane, seed, accB);
+        }
+        if (DBG)
+          dbg_store_qk<NH, MODE>(a, (u & 1) ? accB : accA, u % P, t, cur.c * kChunk + 64 * (u / P), n_i,
+                                 ksc[buf], u / P, lane);
+        epi_pass<true, true>(q, (u & 1) ? accB : accA, u % P, lane, one, sum);
+        if (u % P == P - 1) {
+          finish_subtile<MODE, DBG>(a, ksc[buf], u / P, t, cur.c * kChunk + 64 * (u / P), n_i, lane, sum,
+                                    a.keys + static_cast<int64_t>(t) * a.ncap + cur.c * kChunk,
+                                    MODE == QLI_MODE_SOURCE
+                                        ? a.bkeys + static_cast<int64_t>(t) * a.nbcap + cur.c * (kChunk / 8)
+                                        : nullptr);
+          sum = 0.0f;
+        }
+        // each step schedules one unit's MFMAs against the previous unit's
+        // epilogue, no further (bounds the live registers); inside the step
+        // the compiler's own order measured faster than forced interleavings
+        // of one to four MFMAs per 12 to 48 VALU instructions
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (DBG)
-        dbg_store_qk<NH, MODE>(a, (u & 1) ? accB : accA, u % P, t, cur.c * kChunk + 64 * (u / P), n_i,
-                               ksc[buf], u / P, lane);
-      epi_pass<true>(q, (u & 1) ? accB : accA, u % P, lane, one, sum);
-      if (u % P == P - 1) {
-        finish_subtile<MODE, DBG>(a, ksc[buf], u / P, t, cur.c * kChunk + 64 * (u / P), n_i, lane, sum,
+    } else {
+      // a token with some |m| >= 32 (never in practice): the plain
+      // epilogue, one sub-tile after the other (wave-uniform branch: each
+      // wave scores one token)
+#pragma unroll 1
+      for (int sub = 0; sub < 4; ++sub) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int ps = 0; ps < P; ++ps) {  // unrolled: the multipliers stay in registers
+          i32x16 acc[2];
+          mfma_pass(q, tl, sub, ps, lane, seed, acc);
+          if (DBG)
+            dbg_store_qk<NH, MODE>(a, acc, ps, t, cur.c * kChunk + 64 * sub, n_i, ksc[buf], sub, lane);
+          epi_pass<true, false>(q, acc, ps, lane, one, sum);
+        }
+        finish_subtile<MODE, DBG>(a, ksc[buf], sub, t, cur.c * kChunk + 64 * sub, n_i, lane, sum,
                                   a.keys + static_cast<int64_t>(t) * a.ncap + cur.c * kChunk,
                                   MODE == QLI_MODE_SOURCE
                                       ? a.bkeys + static_cast<int64_t>(t) * a.nbcap + cur.c * (kChunk / 8)
                                       : nullptr);
-        sum = 0.0f;
       }
-      // each step schedules one unit's MFMAs against the previous unit's
-      // epilogue, no further (bounds the live registers); inside the step
-      // the compiler's own order measured faster than forced interleavings
-      // of one to four MFMAs per 12 to 48 VALU instructions
-      __builtin_amdgcn_sched_barrier(0);
     }
     cur = n1;
     n1 = n2;

@@ -104,6 +104,45 @@ def test_heavy_ties(mode, patterns):
     check_invariants(pb, gpu)
 
 
+@pytest.mark.parametrize("ratio,N,mode", [(2, 64, 2), (1, 32, 1), (2, 32, 3)])
+def test_head_multiplier_ranges(ratio, N, mode):
+    """Head multipliers m = fp16(w * q_scale) across the ranges the score
+    kernel treats differently: |m| < 32 (m * 2^11 is a finite fp16, the
+    scaled epilogue), exactly 32 and -1024 (the plain epilogue for that
+    token), the largest fp16 below 32, and fp16-subnormal m.  Queries are
+    small so that no product overflows.  Requests of 5-9 queries make
+    groups of four tokens share K tiles, so tokens of one group take
+    different epilogues."""
+    pb = small_problem(330 + ratio + N + mode, ratio=ratio, N=N, mode=mode, topk=150, cb=64, cb_in=128,
+                       requests=((9, 3000), (5, 1100), (2, 500), (1, 64)))
+    rng = np.random.default_rng(331)
+    T = pb.num_tokens
+    pb.q = rng.integers(-3, 4, size=pb.q.shape).astype(np.int8)
+    w = pb.weights.view(np.float16).astype(np.float32).copy()
+    qs = pb.q_scale.view(np.float16).astype(np.float32).copy()
+    for t in range(T):
+        h = (7 * t) % N
+        kind = t % 5
+        if kind == 1:                      # m = 32 exactly: plain epilogue
+            w[t, h], qs[t, h] = 64.0, 0.5
+        elif kind == 2:                    # largest fp16 below 32: scaled
+            w[t, h], qs[t, h] = 31.984375, 1.0
+        elif kind == 3:                    # every m an fp16 subnormal
+            w[t] = np.where(rng.random(N) < 0.5, -1.0, 1.0) * 1e-3
+            qs[t] = rng.uniform(1e-3, 2e-2, N)
+        elif kind == 4:                    # a large negative m: plain epilogue
+            w[t, h], qs[t, h] = -1024.0, 1.0
+    pb.weights = w.astype(np.float16).view(np.uint16)
+    pb.q_scale = qs.astype(np.float16).view(np.uint16)
+    m = (pb.weights.view(np.float16).astype(np.float32) * pb.q_scale.view(np.float16).astype(np.float32))
+    assert np.any(np.abs(m) >= 32) and np.any((np.abs(m) < 2 ** -14) & (m != 0))
+    say(f"multipliers {pb.name}: T={T} L={pb.max_k_len}")
+    gpu = run_gpu(pb, debug=True)
+    orc = oracle_rows(pb, scores=True)
+    compare(pb, gpu, orc)
+    check_invariants(pb, gpu)
+
+
 def test_consumer_long_context_bound():
     """A context bound above 2^21 positions takes the sorting candidate
     preparation instead of the bitmap one: same outputs, same as the oracle."""
