@@ -850,6 +850,11 @@ __device__ __forceinline__ int resolve(const KArgs& a, const Addr& ad, bool& bad
 template <bool STREAM>
 __device__ __forceinline__ void stage_load(const KArgs& a, int v, int lane, i32x4 (&kr)[8],
                                            i32x4& sc) {
+  // the scales first: consumed first (stage_store), so waiting for them
+  // never waits for anything issued after the K rows
+  const int row = v < 0 ? 0 : v;
+  sc = *reinterpret_cast<const i32x4*>(a.ks + static_cast<int64_t>(row >> a.rlog) * a.sstride +
+                                       static_cast<int64_t>(row & (a.R - 1)) * 2);
   const int lane_off = (lane >> 3) * 128 + (lane & 7) * 16;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
@@ -860,25 +865,30 @@ __device__ __forceinline__ void stage_load(const KArgs& a, int v, int lane, i32x
     const i32x4* p = reinterpret_cast<const i32x4*>(src);
     kr[u] = STREAM ? __builtin_nontemporal_load(p) : *p;
   }
-  const int row = v < 0 ? 0 : v;
-  sc = *reinterpret_cast<const i32x4*>(a.ks + static_cast<int64_t>(row >> a.rlog) * a.sstride +
-                                       static_cast<int64_t>(row & (a.R - 1)) * 2);
 }
+
+// 16-byte slot of column group col (0..7) of tile row row (128 bytes).  The
+// LDS serves a 128-bit read 16 lanes at a time over 64 four-byte banks, so
+// two consecutive rows share the banks once and 16 consecutive rows reading
+// one column group (an MFMA B operand) must spread over the 8 slots in both
+// halves: slot = col ^ ((row / 2) mod 8).  Writes of one row (8 lanes, all
+// column groups) stay conflict-free as well.
+__device__ __forceinline__ int tile_slot(int row, int col) { return col ^ ((row >> 1) & 7); }
 
 // Into LDS: K tile rows with the XOR swizzle, scales of valid blocks (0xFFFF
 // halves mark a block without K rows).
 template <bool OWN>
 __device__ __forceinline__ void stage_store(int8_t* tile, uint16_t* ksc, const i32x4 (&kr)[8],
                                             const i32x4& sc, int v, int wave, int lane) {
+  if (lane < 8) {
+    const i32x4 none = {-1, -1, -1, -1};
+    *reinterpret_cast<i32x4*>(ksc + 8 * (OWN ? 8 * wave + lane : 4 * lane + wave)) = v < 0 ? none : sc;
+  }
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int row = 8 * (OWN ? 8 * wave + u : 4 * u + wave) + (lane >> 3);
     const int col = lane & 7;
-    *reinterpret_cast<i32x4*>(tile + row * 128 + ((col ^ (row & 7)) << 4)) = kr[u];
-  }
-  if (lane < 8) {
-    const i32x4 none = {-1, -1, -1, -1};
-    *reinterpret_cast<i32x4*>(ksc + 8 * (OWN ? 8 * wave + lane : 4 * lane + wave)) = v < 0 ? none : sc;
+    *reinterpret_cast<i32x4*>(tile + row * 128 + (tile_slot(row, col) << 4)) = kr[u];
   }
 }
 
@@ -989,6 +999,32 @@ __device__ __forceinline__ void load_q_lds(const KArgs& a, int t, i32x4* fr, uin
 // 32p+15 and lanes 32..63 heads 32p+16 .. 32p+31 of the same 64 positions,
 // and one v_permlane32_swap per register pair leaves each lane L with all
 // 32 heads of the pass for slot s0+L, summed in ascending head order.
+// The B fragments of one sub-tile (2 x 4 per lane), from the swizzled tile.
+__device__ __forceinline__ void load_b(const int8_t* tile, int sub, int lane, i32x4 (&b)[2][4]) {
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int row = 64 * sub + 32 * n + (lane & 31);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int col = 4 * (lane >> 5) + s;
+      b[n][s] = *reinterpret_cast<const i32x4*>(tile + row * 128 + (tile_slot(row, col) << 4));
+    }
+  }
+}
+
+// One pass from B fragments already in registers (every pass of a
+// sub-tile reuses them: the matrix core would otherwise wait on LDS reads).
+template <class QSrc>
+__device__ __forceinline__ void mfma_pass_b(const QSrc& qs, const i32x4 (&b)[2][4], int ps, int lane,
+                                            const i32x16& seed, i32x16 (&acc)[2]) {
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      acc[n] = __builtin_amdgcn_mfma_i32_32x32x32_i8(qs.frag(ps, s, lane), b[n][s], s == 0 ? seed : acc[n],
+                                                     0, 0, 0);
+}
+
 template <class QSrc>
 __device__ __forceinline__ void mfma_pass(const QSrc& qs, const int8_t* tile, int sub, int ps, int lane,
                                           const i32x16& seed, i32x16 (&acc)[2]) {
@@ -998,7 +1034,7 @@ __device__ __forceinline__ void mfma_pass(const QSrc& qs, const int8_t* tile, in
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int col = 4 * (lane >> 5) + s;
-      const i32x4 bk = *reinterpret_cast<const i32x4*>(tile + row * 128 + ((col ^ (row & 7)) << 4));
+      const i32x4 bk = *reinterpret_cast<const i32x4*>(tile + row * 128 + (tile_slot(row, col) << 4));
       acc[n] = __builtin_amdgcn_mfma_i32_32x32x32_i8(qs.frag(ps, s, lane), bk, s == 0 ? seed : acc[n],
                                                      0, 0, 0);
     }
@@ -1125,48 +1161,70 @@ __device__ __forceinline__ void score_subtile(const KArgs& a, const QSrc& qs,
 // t0 + w, keeping its queries in registers.  The item's (sub-tile, pass)
 // units form a software pipeline: the MFMAs of unit u + 1 are issued
 // before the epilogue of unit u, so the matrix core runs under the VALU
-// epilogue (two accumulator sets alternate).  One item of K in flight.
+// epilogue (two accumulator sets alternate).
+//
+// K staging, two LDS buffers: item i is scored from buffer i & 1 while,
+// halfway through it, each wave writes its part of item i + 1 (loaded into
+// registers halfway through item i - 1) into the other buffer and issues
+// the loads of item i + 2; the block-table lookups of item i + 2 are issued
+// when item i starts.  One workgroup barrier per item, at its end: every
+// wave has finished reading buffer i & 1 and written its part of item i + 1.
+// Waiting for K rows halfway through an item therefore never waits for
+// loads or score stores issued just before (the memory counter is in
+// order, so waiting for the last K load also waits for every older store).
 template <int NH, int MODE, bool DBG>
 __device__ void run_multi(const KArgs& a, const ListView& L, Cursor cur, int hi, int8_t (*tile)[kChunk * 128],
                           uint16_t (*ksc)[kChunk], int wave, int lane, const i32x16& seed, bool& bad) {
   constexpr int P = NH / 32;   // passes per sub-tile
   constexpr int NU = 4 * P;    // (sub-tile, pass) units per item
+  constexpr int MID = NU / 2;  // the next tile is written before the epilogue of unit MID
   Cursor n1 = next_item(L, cur, hi);
   Cursor n2 = next_item(L, n1, hi);
   Addr ad;
-  stage_addr<false, false>(a, cur.grp, cur.c, cur.valid, wave, lane, ad);
   i32x4 kr[8];
   i32x4 sc;
+  // prologue: item 0 into buffer 0, item 1 into registers
+  stage_addr<false, false>(a, cur.grp, cur.c, cur.valid, wave, lane, ad);
   int v = resolve<false>(a, ad, bad);
-  stage_addr<false, false>(a, n1.grp, n1.c, n1.valid, wave, lane, ad);
   stage_load<false>(a, v, lane, kr, sc);
+  stage_addr<false, false>(a, n1.grp, n1.c, n1.valid, wave, lane, ad);
+  stage_store<false>(tile[0], ksc[0], kr, sc, v, wave, lane);
+  v = resolve<false>(a, ad, bad);
+  stage_load<false>(a, v, lane, kr, sc);
+  __syncthreads();
   QState<NH, true> qs;
   qs.tok = -1;
   int buf = 0;
   const float one = a.one;
   while (cur.valid) {
-    stage_store<false>(tile[buf], ksc[buf], kr, sc, v, wave, lane);
-    v = resolve<false>(a, ad, bad);
-    stage_addr<false, false>(a, n2.grp, n2.c, n2.valid, wave, lane, ad);
-    stage_load<false>(a, v, lane, kr, sc);
-    __syncthreads();
+    stage_addr<false, false>(a, n2.grp, n2.c, n2.valid, wave, lane, ad);  // lookups of item i + 2
     const Group& gr = cur.grp;  // multi groups hold kGroupTokens tokens
     const int t = gr.t0 + wave;
     const int n_i = visible(a, static_cast<int64_t>(gr.p0) + wave, gr.L);
     if (t != qs.tok) load_q<NH, true>(a, t, lane, qs);
     const QRegs<NH, true> q{qs};
     const int8_t* tl = tile[buf];
+    // halfway: item i + 1 into the other buffer, loads of item i + 2
+    auto stage_next = [&]() {
+      stage_store<false>(tile[buf ^ 1], ksc[buf ^ 1], kr, sc, v, wave, lane);
+      v = resolve<false>(a, ad, bad);
+      stage_load<false>(a, v, lane, kr, sc);
+    };
     if (qs.scaled) {
       // the item's units, pipelined, with the scaled epilogue
       i32x16 accA[2], accB[2];
+      i32x4 bf[2][4];  // B fragments of the current sub-tile, shared by its passes
       float sum = 0.0f;
-      mfma_pass(q, tl, 0, 0, lane, seed, accA);
+      load_b(tl, 0, lane, bf);
+      mfma_pass_b(q, bf, 0, lane, seed, accA);
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         if (u + 1 < NU) {
-          if (u & 1) mfma_pass(q, tl, (u + 1) / P, (u + 1) % P, lane, seed, accA);
-          else mfma_pass(q, tl, (u + 1) / P, (u + 1) % P, lane, seed, accB);
+          if ((u + 1) % P == 0) load_b(tl, (u + 1) / P, lane, bf);
+          if (u & 1) mfma_pass_b(q, bf, (u + 1) % P, lane, seed, accA);
+          else mfma_pass_b(q, bf, (u + 1) % P, lane, seed, accB);
         }
+        if (u == MID) stage_next();
         if (DBG)
           dbg_store_qk<NH, MODE>(a, (u & 1) ? accB : accA, u % P, t, cur.c * kChunk + 64 * (u / P), n_i,
                                  ksc[buf], u / P, lane);
@@ -1191,6 +1249,7 @@ __device__ void run_multi(const KArgs& a, const ListView& L, Cursor cur, int hi,
       // wave scores one token)
 #pragma unroll 1
       for (int sub = 0; sub < 4; ++sub) {
+        if (sub == 2) stage_next();
         float sum = 0.0f;
 #pragma unroll
         for (int ps = 0; ps < P; ++ps) {  // unrolled: the multipliers stay in registers
@@ -1207,6 +1266,7 @@ __device__ void run_multi(const KArgs& a, const ListView& L, Cursor cur, int hi,
                                       : nullptr);
       }
     }
+    __syncthreads();
     cur = n1;
     n1 = n2;
     n2 = next_item(L, n2, hi);
