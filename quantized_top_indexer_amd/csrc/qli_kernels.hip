@@ -1107,9 +1107,12 @@ __device__ __forceinline__ void finish_subtile(const KArgs& a, const uint16_t* k
   kp[local] = key;
   if (MODE == QLI_MODE_SOURCE) {
     uint32_t bk = key;
-    bk = max(bk, static_cast<uint32_t>(__shfl_xor(static_cast<int>(bk), 1)));
-    bk = max(bk, static_cast<uint32_t>(__shfl_xor(static_cast<int>(bk), 2)));
-    bk = max(bk, static_cast<uint32_t>(__shfl_xor(static_cast<int>(bk), 4)));
+    // maximum over the 8 lanes of the block on DPP (no LDS round trips):
+    // pairs, quads, then the half-row mirror, which maps each quad of an
+    // 8-lane half-row onto the other
+    bk = max(bk, dpp_all<0xB1>(bk));   // quad_perm [1, 0, 3, 2]
+    bk = max(bk, dpp_all<0x4E>(bk));   // quad_perm [2, 3, 0, 1]
+    bk = max(bk, dpp_all<0x141>(bk));  // row_half_mirror
     bp[local >> 3] = bk;
   }
 }
