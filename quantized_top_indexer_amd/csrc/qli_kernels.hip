@@ -14,12 +14,12 @@
 //                  slot list + eligible count.
 //   score          persistent, two workgroups per CU.  Each workgroup walks a
 //                  contiguous range of work items (group, 256-slot chunk) with
-//                  a software pipeline: page lookup ahead, K + scale loads one
-//                  item ahead (registers), and for the current item an LDS
-//                  tile (shared by a group's 4 tokens, or each wave's own rows
-//                  for single tokens), INT8 MFMA (v_mfma_i32_32x32x32_i8,
-//                  queries x keys), the golden FP16/FP32 epilogue, block
-//                  maxima and order keys.
+//                  a software pipeline: page lookups and K + scale loads
+//                  ahead of use (registers; one to two items), and for the
+//                  current item an LDS tile (shared by a group's 4 tokens,
+//                  or each wave's own rows for single tokens), INT8 MFMA
+//                  (v_mfma_i32_32x32x32_i8, queries x keys), the golden
+//                  FP16/FP32 epilogue, block maxima and order keys.
 //   select         one workgroup per (token, positions|blocks): keys held in
 //                  registers, range-adaptive radix select (2048-bin digits),
 //                  then an ordered compaction that emits the winners already
