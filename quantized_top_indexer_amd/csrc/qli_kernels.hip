@@ -202,11 +202,16 @@ __device__ __forceinline__ uint32_t relu_h2(uint32_t v) {
   return r;
 }
 
-// Accumulator word holding the bits of 24576 + qk/512 (the MFMA accumulator
-// is seeded with the bits of 24576.0f, whose ulp is 2^-9, so the integer sum
-// of the seed and qk is exactly that float for |qk| < 2^22) -> fp16(qk/1024):
-// 0.5*F - 12288 is exact, and the conversion rounds it once (RNE).  Two
-// forms, same bits:
+// The MFMA accumulator is seeded with the bits of 4.0f (an inline constant
+// of the instruction, so the seed costs no registers), and the integer sum
+// of the seed and qk is then a float F that carries qk:
+//  - qk >= 0: F = 4 + qk * 2^-21 exactly (ulp of [4, 8) is 2^-21, and
+//    qk < 2^21 for any int8 operands: |q.k| <= 128 * 127 * 128);
+//  - qk < 0: the bits fall below those of 4.0, so F lies in [2, 4).
+// Only max(qk, 0) matters after the ReLU, and every negative qk gives F < 4.
+// fp16(qk/1024) for qk >= 0 is fp16(2048 * F - 8192) (the fma is exact and
+// the conversion rounds once, RNE); for qk < 0 that value is negative and
+// the ReLU makes it +0, the golden result.  Two forms, same bits:
 //  - qk_to_half: one fma written so that it becomes one v_fma_mixlo/hi_f16
 //    (fewest instructions and registers);
 //  - qk_over_1024 + a packed conversion of two values: an FP32 fma per
@@ -216,26 +221,26 @@ __device__ __forceinline__ uint32_t relu_h2(uint32_t v) {
 //    the mixed form; it emits no instruction.
 // No inline assembly touches MFMA results, so the compiler inserts the
 // MFMA-to-VALU wait states.
-constexpr int32_t kSeedBits = 0x46C00000;  // 24576.0f
+constexpr int32_t kSeedBits = 0x40800000;  // 4.0f
 __device__ __forceinline__ _Float16 qk_to_half(int32_t acc) {
-  return static_cast<_Float16>(__builtin_fmaf(__int_as_float(acc), 0.5f, -12288.0f));
+  return static_cast<_Float16>(__builtin_fmaf(__int_as_float(acc), 2048.0f, -8192.0f));
 }
 __device__ __forceinline__ float qk_over_1024(int32_t acc) {
-  float y = __builtin_fmaf(__int_as_float(acc), 0.5f, -12288.0f);
+  float y = __builtin_fmaf(__int_as_float(acc), 2048.0f, -8192.0f);
   asm volatile("" : "+v"(y));
   return y;
 }
 
-// Scaled form of the same step with the ReLU folded in: y = qk * 2^-21 =
-// 2^-12 * F - 6 (exact), clamped to [0, 1] by the fma's clamp bit, gives
-// max(qk, 0) * 2^-21, and fp16(y) = fp16(qk/1024) * 2^-11 exactly (for
-// qk < 128, y is an fp16 subnormal on the 2^-21 grid; above, scaling by a
-// power of two commutes with rounding), so fp16(fp16(y) * m * 2^11) equals
-// the golden fp16(relu(fp16(qk/1024)) * m) whenever m * 2^11 is still a
-// finite fp16 (|m| < 32).  One clamped fma per value instead of an fma
-// plus half a packed max.
+// Scaled form of the same step with the ReLU folded in: y = F - 4 is
+// qk * 2^-21 exactly for qk >= 0 and negative otherwise, so clamping it to
+// [0, 1] (the add's clamp bit, 4.0 an inline constant) gives
+// max(qk, 0) * 2^-21 in one instruction; fp16(y) = fp16(qk/1024) * 2^-11
+// exactly (for qk < 128, y is an fp16 subnormal on the 2^-21 grid; above,
+// scaling by a power of two commutes with rounding), so
+// fp16(fp16(y) * m * 2^11) equals the golden fp16(relu(fp16(qk/1024)) * m)
+// whenever m * 2^11 is still a finite fp16 (|m| < 32).
 __device__ __forceinline__ float qk_relu_scaled(int32_t acc) {
-  float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(__int_as_float(acc), 0x1p-12f, -6.0f), 0.0f, 1.0f);
+  float y = __builtin_amdgcn_fmed3f(__int_as_float(acc) - 4.0f, 0.0f, 1.0f);
   asm volatile("" : "+v"(y));
   return y;
 }

@@ -143,6 +143,34 @@ def test_head_multiplier_ranges(ratio, N, mode):
     check_invariants(pb, gpu)
 
 
+@pytest.mark.parametrize("ratio,N,mode", [(2, 64, 2), (1, 64, 1), (2, 32, 3)])
+def test_extreme_products(ratio, N, mode):
+    """The largest and smallest q.k that int8 operands allow: q = k = -128
+    everywhere gives +2^21, q = -128 against k = 127 gives -2080768, and
+    q = 127 against k = -128 the same negative value, on tokens and rows
+    mixed among ordinary ones.  The score kernels carry q.k in a seeded
+    FP32 accumulator, which must hold exactly over this whole range."""
+    pb = small_problem(340 + ratio + N + mode, ratio=ratio, N=N, mode=mode, topk=120, cb=64, cb_in=128,
+                       requests=((6, 2100), (5, 700), (1, 90)))
+    rng = np.random.default_rng(341)
+    T = pb.num_tokens
+    q = pb.q.copy()
+    q[0::3] = -128            # every head of every third token
+    q[1::3, : N // 2] = 127   # half the heads of the next ones
+    pb.q = q
+    P, R, _ = pb.k_pages.shape
+    k = pb.k_pages.reshape(P * R, 128).copy()
+    pick = rng.random(P * R)
+    k[pick < 0.3] = -128
+    k[(pick >= 0.3) & (pick < 0.5)] = 127
+    pb.k_pages = k.reshape(P, R, 128)
+    say(f"extreme products {pb.name}: T={T} L={pb.max_k_len}")
+    gpu = run_gpu(pb, debug=True)
+    orc = oracle_rows(pb, scores=True)
+    compare(pb, gpu, orc)
+    check_invariants(pb, gpu)
+
+
 def test_consumer_long_context_bound():
     """A context bound above 2^21 positions takes the sorting candidate
     preparation instead of the bitmap one: same outputs, same as the oracle."""
