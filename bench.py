@@ -206,6 +206,49 @@ def measure(pb, steps, warmup, copies=1, cand_sets=None, bound="hbm"):
             "keys_per_s": keys / (ms * 1e-3)}
 
 
+def source_candidates(pb):
+    """Candidate-block output of one GPU call of a source-mode problem
+    (numpy [T, 1, cb]): the incoming candidates of the consumer call that
+    follows it in the mixed batch."""
+    import torch
+    run = Runner(pb)
+    run.step(0)
+    torch.cuda.synchronize()
+    cand = run.cand_out.cpu().numpy()
+    del run
+    torch.cuda.empty_cache()
+    return cand
+
+
+def measure_mixed(steps, warmup):
+    """The mixed batch's four layer calls on one request set and block table
+    (ratio 1 source, its consumer, ratio 2 source, its consumer), each timed
+    on its own; every consumer is fed the candidates its source produced on
+    the GPU.  The roofline of a call is the one its arithmetic intensity
+    selects (INT8 ops per algorithmic byte against the ridge point)."""
+    import qli_workloads as W
+    ridge = INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    out, cand = {}, None
+    tot_keys, tot_ms = 0, 0.0
+    for pb in W.mixed_calls():
+        sets = [cand] if pb.mode == 3 else None
+        _, nbytes, ops = algorithmic(pb, cand if pb.mode == 3 else None)
+        bound = "mfma" if ops > ridge * nbytes else "hbm"
+        m = measure(pb, steps, warmup, cand_sets=sets, bound=bound)
+        out[pb.name] = {"tokens": pb.num_tokens, "mode": {2: "source", 3: "consumer"}[pb.mode],
+                        "ratio": pb.ratio, "topk": pb.topk,
+                        "cand_blocks": pb.cand_blocks or pb.cand_in_blocks,
+                        "keys": m["keys"], "keys_per_s": round(m["keys_per_s"], 1),
+                        "ms_per_call": round(m["ms_per_step"], 5), "kernels_ms": m["kernels_ms"],
+                        "roofline": m["roofline"]}
+        tot_keys += m["keys"]
+        tot_ms += m["ms_per_step"]
+        log(f"{pb.name}: {m['ms_per_step']:.4f} ms/call kernels {m['kernels_ms']}")
+        cand = source_candidates(pb) if pb.mode == 2 else None
+    return {"keys_per_s": round(tot_keys / (tot_ms * 1e-3), 1), "ms_per_four_calls": round(tot_ms, 5),
+            "calls": out}
+
+
 def measure_producers(steps, warmup, copies=2):
     """Query quantization and the index-K write at the shapes of the decode
     and prefill workloads: each launch timed with HIP events on its stream
@@ -387,8 +430,9 @@ def main():
     ap.add_argument("--workload", default="decode_source",
                     help="main workload (decode_source is the headline configuration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--others", default="prefill_chunk,decode_consumer_1m",
-                    help="comma list of secondary workloads ('' for none)")
+    ap.add_argument("--others", default="prefill_chunk,decode_consumer_1m,mixed",
+                    help="comma list of secondary workloads ('' for none; 'mixed' = the four "
+                         "layer calls of the mixed batch)")
     ap.add_argument("--no-producers", action="store_true",
                     help="skip the query-quantization and index-K write measurements")
     ap.add_argument("--no-ceilings", action="store_true",
@@ -447,6 +491,10 @@ def main():
     pb, main_m = run_workload(args.workload, args.steps, args.copies)
     others = {}
     for name in [s for s in args.others.split(",") if s and s != args.workload]:
+        if name == "mixed":
+            log("mixed: generating the four layer calls")
+            others["mixed"] = measure_mixed(max(10, args.steps // 5), args.warmup)
+            continue
         opb, m = run_workload(name, max(10, args.steps // 5) if name == "prefill_chunk"
                               else args.steps, args.copies)
         others[name] = {"keys_per_s": round(m["keys_per_s"], 1),
@@ -468,7 +516,9 @@ def main():
         log(f"ceilings: {ceilings}")
         with_measured(main_m["roofline"], ceilings)
         for v in list(others.values()) + list(producers.values()):
-            with_measured(v["roofline"], ceilings)
+            for r in ([c["roofline"] for c in v["calls"].values()] if "calls" in v
+                      else [v["roofline"]]):
+                with_measured(r, ceilings)
 
     cpu = None
     if not args.no_cpu_baseline and pb.mode != 3:
