@@ -445,7 +445,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the indexer has no multi-GPU path in this build "
+        print("bench.py measures one GPU: the indexer library has no multi-GPU path "
               "(requests or positions would shard with no exchange / one top-k merge; "
               "see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
