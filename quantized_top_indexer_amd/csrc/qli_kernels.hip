@@ -1891,8 +1891,16 @@ struct MapSlots {
   __device__ __forceinline__ int32_t operator()(int i) const { return slots[i >> 3] * 8 + (i & 7); }
 };
 
+// Minimum waves per SIMD asked of the compiler: the 512-thread variant
+// (rows of 4097..16384 keys, e.g. every prefill token) would take 123 VGPRs
+// and fit two workgroups per CU; at 80 VGPRs three fit, and the few
+// registers it spills cost less than the extra workgroup gains (prefill
+// chunk select 141 -> 110 us; four workgroups at 64 VGPRs spill too much:
+// 127 us).  The 1024-thread variant runs one workgroup per CU either way.
+__host__ __device__ constexpr int sel_min_waves(int bs) { return bs == 512 ? 6 : 1; }
+
 template <int BS, bool MULTI>
-__global__ __launch_bounds__(BS) void select_kernel(KArgs a) {
+__global__ __launch_bounds__(BS, sel_min_waves(BS)) void select_kernel(KArgs a) {
   __shared__ uint32_t sel_lds[sel_lds_words(BS)];
   const int t = blockIdx.x;
   // plain/source: every position below V and every block below ceil(V/8) is
