@@ -1440,6 +1440,10 @@ __host__ __device__ constexpr int sel_lds_words(int bs) {
 }
 
 __host__ __device__ constexpr int sel_chunk(int bs) { return bs == 256 ? 4096 : 32 * bs; }
+// A shorter chunk for 512 threads (20 keys per thread): rows of up to
+// 10240 keys (prefill tokens up to 10240 compressed positions) then fit 80
+// VGPRs without spilling, where 32 keys per thread spill 40 of them.
+constexpr int kSelShortChunk = 10240;
 
 struct MinOp {
   __device__ __forceinline__ uint32_t operator()(uint32_t x, uint32_t y) const { return min(x, y); }
@@ -1568,10 +1572,10 @@ __device__ __forceinline__ void refine_threshold(Each each, uint32_t lo, uint32_
 // them into a handful of bins.  A pass ends the search as soon as every key
 // of the boundary bin is needed.
 // MULTI = false: the caller guarantees n <= CHUNK (one chunk, loaded once).
-template <int BS, bool MULTI, class Map>
+template <int BS, bool MULTI, int CH, class Map>
 __device__ __forceinline__ void select_topk(const uint32_t* keys, int n, int cap, int k, int pin,
                                             int32_t* out, Map map, uint32_t* lds) {
-  constexpr int CHUNK = MULTI ? 16 * BS : sel_chunk(BS);  // fewer live keys when reloading
+  constexpr int CHUNK = MULTI ? 16 * BS : CH;  // fewer live keys when reloading
   constexpr int NW = BS / 64;
   constexpr int KPW = CHUNK / NW;        // keys per wave per chunk
   constexpr int VPT = CHUNK / (4 * BS);  // 16-byte vectors per thread per chunk
@@ -1891,15 +1895,16 @@ struct MapSlots {
   __device__ __forceinline__ int32_t operator()(int i) const { return slots[i >> 3] * 8 + (i & 7); }
 };
 
-// Minimum waves per SIMD asked of the compiler: the 512-thread variant
-// (rows of 4097..16384 keys, e.g. every prefill token) would take 123 VGPRs
-// and fit two workgroups per CU; at 80 VGPRs three fit, and the few
-// registers it spills cost less than the extra workgroup gains (prefill
-// chunk select 141 -> 110 us; four workgroups at 64 VGPRs spill too much:
-// 127 us).  The 1024-thread variant runs one workgroup per CU either way.
+// Minimum waves per SIMD asked of the compiler: the 512-thread variants
+// (rows of 4097..16384 keys, e.g. every prefill token) would take up to 123
+// VGPRs and fit two workgroups per CU; at 80 VGPRs three fit.  With 32 keys
+// per thread the few registers spilled cost less than the extra workgroup
+// gains (prefill chunk select 141 -> 110 us; four workgroups at 64 VGPRs
+// spill too much: 127 us); with 20 keys per thread nothing spills.  The
+// 1024-thread variant runs one workgroup per CU either way.
 __host__ __device__ constexpr int sel_min_waves(int bs) { return bs == 512 ? 6 : 1; }
 
-template <int BS, bool MULTI>
+template <int BS, bool MULTI, int CH = sel_chunk(BS)>
 __global__ __launch_bounds__(BS, sel_min_waves(BS)) void select_kernel(KArgs a) {
   __shared__ uint32_t sel_lds[sel_lds_words(BS)];
   const int t = blockIdx.x;
@@ -1914,20 +1919,20 @@ __global__ __launch_bounds__(BS, sel_min_waves(BS)) void select_kernel(KArgs a) 
     const uint32_t* keys = a.keys + static_cast<int64_t>(t) * a.ncap;
     const int cap = static_cast<int>(a.ncap);
     if (a.mode == QLI_MODE_CONSUMER) {
-      select_topk<BS, MULTI>(keys, a.ncount[t], cap, a.topk, -1, out,
+      select_topk<BS, MULTI, CH>(keys, a.ncount[t], cap, a.topk, -1, out,
                       MapSlots{a.slots + static_cast<int64_t>(t) * a.cb_in}, sel_lds);
     } else {
       const int32_t tv = a.tokv[t];
       const int V = tv & ~kTokBad;
       if (!(tv & kTokBad) && V <= a.topk) all_of(out, V, a.topk);
-      else select_topk<BS, MULTI>(keys, V, cap, a.topk, -1, out, MapIdentity{}, sel_lds);
+      else select_topk<BS, MULTI, CH>(keys, V, cap, a.topk, -1, out, MapIdentity{}, sel_lds);
     }
   } else {
     const int32_t tv = a.tokv[t];
     const int nb = ((tv & ~kTokBad) + 7) / 8;
     int32_t* out = a.cand_out + static_cast<int64_t>(t) * a.cb;
     if (!(tv & kTokBad) && nb <= a.cb) all_of(out, nb, a.cb);
-    else select_topk<BS, MULTI>(a.bkeys + static_cast<int64_t>(t) * a.nbcap, nb, static_cast<int>(a.nbcap), a.cb,
+    else select_topk<BS, MULTI, CH>(a.bkeys + static_cast<int64_t>(t) * a.nbcap, nb, static_cast<int>(a.nbcap), a.cb,
                            nb - 1, out, MapIdentity{}, sel_lds);
   }
 }
@@ -2110,6 +2115,7 @@ int launch(const qli_params* p, const WsLayout& w, void* stream) {
     // rows no longer than a chunk (every n <= its row capacity) take the
     // single-chunk variants
     if (longest <= sel_chunk(256)) select_kernel<256, false><<<grid, 256, 0, st>>>(a);
+    else if (longest <= kSelShortChunk) select_kernel<512, false, kSelShortChunk><<<grid, 512, 0, st>>>(a);
     else if (longest <= sel_chunk(512)) select_kernel<512, false><<<grid, 512, 0, st>>>(a);
     else if (longest <= sel_chunk(1024)) select_kernel<1024, false><<<grid, 1024, 0, st>>>(a);
     else select_kernel<1024, true><<<grid, 1024, 0, st>>>(a);

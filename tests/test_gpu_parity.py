@@ -20,6 +20,10 @@ MEDIUM = [
     (1, 64, 3, 64, 64, ((3, 3333), (2, 700))),
     (2, 32, 3, 500, 128, ((4, 5000), (1, 20))),
     (1, 32, 2, 2048, 2048, ((2, 2600),)),
+    # rows of 4097..10240 and 10241..16384 keys: the two 512-thread
+    # selections (20 and 32 keys per thread)
+    (1, 32, 2, 2048, 512, ((3, 9000), (1, 5000))),
+    (1, 64, 1, 1500, 64, ((2, 12000), (1, 10300))),
 ]
 
 
