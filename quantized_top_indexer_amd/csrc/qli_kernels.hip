@@ -2116,7 +2116,16 @@ int launch(const qli_params* p, const WsLayout& w, void* stream) {
     // single-chunk variants
     if (longest <= sel_chunk(256)) select_kernel<256, false><<<grid, 256, 0, st>>>(a);
     else if (longest <= kSelShortChunk) select_kernel<512, false, kSelShortChunk><<<grid, 512, 0, st>>>(a);
-    else if (longest <= sel_chunk(512)) select_kernel<512, false><<<grid, 512, 0, st>>>(a);
+    else if (longest <= sel_chunk(512)) {
+      // rows of 10241..16384 keys: when they leave CUs idle (decode-sized
+      // batches), 1024 threads with 16 keys each finish a row sooner (76
+      // VGPRs, nothing spilled: consumer rows of 16384 keys 14.4 -> 13.4 us);
+      // otherwise three 512-thread workgroups share a CU
+      if (static_cast<int64_t>(grid.x) * grid.y <= cu_count())
+        select_kernel<1024, false, 16384><<<grid, 1024, 0, st>>>(a);
+      else
+        select_kernel<512, false><<<grid, 512, 0, st>>>(a);
+    }
     else if (longest <= sel_chunk(1024)) select_kernel<1024, false><<<grid, 1024, 0, st>>>(a);
     else select_kernel<1024, true><<<grid, 1024, 0, st>>>(a);
   }
