@@ -1440,9 +1440,9 @@ __host__ __device__ constexpr int sel_lds_words(int bs) {
 }
 
 __host__ __device__ constexpr int sel_chunk(int bs) { return bs == 256 ? 4096 : 32 * bs; }
-// A shorter chunk for 512 threads (20 keys per thread): rows of up to
-// 10240 keys (prefill tokens up to 10240 compressed positions) then fit 80
-// VGPRs without spilling, where 32 keys per thread spill 40 of them.
+// A shorter chunk for 512 threads (20 keys per thread) for rows of up to
+// 10240 keys (prefill tokens up to 10240 compressed positions): fewer live
+// registers, so that more workgroups share a CU (sel_min_waves).
 constexpr int kSelShortChunk = 10240;
 
 struct MinOp {
@@ -1897,15 +1897,19 @@ struct MapSlots {
 
 // Minimum waves per SIMD asked of the compiler: the 512-thread variants
 // (rows of 4097..16384 keys, e.g. every prefill token) would take up to 123
-// VGPRs and fit two workgroups per CU; at 80 VGPRs three fit.  With 32 keys
-// per thread the few registers spilled cost less than the extra workgroup
-// gains (prefill chunk select 141 -> 110 us; four workgroups at 64 VGPRs
-// spill too much: 127 us); with 20 keys per thread nothing spills.  The
-// 1024-thread variant runs one workgroup per CU either way.
-__host__ __device__ constexpr int sel_min_waves(int bs) { return bs == 512 ? 6 : 1; }
+// VGPRs and fit two workgroups per CU.  With 32 keys per thread, 80 VGPRs
+// (three workgroups per CU) spill a few registers, which costs less than
+// the extra workgroup gains (prefill chunk select 141 -> 110 us), while 64
+// VGPRs spill too much (127 us).  With 20 keys per thread, 80 VGPRs spill
+// nothing (110 -> 100 us) and 64 VGPRs (four workgroups per CU, 134 KB of
+// LDS) spill 12 and are faster still (99 -> 88 us).  The 1024-thread
+// variants run one workgroup per CU either way.
+__host__ __device__ constexpr int sel_min_waves(int bs, int ch) {
+  return bs == 512 ? (ch == kSelShortChunk ? 8 : 6) : 1;
+}
 
 template <int BS, bool MULTI, int CH = sel_chunk(BS)>
-__global__ __launch_bounds__(BS, sel_min_waves(BS)) void select_kernel(KArgs a) {
+__global__ __launch_bounds__(BS, sel_min_waves(BS, CH)) void select_kernel(KArgs a) {
   __shared__ uint32_t sel_lds[sel_lds_words(BS)];
   const int t = blockIdx.x;
   // plain/source: every position below V and every block below ceil(V/8) is
