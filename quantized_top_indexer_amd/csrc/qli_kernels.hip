@@ -83,6 +83,7 @@ struct KArgs {
   float one;  // 1.0f
   int mode, ratio, rshift, B, T, topk, cb, cb_in, R, rlog, bt_stride, num_pages, max_k_len;
   int score_grid;
+  int sel_lo, sel_hi;  // this select launch takes the rows whose length n has sel_lo <= n <= sel_hi
   int64_t kstride, sstride, ncap, nbcap;
   const int8_t* q;
   const uint16_t* qs;
@@ -1918,22 +1919,28 @@ __global__ __launch_bounds__(BS, sel_min_waves(BS, CH)) void select_kernel(KArgs
   auto all_of = [](int32_t* out, int n, int k) {
     for (int i = threadIdx.x; i < k; i += BS) out[i] = i < n ? i : -1;
   };
+  // the row's length decides whether this launch takes it (wave-uniform)
+  auto mine = [&](int n) { return n >= a.sel_lo && n <= a.sel_hi; };
   if (blockIdx.y == 0) {
     int32_t* out = a.topk_out + static_cast<int64_t>(t) * a.topk;
     const uint32_t* keys = a.keys + static_cast<int64_t>(t) * a.ncap;
     const int cap = static_cast<int>(a.ncap);
     if (a.mode == QLI_MODE_CONSUMER) {
-      select_topk<BS, MULTI, CH>(keys, a.ncount[t], cap, a.topk, -1, out,
+      const int n = a.ncount[t];
+      if (!mine(n)) return;
+      select_topk<BS, MULTI, CH>(keys, n, cap, a.topk, -1, out,
                       MapSlots{a.slots + static_cast<int64_t>(t) * a.cb_in}, sel_lds);
     } else {
       const int32_t tv = a.tokv[t];
       const int V = tv & ~kTokBad;
+      if (!mine(V)) return;
       if (!(tv & kTokBad) && V <= a.topk) all_of(out, V, a.topk);
       else select_topk<BS, MULTI, CH>(keys, V, cap, a.topk, -1, out, MapIdentity{}, sel_lds);
     }
   } else {
     const int32_t tv = a.tokv[t];
     const int nb = ((tv & ~kTokBad) + 7) / 8;
+    if (!mine(nb)) return;
     int32_t* out = a.cand_out + static_cast<int64_t>(t) * a.cb;
     if (!(tv & kTokBad) && nb <= a.cb) all_of(out, nb, a.cb);
     else select_topk<BS, MULTI, CH>(a.bkeys + static_cast<int64_t>(t) * a.nbcap, nb, static_cast<int>(a.nbcap), a.cb,
@@ -2118,7 +2125,25 @@ int launch(const qli_params* p, const WsLayout& w, void* stream) {
     const dim3 grid(T, source ? 2 : 1);
     // rows no longer than a chunk (every n <= its row capacity) take the
     // single-chunk variants
-    if (longest <= sel_chunk(256)) select_kernel<256, false><<<grid, 256, 0, st>>>(a);
+    const int64_t rows = static_cast<int64_t>(grid.x) * grid.y;
+    a.sel_lo = 0;
+    a.sel_hi = INT32_MAX;
+    if (rows > 4 * static_cast<int64_t>(cu_count()) && longest > kSelShortChunk) {
+      // many rows whose lengths may differ widely (mixed batches): one
+      // launch per length class, each taking only its rows, so that short
+      // rows run at the occupancy of the narrow variants instead of all at
+      // that of the longest row's variant
+      const int bounds[4] = {kSelShortChunk, sel_chunk(512), sel_chunk(1024), INT32_MAX};
+      for (int c = 0; c < 4; ++c) {
+        a.sel_lo = c == 0 ? 0 : bounds[c - 1] + 1;
+        a.sel_hi = bounds[c];
+        if (a.sel_lo > longest) break;
+        if (c == 0) select_kernel<512, false, kSelShortChunk><<<grid, 512, 0, st>>>(a);
+        else if (c == 1) select_kernel<512, false><<<grid, 512, 0, st>>>(a);
+        else if (c == 2) select_kernel<1024, false><<<grid, 1024, 0, st>>>(a);
+        else select_kernel<1024, true><<<grid, 1024, 0, st>>>(a);
+      }
+    } else if (longest <= sel_chunk(256)) select_kernel<256, false><<<grid, 256, 0, st>>>(a);
     else if (longest <= kSelShortChunk) select_kernel<512, false, kSelShortChunk><<<grid, 512, 0, st>>>(a);
     else if (longest <= sel_chunk(512)) {
       // rows of 10241..16384 keys: when they leave CUs idle (decode-sized
