@@ -24,6 +24,9 @@ MEDIUM = [
     # selections (20 and 32 keys per thread)
     (1, 32, 2, 2048, 512, ((3, 9000), (1, 5000))),
     (1, 64, 1, 1500, 64, ((2, 12000), (1, 10300))),
+    # 32 heads: several groups of four tokens per request, plus leftover tokens
+    (2, 32, 2, 300, 128, ((19, 4000), (8, 900), (3, 300))),
+    (1, 32, 1, 1000, 64, ((16, 2600), (11, 1300), (1, 40))),
 ]
 
 
