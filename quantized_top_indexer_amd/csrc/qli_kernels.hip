@@ -316,15 +316,18 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total, uint32_t* 
 // ---------------------------------------------------------------------------
 // consumer_prep: sorted unique visible incoming block ids per token
 // ---------------------------------------------------------------------------
-constexpr int kPrepThreads = 1024;
+constexpr int kPrepThreads = 1024;      // preparation with the plan in block 0 (sorting: two ids per thread)
+constexpr int kPrepBitmapThreads = 256; // lean bitmap preparation (up to 8 ids and 32 bitmap words per thread)
 constexpr int kPrepBitmapWords = 8192;  // bitmap of up to 2^18 block ids (32 KB of LDS)
+constexpr int kPrepLeanMinTokens = 1024;  // consumer batches this large plan in a launch of their own
 
 // The request holding token t, found by all threads at once (one round of
 // loads instead of a dependent binary search); every thread gets it.
+template <int PT>
 __device__ __forceinline__ int prep_request(const KArgs& a, int t, int* s_req) {
   if (threadIdx.x == 0) *s_req = 0;
   __syncthreads();
-  for (int i = threadIdx.x; i < a.B; i += kPrepThreads)
+  for (int i = threadIdx.x; i < a.B; i += PT)
     if (a.qsl[i] <= t && t < a.qsl[i + 1]) *s_req = i;
   __syncthreads();
   return *s_req;
@@ -332,12 +335,13 @@ __device__ __forceinline__ int prep_request(const KArgs& a, int t, int* s_req) {
 
 // Slot table of token t from its kept block ids in ascending order (sl[0 ..
 // total), in LDS): slots, page rows and the eligible count.
+template <int PT>
 __device__ __forceinline__ void prep_write(const KArgs& a, int t, int b, int V, const int32_t* sl,
                                            int total) {
   int32_t* slots = a.slots + static_cast<int64_t>(t) * a.cb_in;
   int32_t* srow = a.srow + static_cast<int64_t>(t) * a.cb_in;
   bool bad = false;
-  for (int i = threadIdx.x; i < total; i += kPrepThreads) {
+  for (int i = threadIdx.x; i < total; i += PT) {
     const int blk = sl[i];
     const int pos0 = blk * 8;
     const int page = page_checked(a, b, pos0 >> a.rlog);
@@ -369,38 +373,33 @@ constexpr int kConsumerLdsWords = kPrepLdsWords > kPlanLdsWords ? kPrepLdsWords 
 // Sorted unique visible incoming block ids per token, through a bitmap of
 // the visible block ids: duplicates merge, and a prefix count of set bits
 // places every id (contexts of up to 2^18 blocks).
-__global__ __launch_bounds__(kPrepThreads) void consumer_prep_kernel(KArgs a) {
-  __shared__ uint32_t lds[kConsumerLdsWords];
-  if (blockIdx.x == 0) {
-    plan_role<kPrepThreads>(a, lds);
-    return;
-  }
-  uint32_t* bm = lds;
-  int32_t* sl = reinterpret_cast<int32_t*>(lds + kPrepBitmapWords);
-  uint32_t* sh = lds + kPrepBitmapWords + QLI_MAX_CAND_BLOCKS;
-  int* s_req = reinterpret_cast<int*>(sh + 64);
-  const int t = blockIdx.x - 1;
+// Preparation of token t through the bitmap: bm (one bit per visible
+// block), sl (the kept ids, at most cb_in), sh (64 words of scan scratch)
+// and s_req (one word) are LDS.
+template <int PT>
+__device__ __forceinline__ void prep_bitmap_token(const KArgs& a, int t, uint32_t* bm, int32_t* sl,
+                                                  uint32_t* sh, int* s_req) {
   const int tid = threadIdx.x;
-  const int b = prep_request(a, t, s_req);
+  const int b = prep_request<PT>(a, t, s_req);
   const ReqView r = request_view(a, global_meta(a), b, tid == 0);
   const int V = (t >= r.q0 && t < r.q1)
                     ? visible(a, r.S - (r.q1 - r.q0) + (t - r.q0), r.L) : 0;
   const int nblocks = (V + 7) / 8;
-  const int nwords = (nblocks + 31) / 32;  // <= kPrepBitmapWords (checked at launch)
-  for (int i = tid; i < nwords; i += kPrepThreads) bm[i] = 0;
+  const int nwords = (nblocks + 31) / 32;  // within the bitmap: V <= max_k_len (checked at launch)
+  for (int i = tid; i < nwords; i += PT) bm[i] = 0;
   __syncthreads();
   const int32_t* cin = a.cand_in + static_cast<int64_t>(t) * a.cb_in;
-  for (int i = tid; i < a.cb_in; i += kPrepThreads) {
+  for (int i = tid; i < a.cb_in; i += PT) {
     const int c = cin[i];
     if (c >= 0 && c < nblocks) atomicOr(&bm[c >> 5], 1u << (c & 31));
   }
   __syncthreads();
-  const int wpt = (nwords + kPrepThreads - 1) / kPrepThreads;
+  const int wpt = (nwords + PT - 1) / PT;
   const int w0 = min(nwords, tid * wpt), w1 = min(nwords, w0 + wpt);
   uint32_t cnt = 0;
   for (int w = w0; w < w1; ++w) cnt += __popc(bm[w]);
   uint32_t total;
-  uint32_t at = block_exclusive_scan<kPrepThreads>(cnt, &total, sh);
+  uint32_t at = block_exclusive_scan<PT>(cnt, &total, sh);
   for (int w = w0; w < w1; ++w) {
     uint32_t bits = bm[w];
     while (bits) {
@@ -410,7 +409,30 @@ __global__ __launch_bounds__(kPrepThreads) void consumer_prep_kernel(KArgs a) {
     }
   }
   __syncthreads();
-  prep_write(a, t, b, V, sl, static_cast<int>(total));
+  prep_write<PT>(a, t, b, V, sl, static_cast<int>(total));
+}
+
+__global__ __launch_bounds__(kPrepThreads) void consumer_prep_kernel(KArgs a) {
+  constexpr int PT = kPrepThreads;
+  __shared__ uint32_t lds[kConsumerLdsWords];
+  if (blockIdx.x == 0) {
+    plan_role<PT>(a, lds);
+    return;
+  }
+  uint32_t* sh = lds + kPrepBitmapWords + QLI_MAX_CAND_BLOCKS;
+  prep_bitmap_token<PT>(a, blockIdx.x - 1, lds, reinterpret_cast<int32_t*>(lds + kPrepBitmapWords), sh,
+                        reinterpret_cast<int*>(sh + 64));
+}
+
+// Large batches: the plan runs as a launch of its own and every workgroup
+// prepares one token in LDS sized for this call (nwcap bitmap words for the
+// longest context, cb_in kept ids), so that several workgroups share a CU
+// (the plan's metadata staging would otherwise size every workgroup's LDS).
+__global__ __launch_bounds__(kPrepBitmapThreads) void consumer_prep_lean_kernel(KArgs a, int nwcap) {
+  extern __shared__ uint32_t dlds[];
+  uint32_t* sh = dlds + nwcap + a.cb_in;
+  prep_bitmap_token<kPrepBitmapThreads>(a, blockIdx.x, dlds, reinterpret_cast<int32_t*>(dlds + nwcap), sh,
+                                        reinterpret_cast<int*>(sh + 64));
 }
 
 // The same by a bitonic sort of the incoming ids (any context length).
@@ -426,7 +448,7 @@ __global__ __launch_bounds__(kPrepThreads) void consumer_prep_sort_kernel(KArgs 
   int* s_req = reinterpret_cast<int*>(sh + 64);
   const int t = blockIdx.x - 1;
   const int tid = threadIdx.x;
-  const int b = prep_request(a, t, s_req);
+  const int b = prep_request<kPrepThreads>(a, t, s_req);
   const ReqView r = request_view(a, global_meta(a), b, tid == 0);
   const int V = (t >= r.q0 && t < r.q1)
                     ? visible(a, r.S - (r.q1 - r.q0) + (t - r.q0), r.L) : 0;
@@ -471,7 +493,7 @@ __global__ __launch_bounds__(kPrepThreads) void consumer_prep_sort_kernel(KArgs 
   for (int e = 0; e < 2; ++e)
     if (f[e]) sl[at++] = v[i0 + e];
   __syncthreads();
-  prep_write(a, t, b, V, sl, static_cast<int>(total));
+  prep_write<kPrepThreads>(a, t, b, V, sl, static_cast<int>(total));
 }
 
 // ---------------------------------------------------------------------------
@@ -2114,11 +2136,22 @@ int launch(const qli_params* p, const WsLayout& w, void* stream) {
   a.tokv = reinterpret_cast<int32_t*>(ws + w.tokv_off);
 
   const unsigned T = static_cast<unsigned>(p->num_tokens);
-  if (consumer) {
+  const int64_t max_blocks = (static_cast<int64_t>(p->max_k_len) + 7) / 8;
+  const bool bitmap = max_blocks <= 32 * static_cast<int64_t>(kPrepBitmapWords);
+  if (consumer && bitmap && T >= static_cast<unsigned>(kPrepLeanMinTokens)) {
+    // the plan, then one lean workgroup per token
+    {
+      Stamp s(QLI_KERNEL_PLAN, st);
+      plan_kernel<kPlanThreads><<<1, kPlanThreads, 0, st>>>(a);
+    }
+    Stamp s(QLI_KERNEL_CONSUMER_PREP, st);
+    const int nwcap = static_cast<int>((max_blocks + 31) / 32);
+    const size_t lds = (static_cast<size_t>(nwcap) + static_cast<size_t>(p->cand_in_blocks) + 65) * 4;
+    consumer_prep_lean_kernel<<<T, kPrepBitmapThreads, lds, st>>>(a, nwcap);
+  } else if (consumer) {
     // block 0 plans, blocks 1..T prepare the tokens
     Stamp s(QLI_KERNEL_CONSUMER_PREP, st);
-    const int64_t max_blocks = (static_cast<int64_t>(p->max_k_len) + 7) / 8;
-    if (max_blocks <= 32 * static_cast<int64_t>(kPrepBitmapWords))
+    if (bitmap)
       consumer_prep_kernel<<<T + 1, kPrepThreads, 0, st>>>(a);
     else
       consumer_prep_sort_kernel<<<T + 1, kPrepThreads, 0, st>>>(a);
