@@ -1,13 +1,15 @@
 // HIP kernels of the quantized lightning indexer for CDNA4 (gfx950).
 //
-// One call = three launches (DeepSeek V4.1 QLI developer guide, "数据流"
-// and "当前 A3 契约"):
+// One call = three launches in the usual case (DeepSeek V4.1 QLI developer
+// guide, "数据流" and "当前 A3 契约"):
 //   plan           one workgroup (one wave for decode-sized batches): cut the
 //                  batch into groups (up to 4 consecutive query tokens of one
 //                  request in plain/source mode, one token in consumer mode)
 //                  and prefix-sum their 256-slot work units, so that a
 //                  persistent kernel can split any mix of decode tokens and
 //                  prefill chunks evenly.  In consumer mode it is block 0 of
+//                  the preparation launch (batches of 1024 tokens and more:
+//                  a launch of its own before it).
 //   consumer_prep  (consumer mode) one workgroup per token: de-duplicate the
 //                  incoming candidate block ids, drop ids without a visible
 //                  position, resolve each kept block to its page row -> dense
@@ -23,7 +25,9 @@
 //   select         one workgroup per (token, positions|blocks): keys held in
 //                  registers, range-adaptive radix select (2048-bin digits),
 //                  then an ordered compaction that emits the winners already
-//                  in ascending order, -1 tail.
+//                  in ascending order, -1 tail.  The workgroup size follows
+//                  the row length; batches of many rows of mixed lengths run
+//                  one launch per length class.
 //
 // Exactness: the epilogue applies one IEEE round-to-nearest-even per golden
 // step and sums heads in ascending order from +0.0f in a single lane, so the
