@@ -356,21 +356,23 @@ def test_zero_tokens():
     assert idx.shape == (0, 1, 8) and cand.shape == (0, 1, 64)
 
 
-@pytest.mark.parametrize("mode", [2, 3])
-def test_select_length_classes(mode):
+@pytest.mark.parametrize("mode,policy", [(2, None), (3, "random"), (3, "messy")])
+def test_select_length_classes(mode, policy):
     """More than four rows per CU and rows of widely different lengths: the
     selection runs one launch per row-length class, each taking its own
     rows.  Source: position rows in every class (up to 10240, up to 16384,
     up to 32768, longer) and short block rows; consumer: rows up to 10240
-    and up to 16384 eligible slots.  The first and last token of every
-    request and a random sample against the oracle; invariants on every
-    token."""
+    and up to 16384 eligible slots, prepared by the lean per-token launch
+    that batches of 1024 tokens and more take (messy: duplicated, negative
+    and invisible incoming ids).  The first and last token of every request
+    and a random sample against the oracle; invariants on every token."""
     if mode == 2:
         req = ((520, 12000), (3, 40000), (2, 20000), (3, 3000), (1, 9))
         pb = small_problem(350, ratio=1, N=32, mode=2, topk=700, cb=256, requests=req)
     else:
         req = ((1030, 40000), (20, 6000), (1, 1))
-        pb = small_problem(351, ratio=2, N=32, mode=3, topk=900, cb_in=2048, requests=req)
+        pb = small_problem(351 if policy == "random" else 352, ratio=2, N=32, mode=3, topk=900,
+                           cb_in=2048, requests=req, cand_policy=policy)
     starts = np.concatenate([[0], np.cumsum([r[0] for r in req])])
     include = np.concatenate([starts[:-1], starts[1:] - 1])
     say(f"length classes {pb.name}: T={pb.num_tokens} L={pb.max_k_len}")
