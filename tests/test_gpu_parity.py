@@ -196,6 +196,26 @@ def test_consumer_long_context_bound():
     compare(pb, big, oracle_rows(pb, scores=True))
 
 
+def test_large_consumer_batch_sorting_preparation():
+    """A consumer batch of more than 1024 tokens whose context bound exceeds
+    2^21 positions takes the sorting preparation (the plan in its block 0)
+    instead of the lean bitmap launch: the same indices as with the tight
+    bound, which test_select_length_classes checks against the oracle."""
+    req = ((1030, 40000), (20, 6000), (1, 1))
+    pb = small_problem(352, ratio=2, N=32, mode=3, topk=900, cb_in=2048, requests=req,
+                       cand_policy="messy")
+    say(f"large consumer batch: T={pb.num_tokens} L={pb.max_k_len}")
+    base = run_gpu(pb)
+    bound = (1 << 21) + 8
+    R = pb.k_pages.shape[1]
+    bt = np.zeros((pb.block_table.shape[0], -(-bound // R)), np.int32)
+    bt[:, :pb.block_table.shape[1]] = pb.block_table
+    pb.block_table = bt
+    big = run_gpu(pb, max_k_len=bound)
+    assert np.array_equal(base["topk"], big["topk"])
+    check_invariants(pb, big)
+
+
 def test_layout_invariance():
     """A larger page stride with K and scales moved inside the page gives
     identical outputs (the kernels only follow the strides)."""
