@@ -1419,7 +1419,7 @@ __device__ void run_single(const KArgs& a, const ListView& L, Cursor cu, int hi,
 // several query tokens read them with ordinary loads instead: each token
 // reads its own candidate rows, so the rows of a request are read again and
 // again and the caches serve the repeats (mixed batch consumer score
-// kernels 2.96 -> 1.77 ms and 2.42 -> 1.50 ms on one box).
+// kernels 2.96 -> 1.77 ms and 2.42 -> 1.50 ms in one A/B measurement).
 template <int NH, int MODE, bool DBG, bool STREAM = true>
 __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(KArgs a) {
   __shared__ __attribute__((aligned(16))) int8_t tile[2][kChunk * 128];
