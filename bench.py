@@ -32,6 +32,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, published (5.0 POP/s)
 KEY_BYTES = 130                # one 128-byte index-K row + its 2-byte FP16 scale
+# what roofline.achieved divides by (roofline.kernel_ms)
+DURATION_SOURCE = ("average duration per launch of roofline.kernel, from HIP events the library "
+                   "records around each launch on the launch stream, over `steps` calls run after "
+                   "the timed region (same process, same inputs)")
 
 
 def log(msg):
@@ -191,14 +195,15 @@ def measure(pb, steps, warmup, copies=1, cand_sets=None, bound="hbm"):
         roof = {"bound": "hbm", "kernel": kern, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "traffic_summary": summary, "alg_bytes_per_launch": nbytes,
-                "kernel_ms": round(kms[kern], 5)}
+                "kernel_ms": round(kms[kern], 5), "duration_source": DURATION_SOURCE}
     else:
         achieved = ops / kt / 1e12
         roof = {"bound": "mfma", "kernel": kern, "achieved": round(achieved, 1),
                 "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
                 "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic,
                 "traffic_summary": summary,
-                "alg_ops_per_launch": ops, "kernel_ms": round(kms[kern], 5)}
+                "alg_ops_per_launch": ops, "kernel_ms": round(kms[kern], 5),
+                "duration_source": DURATION_SOURCE}
     del run
     import torch
     torch.cuda.empty_cache()
@@ -395,28 +400,65 @@ def _producer_line(name, kernel, kms, nbytes, rows, config):
                          "traffic_summary": summary, "alg_bytes_per_launch": nbytes}}
 
 
-def cpu_baseline(pb, budget_tokens=None):
-    """The oracle as it stands, on the host cores, on a bounded sample of the
-    workload's tokens."""
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def host_threads():
+    """Threads the all-core oracle run uses: the CPUs this process may run
+    on, capped by OMP_NUM_THREADS when that is set (the host's CPU share of
+    one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def cpu_baseline(pb, single_tokens=16):
+    """The oracle as it stands, timed on the host: once on one thread over
+    the first ``single_tokens`` query tokens, once on every thread of the
+    host's share over all of the workload's tokens (threads take tokens)."""
     import numpy as np
 
     import oracle
-    nthreads = max(1, min(16, os.cpu_count() or 1))
-    toks = np.arange(pb.num_tokens if budget_tokens is None else min(budget_tokens,
-                                                                     pb.num_tokens))
-    o = oracle.OracleProblem(pb)
-    t0 = time.perf_counter()
-    o.run(tokens=toks, nthreads=nthreads)
-    dt = time.perf_counter() - t0
+    assert pb.mode != 3, "the CPU baseline runs on a source or plain workload"
     vis = []
     for b in range(pb.batch):
         n = int(pb.query_start_loc[b + 1] - pb.query_start_loc[b])
         vis += [(int(pb.raw_lens[b]) - n + i + 1) // pb.ratio for i in range(n)]
-    assert pb.mode != 3, "the CPU baseline runs on a source or plain workload"
-    keys = int(sum(vis[int(t)] for t in toks))
-    return {"value": round(keys / dt, 1), "unit": "keys/s", "cores": nthreads, "kind": "oracle",
-            "sample": f"{len(toks)} of {pb.num_tokens} query tokens of {pb.name} "
-                      f"({keys} keys, {dt:.2f} s wall on {nthreads} threads)"}
+    o = oracle.OracleProblem(pb)
+
+    def timed(toks, nthreads):
+        t0 = time.perf_counter()
+        o.run(tokens=toks, nthreads=nthreads)
+        dt = time.perf_counter() - t0
+        keys = int(sum(vis[int(t)] for t in toks))
+        return keys, dt
+
+    one = np.arange(min(single_tokens, pb.num_tokens))
+    k1, d1 = timed(one, 1)
+    nthreads = host_threads()
+    allt = np.arange(pb.num_tokens)
+    kn, dn = timed(allt, nthreads)
+    return {"value": round(kn / dn, 1), "unit": "keys/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"all {len(allt)} query tokens of {pb.name} ({kn} keys, {dn:.2f} s wall "
+                      f"on {nthreads} threads, one token per thread at a time)",
+            "single_thread": {"value": round(k1 / d1, 1), "unit": "keys/s", "cores": 1,
+                              "sample": f"first {len(one)} of {pb.num_tokens} query tokens "
+                                        f"({k1} keys, {d1:.2f} s wall)"},
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def main():
@@ -471,6 +513,23 @@ def main():
 
     def run_workload(name, steps, copies):
         log(f"{name}: generating")
+        if name.startswith("mixed_r"):
+            # one of the mixed batch's four layer calls on its own (for
+            # profiling); a consumer is fed its source's GPU candidates
+            calls = {c.name: c for c in W.mixed_calls()}
+            wpb = calls[name]
+            _, nbytes, ops = algorithmic(wpb, None) if wpb.mode == 2 else (None, None, None)
+            sets = None
+            if wpb.mode == 3:
+                src = calls[name.replace("consumer", "source")]
+                sets = [source_candidates(src)]
+                wpb.cand_in_blocks = src.cand_blocks
+                _, nbytes, ops = algorithmic(wpb, sets[0])
+            ridge = INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+            m = measure(wpb, steps, args.warmup, cand_sets=sets,
+                        bound="mfma" if ops > ridge * nbytes else "hbm")
+            log(f"{name}: {m['ms_per_step']:.4f} ms/call kernels {m['kernels_ms']}")
+            return wpb, m
         wpb = W.WORKLOADS[name]()
         if name == "decode_consumer_1m":
             import numpy as np

@@ -45,7 +45,9 @@
  * Memory: every pointer in qli_params is DEVICE memory owned by the caller
  * (typically torch tensors); the library allocates nothing.  Integer
  * metadata is read on the device only, so a call never synchronises with
- * the host.
+ * the host.  Alignment: the 16-B and 2-B cases are stated per field; every
+ * other pointer (int32 / uint32 / float arrays, optional ones included when
+ * not NULL) must be 4-byte aligned, or the call returns QLI_ERR_INVALID_ARG.
  */
 #ifndef QLI_H
 #define QLI_H

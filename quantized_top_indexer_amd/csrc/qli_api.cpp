@@ -44,6 +44,33 @@ int check_scalars(const qli_params* p) {
   return QLI_OK;
 }
 
+// Every check of a call except the workspace's (shared by the two entry
+// points that enqueue the indexer).
+int check_args(const qli_params* p) {
+  int rc = check_scalars(p);
+  if (rc != QLI_OK) return rc;
+  // residual: the guide requires it to be absent at ratio 1; ratio 2 needs it
+  if (p->ratio == 1 && p->seq_mod) return QLI_ERR_INVALID_ARG;
+  if (p->mode == QLI_MODE_CONSUMER && !p->cand_in) return QLI_ERR_NO_SOURCE;
+  if (p->num_tokens == 0) return QLI_OK;
+  if (p->ratio == 2 && !p->seq_mod) return QLI_ERR_INVALID_ARG;
+  if (!p->q || !p->q_scale || !p->weights || !p->k_cache || !p->k_scale || !p->block_table ||
+      !p->query_start_loc || !p->k_lens || !p->topk_out)
+    return QLI_ERR_INVALID_ARG;
+  if (p->mode == QLI_MODE_SOURCE && !p->cand_out) return QLI_ERR_INVALID_ARG;
+  if (p->dbg_qk && (!p->dbg_scores || !aligned(p->dbg_qk, 4))) return QLI_ERR_INVALID_ARG;
+  if (!aligned(p->q, 16) || !aligned(p->k_cache, 16) || !aligned(p->k_scale, 16) ||
+      !aligned(p->q_scale, 2) || !aligned(p->weights, 2) || !aligned(p->block_table, 4) ||
+      !aligned(p->query_start_loc, 4) || !aligned(p->k_lens, 4) || !aligned(p->topk_out, 4))
+    return QLI_ERR_INVALID_ARG;
+  // optional and mode-dependent pointers (NULL passes): 32-bit words, and
+  // the status word takes device atomics
+  if (!aligned(p->seq_mod, 4) || !aligned(p->cand_in, 4) || !aligned(p->cand_out, 4) ||
+      !aligned(p->dbg_scores, 4) || !aligned(p->status_out, 4))
+    return QLI_ERR_INVALID_ARG;
+  return QLI_OK;
+}
+
 bool dtype_ok(int32_t d) { return d == QLI_DTYPE_F32 || d == QLI_DTYPE_BF16; }
 
 int check_quant(const qli_quant_params* p) {
@@ -104,22 +131,8 @@ int qli_write_index_k(const qli_kwrite_params* p, void* stream) {
 int qli_abi_version(void) { return QLI_ABI_VERSION; }
 
 int qli_validate(const qli_params* p) {
-  int rc = check_scalars(p);
-  if (rc != QLI_OK) return rc;
-  // residual: the guide requires it to be absent at ratio 1; ratio 2 needs it
-  if (p->ratio == 1 && p->seq_mod) return QLI_ERR_INVALID_ARG;
-  if (p->mode == QLI_MODE_CONSUMER && !p->cand_in) return QLI_ERR_NO_SOURCE;
-  if (p->num_tokens == 0) return QLI_OK;
-  if (p->ratio == 2 && !p->seq_mod) return QLI_ERR_INVALID_ARG;
-  if (!p->q || !p->q_scale || !p->weights || !p->k_cache || !p->k_scale || !p->block_table ||
-      !p->query_start_loc || !p->k_lens || !p->topk_out)
-    return QLI_ERR_INVALID_ARG;
-  if (p->mode == QLI_MODE_SOURCE && !p->cand_out) return QLI_ERR_INVALID_ARG;
-  if (p->dbg_qk && (!p->dbg_scores || !aligned(p->dbg_qk, 4))) return QLI_ERR_INVALID_ARG;
-  if (!aligned(p->q, 16) || !aligned(p->k_cache, 16) || !aligned(p->k_scale, 16) ||
-      !aligned(p->q_scale, 2) || !aligned(p->weights, 2) || !aligned(p->block_table, 4) ||
-      !aligned(p->query_start_loc, 4) || !aligned(p->k_lens, 4) || !aligned(p->topk_out, 4))
-    return QLI_ERR_INVALID_ARG;
+  const int rc = check_args(p);
+  if (rc != QLI_OK || p->num_tokens == 0) return rc;
   const qli::WsLayout w = qli::ws_layout(p);
   if (w.total > 0 && (!p->workspace || !aligned(p->workspace, 256))) return QLI_ERR_WORKSPACE;
   if (p->workspace_bytes < w.total) return QLI_ERR_WORKSPACE;

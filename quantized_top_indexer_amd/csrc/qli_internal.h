@@ -103,8 +103,9 @@ class Stamp {
   void* stop_ = nullptr;
 };
 
-// Compute units of the current device (cached per device).
+// Compute units and XCDs of the current device (cached per device).
 int cu_count();
+int xcd_count();
 
 // Enqueue the quantization / K-write kernels (arguments already validated).
 int launch_quantize(const qli_quant_params* p, void* stream);

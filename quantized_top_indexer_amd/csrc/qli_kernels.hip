@@ -87,6 +87,7 @@ struct KArgs {
   float one;  // 1.0f
   int mode, ratio, rshift, B, T, topk, cb, cb_in, R, rlog, bt_stride, num_pages, max_k_len;
   int score_grid;
+  int nxcd;            // XCDs of the device (accelerator dies, each with its own L2)
   int sel_lo, sel_hi;  // this select launch takes the rows whose length n has sel_lo <= n <= sel_hi
   int64_t kstride, sstride, ncap, nbcap;
   const int8_t* q;
@@ -1413,6 +1414,17 @@ __device__ void run_single(const KArgs& a, const ListView& L, Cursor cu, int hi,
   if (ne > 0) flush_keys<MODE>(a, stage, meta, ne);
 }
 
+// The dispatcher hands workgroup i to XCD i mod nxcd, and each XCD has its
+// own L2.  The plan splits the work lists into contiguous ranges in token
+// order (the tokens of a request are neighbours), so workgroup i takes
+// start entry (i mod nxcd) * (grid / nxcd) + i / nxcd: every XCD walks one
+// contiguous stretch of the lists, and the tokens of a request that read
+// the same K rows share an L2 instead of fetching them through all of them.
+__device__ __forceinline__ int start_entry(int i, int grid, int nxcd) {
+  if (nxcd <= 1 || grid % nxcd) return i;
+  return (i % nxcd) * (grid / nxcd) + i / nxcd;
+}
+
 // Each workgroup takes its list, first item and unit range from the plan.
 // STREAM: K rows of single-token groups are read with non-temporal loads
 // (read once per call: decode).  Consumer batches whose requests hold
@@ -1429,7 +1441,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(KArgs a) {
 
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
-  const WgStart st = a.wgs[blockIdx.x];
+  const WgStart st = a.wgs[start_entry(blockIdx.x, gridDim.x, a.nxcd)];
   if (st.g < 0 || st.unit >= st.hi) return;
   const int l = st.list;
   const ListView L{a.groups + static_cast<int64_t>(l) * a.T,
@@ -1997,6 +2009,8 @@ double g_ms[QLI_NUM_KERNELS];
 int64_t g_count[QLI_NUM_KERNELS];
 
 int g_cu_count[64];
+int g_xcd_count[64];
+
 }  // namespace
 
 Stamp::Stamp(int k, void* s) : kernel_(k), st_(s) {
@@ -2029,6 +2043,17 @@ int cu_count() {
     g_cu_count[dev] = n;
   }
   return g_cu_count[dev];
+}
+
+int xcd_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  if (!g_xcd_count[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || n <= 0) n = 1;
+    g_xcd_count[dev] = n;
+  }
+  return g_xcd_count[dev];
 }
 
 int timing_enable(int on) {
@@ -2134,6 +2159,7 @@ int launch(const qli_params* p, const WsLayout& w, void* stream) {
   a.ustart = reinterpret_cast<int32_t*>(ws + w.ustart_off);
   a.wgs = reinterpret_cast<WgStart*>(ws + w.wgs_off);
   a.score_grid = std::min(kMaxScoreWGs, std::max(2, 2 * cu_count()));
+  a.nxcd = xcd_count();
   a.slots = consumer ? reinterpret_cast<int32_t*>(ws + w.slots_off) : nullptr;
   a.srow = consumer ? reinterpret_cast<int32_t*>(ws + w.srow_off) : nullptr;
   a.ncount = consumer ? reinterpret_cast<int32_t*>(ws + w.ncount_off) : nullptr;

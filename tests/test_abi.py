@@ -282,6 +282,20 @@ def test_write_k_noop(lib):
     assert Q.qli_write_index_k(p, 0) == Q.QLI_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("field,mode", [("status_out", 2), ("cand_out", 2), ("dbg_scores", 2),
+                                        ("seq_mod", 2), ("cand_in", 3)])
+def test_word_pointer_alignment(lib, field, mode):
+    """Optional and mode-dependent pointers are read or written as 32-bit
+    words (the status word with device atomics): a pointer off a 4-byte
+    boundary is rejected before any launch; an aligned one passes."""
+    p = base_params(mode=mode, ratio=2)
+    setattr(p, field, 0x7F0000300000 + 2)
+    assert Q.qli_validate(p) == Q.QLI_ERR_INVALID_ARG
+    assert lib.qli_score_topk(C.byref(p), None) == Q.QLI_ERR_INVALID_ARG
+    setattr(p, field, 0x7F0000300000)
+    assert Q.qli_validate(p) == Q.QLI_OK
+
+
 def test_debug_qk_alignment(lib):
     p = base_params(mode=2, ratio=2)
     p.dbg_scores = 0x7F0000200000

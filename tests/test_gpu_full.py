@@ -42,7 +42,10 @@ def test_tiny():
 
 
 def test_decode_source():
-    _full_case(W.decode_source(), 8)
+    """Every one of the 64 tokens against the oracle (32768-key rows: the
+    sampled-bracket selection on uniform random keys)."""
+    pb = W.decode_source()
+    _full_case(pb, pb.num_tokens)
 
 
 def test_prefill_chunk():

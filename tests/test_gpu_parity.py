@@ -111,6 +111,47 @@ def test_heavy_ties(mode, patterns):
     check_invariants(pb, gpu)
 
 
+# Rows of 24576..32768 eligible keys in batches of at most 4 rows per CU: the
+# single-chunk 1024-thread selection, which first brackets the threshold from
+# a sample of the keys, gathers the keys inside the bracket (at most 4096) and
+# refines among them alone; when the bracket misses the threshold or holds
+# more keys it falls back to refining over the whole row.
+SEL_BRACKET_REQ = ((4, 32768), (2, 30001), (1, 24577), (1, 28000))
+SEL_GATHER_CAP = 4096   # keys the bracket may gather (an eighth of the chunk)
+
+
+@pytest.mark.parametrize("mode,patterns", [(1, 0), (2, 0), (1, 3), (2, 3), (1, 200), (2, 200)])
+def test_sampled_bracket_selection(mode, patterns):
+    """Every token's row in the sampled-bracket range, every output compared
+    with the oracle.  patterns = 0: random K (no ties, the bracket holds);
+    3: K rows from three patterns with one scale, so a token sees at most
+    three distinct scores and the value at the k-th rank repeats more than
+    4096 times: any bracket that contains the threshold holds more keys than
+    it may gather, so the fallback over the whole row runs (asserted below
+    on the oracle's scores); 200: about 160 copies of each value, so the
+    boundary falls inside a run of equal keys within the bracket."""
+    pb = small_problem(360 + mode + patterns, ratio=1, N=32, mode=mode, topk=2048, cb=512,
+                       requests=SEL_BRACKET_REQ)
+    vis = visible(pb)
+    assert vis.min() >= 24576 and pb.max_k_len <= 32768 and 2 * pb.num_tokens <= 4 * 256
+    if patterns:
+        rng = np.random.default_rng(361 + patterns)
+        pats = rng.integers(-128, 128, size=(patterns, 128), dtype=np.int64).astype(np.int8)
+        P, R, _ = pb.k_pages.shape
+        pb.k_pages = pats[rng.integers(0, patterns, size=P * R)].reshape(P, R, 128).copy()
+        pb.s_pages = np.full((P, R), 0x3C00, dtype=np.uint16)
+    say(f"sampled bracket {pb.name} patterns={patterns}: T={pb.num_tokens} L={pb.max_k_len}")
+    gpu = run_gpu(pb, debug=True)
+    orc = oracle_rows(pb, scores=True)
+    compare(pb, gpu, orc)
+    check_invariants(pb, gpu)
+    if patterns == 3:
+        for t in range(pb.num_tokens):
+            row = orc["scores"][t, : vis[t]].astype(np.float64)
+            kth = np.sort(row)[::-1][pb.topk - 1]
+            assert np.count_nonzero(row == kth) > SEL_GATHER_CAP, t
+
+
 @pytest.mark.parametrize("ratio,N,mode", [(2, 64, 2), (1, 32, 1), (2, 32, 3)])
 def test_head_multiplier_ranges(ratio, N, mode):
     """Head multipliers m = fp16(w * q_scale) across the ranges the score
