@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define QLI_ABI_VERSION 2
+#define QLI_ABI_VERSION 3
 
 /* Status codes returned by the host entry points. */
 enum qli_status {
@@ -72,7 +72,9 @@ enum qli_status {
   QLI_ERR_NO_SOURCE = 3,   /* consumer mode without incoming candidates */
   QLI_ERR_WORKSPACE = 4,   /* workspace missing or smaller than
                               qli_workspace_bytes() */
-  QLI_ERR_HIP = 5          /* a kernel launch failed */
+  QLI_ERR_HIP = 5,         /* a kernel launch failed */
+  QLI_ERR_SCRATCH_LIMIT = 6 /* qli_score_topk_noalloc: the call needs more
+                               than QLI_STATIC_SCRATCH_BYTES of scratch */
 };
 
 /* Candidate modes: all three run through the same operator (guide, section
@@ -183,6 +185,29 @@ size_t qli_workspace_bytes(const qli_params* p);
  * Re-entrant for calls with distinct workspaces and outputs; calls that
  * share a workspace must be ordered on one stream. Returns a qli_status. */
 int qli_score_topk(const qli_params* p, void* stream);
+
+/* Scratch of qli_score_topk_noalloc: a device array of this many bytes
+ * inside the library, one per GPU it runs on, held until the process
+ * ends. */
+#define QLI_STATIC_SCRATCH_BYTES (32u << 20)
+
+/* The same operation as qli_score_topk, for callers that cannot allocate
+ * device memory or hand the library a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * scratch is the library's own static device array
+ * (QLI_STATIC_SCRATCH_BYTES per GPU); p->workspace and p->workspace_bytes
+ * are ignored.  Every other field, the validation and the outputs are those
+ * of qli_score_topk.  A call whose workspace (qli_workspace_bytes) exceeds
+ * the array returns QLI_ERR_SCRATCH_LIMIT before anything is launched;
+ * decode-sized calls fit (64 tokens over 32768 positions in source mode
+ * need 9.5 MB).  Nothing here allocates: the first call on a device looks
+ * the array up once (hipGetSymbolAddress), no hipMalloc/hipFree and no
+ * timing events.  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (other streams, other threads) race and give
+ * undefined results; calls ordered on one stream are safe, and each call
+ * rewrites every scratch word it reads, so nothing needs clearing between
+ * calls.  Returns a qli_status. */
+int qli_score_topk_noalloc(const qli_params* p, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* qli_status_string(int status);

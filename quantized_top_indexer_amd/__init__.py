@@ -6,7 +6,7 @@ of the indexer runs in the HIP kernels.  There is no fallback: if the
 library is not built, importing the entry points raises.
 
 Entry points (same names as the C ABI): ``qli_score_topk``,
-``qli_workspace_bytes``, ``qli_validate``, ``qli_status_string``,
+``qli_score_topk_noalloc``, ``qli_workspace_bytes``, ``qli_validate``, ``qli_status_string``,
 ``qli_abi_version``, ``qli_quantize_query``, ``qli_write_index_k``; plus
 ``score_topk``, ``quantize_query`` and ``write_index_k``, convenience
 wrappers that allocate the outputs (and the workspace) with torch and run
@@ -22,7 +22,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqli.so")
 
 QLI_OK, QLI_ERR_INVALID_ARG, QLI_ERR_UNSUPPORTED, QLI_ERR_NO_SOURCE, QLI_ERR_WORKSPACE, \
-    QLI_ERR_HIP = range(6)
+    QLI_ERR_HIP, QLI_ERR_SCRATCH_LIMIT = range(7)
+QLI_STATIC_SCRATCH_BYTES = 32 << 20
 QLI_MODE_PLAIN, QLI_MODE_SOURCE, QLI_MODE_CONSUMER = 1, 2, 3
 QLI_QUANT_INT8 = 2
 QLI_DEV_BAD_PAGE, QLI_DEV_BAD_LENGTH, QLI_DEV_BAD_METADATA = 1, 2, 4
@@ -73,7 +74,7 @@ class qli_kwrite_params(C.Structure):
 
 
 EXPORTS = ("qli_abi_version", "qli_validate", "qli_workspace_bytes", "qli_score_topk",
-           "qli_status_string", "qli_timing_enable", "qli_timing_read", "qli_quantize_query",
+           "qli_score_topk_noalloc", "qli_status_string", "qli_timing_enable", "qli_timing_read", "qli_quantize_query",
            "qli_write_index_k", "qli_probe_hbm_read", "qli_probe_int8_mfma",
            "qli_probe_int8_mfma_ops")
 QLI_KERNEL_CONSUMER_PREP, QLI_KERNEL_PLAN, QLI_KERNEL_SCORE, QLI_KERNEL_SELECT, \
@@ -105,6 +106,8 @@ def load_library(path: str = LIB_PATH):
     L.qli_workspace_bytes.argtypes = [C.POINTER(qli_params)]
     L.qli_score_topk.restype = C.c_int
     L.qli_score_topk.argtypes = [C.POINTER(qli_params), C.c_void_p]
+    L.qli_score_topk_noalloc.restype = C.c_int
+    L.qli_score_topk_noalloc.argtypes = [C.POINTER(qli_params), C.c_void_p]
     L.qli_status_string.restype = C.c_char_p
     L.qli_status_string.argtypes = [C.c_int]
     L.qli_timing_enable.restype = C.c_int
@@ -145,6 +148,12 @@ def qli_score_topk(p: qli_params, stream=None) -> int:
         import torch
         stream = torch.cuda.current_stream().cuda_stream
     return load_library().qli_score_topk(C.byref(p), C.c_void_p(stream))
+
+
+def qli_score_topk_noalloc(p: qli_params, stream=None) -> int:
+    """Enqueue one call with the library's static scratch instead of a
+    workspace (p.workspace is ignored); see include/qli.h."""
+    return load_library().qli_score_topk_noalloc(C.byref(p), _stream(stream))
 
 
 def _stream(stream):

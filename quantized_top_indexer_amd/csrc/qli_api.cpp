@@ -148,8 +148,25 @@ int qli_score_topk(const qli_params* p, void* stream) {
   int rc = qli_validate(p);
   if (rc != QLI_OK) return rc;
   if (p->num_tokens == 0) return QLI_OK;
-  return qli::launch(p, qli::ws_layout(p), stream);
+  return qli::launch(p, qli::ws_layout(p), stream, true);
 }
+
+int qli_score_topk_noalloc(const qli_params* p, void* stream) {
+  int rc = check_args(p);
+  if (rc != QLI_OK) return rc;
+  const qli::WsLayout w = qli::ws_layout(p);
+  if (w.total > QLI_STATIC_SCRATCH_BYTES) return QLI_ERR_SCRATCH_LIMIT;
+  if (p->num_tokens == 0) return QLI_OK;
+  void* scratch = nullptr;
+  rc = qli::static_scratch(&scratch);
+  if (rc != QLI_OK) return rc;
+  qli_params q = *p;
+  q.workspace = scratch;
+  q.workspace_bytes = QLI_STATIC_SCRATCH_BYTES;
+  // no timing events either: recording them creates HIP events
+  return qli::launch(&q, w, stream, false);
+}
+
 
 int qli_timing_enable(int on) { return qli::timing_enable(on); }
 
@@ -165,6 +182,9 @@ const char* qli_status_string(int status) {
     case QLI_ERR_NO_SOURCE: return "QLI_ERR_NO_SOURCE: consumer mode needs incoming candidates";
     case QLI_ERR_WORKSPACE: return "QLI_ERR_WORKSPACE: workspace missing or too small";
     case QLI_ERR_HIP: return "QLI_ERR_HIP: kernel launch failed";
+    case QLI_ERR_SCRATCH_LIMIT:
+      return "QLI_ERR_SCRATCH_LIMIT: the call needs more than the static scratch of "
+             "qli_score_topk_noalloc (QLI_STATIC_SCRATCH_BYTES); use qli_score_topk with a workspace";
     default: return "QLI: unknown status";
   }
 }

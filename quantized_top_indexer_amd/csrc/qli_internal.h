@@ -81,8 +81,13 @@ inline WsLayout ws_layout(const qli_params* p) {
   return w;
 }
 
-// Enqueue the kernels (arguments already validated).
-int launch(const qli_params* p, const WsLayout& w, void* stream);
+// Enqueue the kernels (arguments already validated).  timed: record the
+// optional timing events (when the timing facility is on).
+int launch(const qli_params* p, const WsLayout& w, void* stream, bool timed);
+
+// Device address of the library's static scratch array on the current
+// device (looked up once per device); a qli_status.
+int static_scratch(void** ptr);
 
 int timing_enable(int on);
 int timing_read(double* ms, int64_t* count, int reset);
@@ -91,7 +96,7 @@ int timing_read(double* ms, int64_t* count, int reset);
 // and another at destruction, queued for timing_read() under `kernel`.
 class Stamp {
  public:
-  Stamp(int kernel, void* stream);
+  Stamp(int kernel, void* stream, bool enabled = true);
   ~Stamp();
   Stamp(const Stamp&) = delete;
   Stamp& operator=(const Stamp&) = delete;

@@ -2011,10 +2011,30 @@ int64_t g_count[QLI_NUM_KERNELS];
 int g_cu_count[64];
 int g_xcd_count[64];
 
+// Scratch of the entry point that allocates nothing.  In host code the name
+// only stands for the array; its device address (one copy per GPU) comes
+// from hipGetSymbolAddress and is the only form ever passed to a kernel or
+// a copy.
+static __device__ __align__(256) unsigned char scratch[QLI_STATIC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
 }  // namespace
 
-Stamp::Stamp(int k, void* s) : kernel_(k), st_(s) {
-  if (!g_timing_on) return;
+int static_scratch(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return QLI_ERR_HIP;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;  // looked up with device `dev` current
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return QLI_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return QLI_OK;
+}
+
+Stamp::Stamp(int k, void* s, bool enabled) : kernel_(k), st_(s) {
+  if (!enabled || !g_timing_on) return;
   hipEvent_t a = nullptr, b = nullptr;
   if (hipEventCreate(&a) != hipSuccess) return;
   if (hipEventCreate(&b) != hipSuccess) {
@@ -2112,7 +2132,7 @@ void launch_score(int heads, int mode, bool dbg, bool cached, unsigned grid, hip
   else launch_score_mode<32>(mode, dbg, cached, grid, st, a);
 }
 
-int launch(const qli_params* p, const WsLayout& w, void* stream) {
+int launch(const qli_params* p, const WsLayout& w, void* stream, bool timed) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // an earlier failure elsewhere on this thread is not ours to report
   KArgs a;
@@ -2171,28 +2191,28 @@ int launch(const qli_params* p, const WsLayout& w, void* stream) {
   if (consumer && bitmap && T >= static_cast<unsigned>(kPrepLeanMinTokens)) {
     // the plan, then one lean workgroup per token
     {
-      Stamp s(QLI_KERNEL_PLAN, st);
+      Stamp s(QLI_KERNEL_PLAN, st, timed);
       plan_kernel<kPlanThreads><<<1, kPlanThreads, 0, st>>>(a);
     }
-    Stamp s(QLI_KERNEL_CONSUMER_PREP, st);
+    Stamp s(QLI_KERNEL_CONSUMER_PREP, st, timed);
     const int nwcap = static_cast<int>((max_blocks + 31) / 32);
     const size_t lds = (static_cast<size_t>(nwcap) + static_cast<size_t>(p->cand_in_blocks) + 65) * 4;
     consumer_prep_lean_kernel<<<T, kPrepBitmapThreads, lds, st>>>(a, nwcap);
   } else if (consumer) {
     // block 0 plans, blocks 1..T prepare the tokens
-    Stamp s(QLI_KERNEL_CONSUMER_PREP, st);
+    Stamp s(QLI_KERNEL_CONSUMER_PREP, st, timed);
     if (bitmap)
       consumer_prep_kernel<<<T + 1, kPrepThreads, 0, st>>>(a);
     else
       consumer_prep_sort_kernel<<<T + 1, kPrepThreads, 0, st>>>(a);
   } else {
-    Stamp s(QLI_KERNEL_PLAN, st);
+    Stamp s(QLI_KERNEL_PLAN, st, timed);
     // a decode-sized batch is planned by one wave
     if (p->num_tokens <= 64 && p->batch <= 256) plan_kernel<64><<<1, 64, 0, st>>>(a);
     else plan_kernel<kPlanThreads><<<1, kPlanThreads, 0, st>>>(a);
   }
   if (w.ncap > 0) {
-    Stamp s(QLI_KERNEL_SCORE, st);
+    Stamp s(QLI_KERNEL_SCORE, st, timed);
     // some request holds several query tokens (consumer mode: each reads its
     // own candidate rows of the request's K, so the rows are read repeatedly)
     const bool cached = p->num_tokens > p->batch;
@@ -2200,7 +2220,7 @@ int launch(const qli_params* p, const WsLayout& w, void* stream) {
                  st, a);
   }
   {
-    Stamp s(QLI_KERNEL_SELECT, st);
+    Stamp s(QLI_KERNEL_SELECT, st, timed);
     const int64_t longest = w.ncap > w.nbcap ? w.ncap : w.nbcap;
     const dim3 grid(T, source ? 2 : 1);
     // rows no longer than a chunk (every n <= its row capacity) take the

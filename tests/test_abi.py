@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert Q.qli_abi_version() == 2
+    assert Q.qli_abi_version() == 3
 
 
 @pytest.mark.parametrize("struct", ["qli_params", "qli_quant_params", "qli_kwrite_params"])
@@ -294,6 +294,24 @@ def test_word_pointer_alignment(lib, field, mode):
     assert lib.qli_score_topk(C.byref(p), None) == Q.QLI_ERR_INVALID_ARG
     setattr(p, field, 0x7F0000300000)
     assert Q.qli_validate(p) == Q.QLI_OK
+
+
+def test_noalloc_rejections(lib):
+    """The entry point without a workspace checks every argument as
+    qli_score_topk does (the workspace fields aside) and rejects a call whose
+    scratch need exceeds the static array, before any launch."""
+    p = base_params(mode=2, ratio=2)
+    p.workspace, p.workspace_bytes = None, 0          # ignored by this entry point
+    for field, value in (("topk", 0), ("q", None), ("cand_out", 0x7F0000300002)):
+        bad = base_params(mode=2, ratio=2)
+        setattr(bad, field, value)
+        assert lib.qli_score_topk_noalloc(C.byref(bad), None) == Q.qli_validate(bad) != Q.QLI_OK
+    p.num_tokens = 40000                              # 40000 x 256 key slots x 4 B > 32 MiB
+    assert Q.qli_workspace_bytes(p) > Q.QLI_STATIC_SCRATCH_BYTES
+    assert lib.qli_score_topk_noalloc(C.byref(p), None) == Q.QLI_ERR_SCRATCH_LIMIT
+    assert "static scratch" in Q.qli_status_string(Q.QLI_ERR_SCRATCH_LIMIT)
+    p.num_tokens = 0                                  # a no-op, nothing looked up
+    assert lib.qli_score_topk_noalloc(C.byref(p), None) == Q.QLI_OK
 
 
 def test_debug_qk_alignment(lib):
