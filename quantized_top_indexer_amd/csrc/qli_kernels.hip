@@ -999,7 +999,10 @@ struct QLds {
 };
 
 // Fill QLds for token t (SPLIT layout), all threads of the workgroup.
-template <int NH>
+// TRY_SCALED: when every head multiplier of the token has |m| < 32, ml
+// holds m * 2^11 and ml[NH / 2] = 1 (the scaled epilogue applies);
+// otherwise ml holds m and ml[NH / 2] = 0.
+template <int NH, bool TRY_SCALED = false>
 __device__ __forceinline__ void load_q_lds(const KArgs& a, int t, i32x4* fr, uint32_t* ml) {
   constexpr int MT = NH / 32;
   const int tid = threadIdx.x;
@@ -1011,12 +1014,26 @@ __device__ __forceinline__ void load_q_lds(const KArgs& a, int t, i32x4* fr, uin
     fr[e] = *reinterpret_cast<const i32x4*>(a.q + (static_cast<int64_t>(t) * NH + head) * 128 + 64 * g +
                                             16 * s);
   }
-  if (tid < NH / 2) {  // pair j = tid >> 1 of group g = tid & 1: heads 32*(j/8) + 16g + 2*(j%8)
-    const int j = tid >> 1, g = tid & 1;
-    const int h0 = 32 * (j >> 3) + 16 * g + 2 * (j & 7);
-    const uint32_t* wr = reinterpret_cast<const uint32_t*>(a.w + static_cast<int64_t>(t) * NH);
-    const uint32_t* qr = reinterpret_cast<const uint32_t*>(a.qs + static_cast<int64_t>(t) * NH);
-    ml[tid] = as_u32(as_h2(wr[h0 >> 1]) * as_h2(qr[h0 >> 1]));  // fp16 RNE
+  if (tid < 64) {  // wave 0: pair j = tid >> 1 of group g = tid & 1: heads 32*(j/8) + 16g + 2*(j%8)
+    uint32_t u = 0;
+    bool small = true;
+    if (tid < NH / 2) {
+      const int j = tid >> 1, g = tid & 1;
+      const int h0 = 32 * (j >> 3) + 16 * g + 2 * (j & 7);
+      const uint32_t* wr = reinterpret_cast<const uint32_t*>(a.w + static_cast<int64_t>(t) * NH);
+      const uint32_t* qr = reinterpret_cast<const uint32_t*>(a.qs + static_cast<int64_t>(t) * NH);
+      u = as_u32(as_h2(wr[h0 >> 1]) * as_h2(qr[h0 >> 1]));  // fp16 RNE
+      small = (u & 0x7FFFu) < kHalfAbs32 && ((u >> 16) & 0x7FFFu) < kHalfAbs32;
+    }
+    if (TRY_SCALED) {
+      // m * 2^11 must stay a finite fp16 for every head (NaN and infinite
+      // multipliers fail the test as well)
+      const bool scaled = __builtin_amdgcn_ballot_w64(!small) == 0;
+      const h2 k2048 = {static_cast<_Float16>(2048.0f), static_cast<_Float16>(2048.0f)};
+      if (scaled) u = as_u32(as_h2(u) * k2048);  // exact
+      if (tid == 0) ml[NH / 2] = scaled ? 1u : 0u;
+    }
+    if (tid < NH / 2) ml[tid] = u;
   }
 }
 
@@ -1175,19 +1192,23 @@ __device__ __forceinline__ void dbg_store_qk(const KArgs& a, const i32x16 (&acc)
 }
 
 // One sub-tile, the passes one after the other (a loop: overlapping them
-// would keep two head tiles of accumulators live).
+// would keep two head tiles of accumulators live).  scaled (wave-uniform):
+// the multipliers are m * 2^11 and the scaled epilogue with a packed
+// conversion applies (fewer VALU instructions where they bound the kernel);
+// otherwise the plain epilogue with the mixed-precision conversion.
 template <int NH, int MODE, bool DBG, class QSrc>
 __device__ __forceinline__ void score_subtile(const KArgs& a, const QSrc& qs,
                                               const int8_t* tile, const uint16_t* ksc, int sub,
                                               int t, int s0, int n_i, int lane, const i32x16& seed,
-                                              uint32_t* kp, uint32_t* bp) {
+                                              uint32_t* kp, uint32_t* bp, bool scaled = false) {
   float sum = 0.0f;
 #pragma unroll 1
   for (int ps = 0; ps < NH / 32; ++ps) {
     i32x16 acc[2];
     mfma_pass(qs, tile, sub, ps, lane, seed, acc);
     if (DBG) dbg_store_qk<NH, MODE>(a, acc, ps, t, s0, n_i, ksc, sub, lane);
-    epi_pass<false, false>(qs, acc, ps, lane, a.one, sum);
+    if (scaled) epi_pass<true, true>(qs, acc, ps, lane, a.one, sum);
+    else epi_pass<false, false>(qs, acc, ps, lane, a.one, sum);
   }
   finish_subtile<MODE, DBG>(a, ksc, sub, t, s0, n_i, lane, sum, kp, bp);
 }
@@ -1325,9 +1346,15 @@ __device__ void run_multi(const KArgs& a, const ListView& L, Cursor cur, int hi,
 // (the second K buffer, unused here) and written out together when the
 // stage is full and at the end of the range: HBM writes spread through the
 // K stream cost far more read bandwidth than the same bytes in bursts.
-constexpr int kKeyStage = 24;                  // staged items
+constexpr int kKeyStage = 24;                  // staged items (the second K buffer of the combined kernel)
 constexpr int kKeyEntry = kChunk + kChunk / 8;  // u32 words per staged item (keys, block maxima)
 static_assert(kKeyStage * kKeyEntry * 4 + kKeyStage * 8 <= kChunk * 128, "key stage exceeds a K buffer");
+// Consumer-mode kernels hold only the single-token path: one K tile and a
+// key stage of their own, small enough that three workgroups share a CU's
+// 160 KB of LDS (K tile 32 KB, queries 4 or 8 KB, stage 11.6 or 16.2 KB).
+// With 32 heads the path fits the 168 VGPRs of three waves per SIMD without
+// spilling; with 64 heads it needs 210 and keeps two workgroups per CU.
+constexpr int key_stage_single(int nh) { return nh == 64 ? 10 : 14; }
 
 template <int MODE>
 __device__ __forceinline__ void flush_keys(const KArgs& a, const uint32_t* stage, const int32_t* meta,
@@ -1345,18 +1372,23 @@ __device__ __forceinline__ void flush_keys(const KArgs& a, const uint32_t* stage
   __syncthreads();  // the stage is free again
 }
 
-template <int NH, int MODE, bool DBG, bool STREAM>
-__device__ void run_single(const KArgs& a, const ListView& L, Cursor cu, int hi,
-                           int8_t (*tile)[kChunk * 128], uint16_t (*ksc)[kChunk], i32x4* qfr,
-                           uint32_t* qml, int wave, int lane, const i32x16& seed, bool& bad) {
+// STAGE: items the key stage holds; SCALED_EPI: tokens whose multipliers
+// allow it take the scaled epilogue (compute-bound batches).  The queries
+// sit in LDS, shared by the four waves (in registers, the 32-head consumer
+// path spills at three workgroups per CU and measured slower: mixed batch
+// consumer score kernels 1.42 -> 1.52 ms).
+template <int NH, int MODE, bool DBG, bool STREAM, int STAGE, bool SCALED_EPI>
+__device__ void run_single(const KArgs& a, const ListView& L, Cursor cu, int hi, int8_t* ktile,
+                           uint16_t* ksc0, uint32_t* stage, i32x4* qfr, uint32_t* qml, int wave,
+                           int lane, const i32x16& seed, bool& bad) {
   static_assert(kScoreThreads == kChunk, "one staged key per thread and item");
   constexpr bool CONSUMER = MODE == QLI_MODE_CONSUMER;
-  uint32_t* stage = reinterpret_cast<uint32_t*>(tile[1]);
-  int32_t* meta = reinterpret_cast<int32_t*>(stage + kKeyStage * kKeyEntry);
+  int32_t* meta = reinterpret_cast<int32_t*>(stage + STAGE * kKeyEntry);
   int ne = 0;  // staged items (the same in every wave)
+  bool scaled = false;  // the current token takes the scaled epilogue
   // score item c of token t into staged entry ne, flushing a full stage
   auto score_item = [&](int t, int c, int n) {
-    if (ne == kKeyStage) {
+    if (ne == STAGE) {
       flush_keys<MODE>(a, stage, meta, ne);
       ne = 0;
     }
@@ -1365,8 +1397,8 @@ __device__ void run_single(const KArgs& a, const ListView& L, Cursor cu, int hi,
       meta[2 * ne + 1] = c;
     }
     uint32_t* kp = stage + ne * kKeyEntry;
-    score_subtile<NH, MODE, DBG>(a, QLds<NH>{qfr, qml}, tile[0], ksc[0], wave, t, c * kChunk + 64 * wave,
-                                 n, lane, seed, kp, kp + kChunk);
+    score_subtile<NH, MODE, DBG>(a, QLds<NH>{qfr, qml}, ktile, ksc0, wave, t, c * kChunk + 64 * wave,
+                                 n, lane, seed, kp, kp + kChunk, SCALED_EPI && scaled);
     ++ne;
   };
   while (cu.valid) {
@@ -1379,7 +1411,7 @@ __device__ void run_single(const KArgs& a, const ListView& L, Cursor cu, int hi,
     if (CONSUMER) gr.n0 = a.ncount[t];
     const int n = gr.n0;
     __syncthreads();  // the previous segment's last item is scored
-    load_q_lds<NH>(a, t, qfr, qml);
+    load_q_lds<NH, SCALED_EPI>(a, t, qfr, qml);
     Addr ad;
     i32x4 krA[8], krB[8];
     i32x4 scA, scB;
@@ -1391,15 +1423,16 @@ __device__ void run_single(const KArgs& a, const ListView& L, Cursor cu, int hi,
     stage_addr<CONSUMER, true>(a, gr, c0 + 2, c0 + 2 < c_end, wave, lane, ad);
     stage_load<STREAM>(a, vB, lane, krB, scB);
     __syncthreads();  // queries in LDS
+    if (SCALED_EPI) scaled = __builtin_amdgcn_readfirstlane(static_cast<int>(qml[NH / 2])) != 0;
     for (int c = c0; c < c_end; c += 2) {
-      stage_store<true>(tile[0], ksc[0], krA, scA, vA, wave, lane);
+      stage_store<true>(ktile, ksc0, krA, scA, vA, wave, lane);
       vA = resolve<CONSUMER>(a, ad, bad);
       stage_addr<CONSUMER, true>(a, gr, c + 3, c + 3 < c_end, wave, lane, ad);
       stage_load<STREAM>(a, vA, lane, krA, scA);
       __builtin_amdgcn_wave_barrier();
       score_item(t, c, n);
       if (c + 1 >= c_end) break;
-      stage_store<true>(tile[0], ksc[0], krB, scB, vB, wave, lane);
+      stage_store<true>(ktile, ksc0, krB, scB, vB, wave, lane);
       vB = resolve<CONSUMER>(a, ad, bad);
       stage_addr<CONSUMER, true>(a, gr, c + 4, c + 4 < c_end, wave, lane, ad);
       stage_load<STREAM>(a, vB, lane, krB, scB);
@@ -1432,12 +1465,26 @@ __device__ __forceinline__ int start_entry(int i, int grid, int nxcd) {
 // reads its own candidate rows, so the rows of a request are read again and
 // again and the caches serve the repeats (mixed batch consumer score
 // kernels 2.96 -> 1.77 ms and 2.42 -> 1.50 ms in one A/B measurement).
+// Consumer tokens are always single groups, so consumer-mode kernels hold
+// only that path (three workgroups per CU instead of two); the cached ones
+// (compute-bound: each prefill token scores its own candidate rows) take
+// the scaled epilogue.
+__host__ __device__ constexpr int score_wgs_per_cu(int mode, int nh) {
+  return mode == QLI_MODE_CONSUMER && nh == 32 ? 3 : 2;
+}
+
 template <int NH, int MODE, bool DBG, bool STREAM = true>
-__global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(KArgs a) {
-  __shared__ __attribute__((aligned(16))) int8_t tile[2][kChunk * 128];
-  __shared__ __attribute__((aligned(16))) uint16_t ksc[2][kChunk];
+__global__ __launch_bounds__(kScoreThreads, score_wgs_per_cu(MODE, NH)) void score_kernel(KArgs a) {
+  constexpr bool SINGLE_ONLY = MODE == QLI_MODE_CONSUMER;
+  constexpr int NTILE = SINGLE_ONLY ? 1 : 2;
+  constexpr int STAGE = SINGLE_ONLY ? key_stage_single(NH) : kKeyStage;
+  __shared__ __attribute__((aligned(16))) int8_t tile[NTILE][kChunk * 128];
+  __shared__ __attribute__((aligned(16))) uint16_t ksc[NTILE][kChunk];
   __shared__ __attribute__((aligned(16))) i32x4 qfr[NH / 32 * 256];
-  __shared__ uint32_t qml[NH / 2];
+  __shared__ uint32_t qml[NH / 2 + 1];
+  // single-only kernels: a key stage of their own (the combined kernel
+  // stages keys in its second K buffer)
+  __shared__ __attribute__((aligned(16))) uint32_t kstage[SINGLE_ONLY ? STAGE * kKeyEntry + 2 * STAGE : 4];
 
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
@@ -1457,11 +1504,17 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(KArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) seed[i] = kSeedBits;
   bool bad = false;
-  // consumer tokens are always single groups
-  if (MODE != QLI_MODE_CONSUMER && l == 0)
-    run_multi<NH, MODE, DBG>(a, L, cu, st.hi, tile, ksc, wave, lane, seed, bad);
-  else
-    run_single<NH, MODE, DBG, STREAM>(a, L, cu, st.hi, tile, ksc, qfr, qml, wave, lane, seed, bad);
+  if constexpr (SINGLE_ONLY) {
+    run_single<NH, MODE, DBG, STREAM, STAGE, !STREAM>(a, L, cu, st.hi, tile[0], ksc[0], kstage, qfr, qml,
+                                                      wave, lane, seed, bad);
+  } else {
+    uint32_t* stage = reinterpret_cast<uint32_t*>(tile[NTILE - 1]);
+    if (l == 0)
+      run_multi<NH, MODE, DBG>(a, L, cu, st.hi, tile, ksc, wave, lane, seed, bad);
+    else
+      run_single<NH, MODE, DBG, STREAM, STAGE, false>(a, L, cu, st.hi, tile[0], ksc[0], stage, qfr, qml,
+                                                      wave, lane, seed, bad);
+  }
   if (bad) raise_flag(a, QLI_DEV_BAD_PAGE);
 }
 
@@ -2178,7 +2231,7 @@ int launch(const qli_params* p, const WsLayout& w, void* stream, bool timed) {
   a.groups = reinterpret_cast<Group*>(ws + w.groups_off);  // [2][T]
   a.ustart = reinterpret_cast<int32_t*>(ws + w.ustart_off);
   a.wgs = reinterpret_cast<WgStart*>(ws + w.wgs_off);
-  a.score_grid = std::min(kMaxScoreWGs, std::max(2, 2 * cu_count()));
+  a.score_grid = std::min(kMaxScoreWGs, std::max(2, score_wgs_per_cu(p->mode, p->num_heads) * cu_count()));
   a.nxcd = xcd_count();
   a.slots = consumer ? reinterpret_cast<int32_t*>(ws + w.slots_off) : nullptr;
   a.srow = consumer ? reinterpret_cast<int32_t*>(ws + w.srow_off) : nullptr;
