@@ -33,9 +33,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, published (5.0 POP/s)
 KEY_BYTES = 130                # one 128-byte index-K row + its 2-byte FP16 scale
 # what roofline.achieved divides by (roofline.kernel_ms)
-DURATION_SOURCE = ("average duration per launch of roofline.kernel, from HIP events the library "
-                   "records around each launch on the launch stream, over `steps` calls run after "
-                   "the timed region (same process, same inputs)")
+DURATION_SOURCE = ("duration per call of roofline.kernel (its launches in one call summed), from HIP "
+                   "events the library records around each launch on the launch stream, averaged "
+                   "over `steps` calls run after the timed region (same process, same inputs)")
 
 
 def log(msg):
@@ -168,8 +168,10 @@ class Runner:
         return start.elapsed_time(stop) / steps, wall
 
     def kernel_ms(self, steps):
-        """Average duration per launch of each kernel (HIP events recorded by
-        the library around each launch, on the launch stream)."""
+        """Duration per call of each kernel (HIP events recorded by the
+        library around each launch, on the launch stream): the sum over the
+        call's launches of that kernel (one, except for slices and the
+        select's row-length classes), averaged over ``steps`` calls."""
         Q = self.Q
         Q.qli_timing_read(reset=True)
         Q.qli_timing_enable(True)
@@ -179,7 +181,8 @@ class Runner:
             ms, cnt = Q.qli_timing_read(reset=True)
         finally:
             Q.qli_timing_enable(False)
-        return {Q.KERNEL_NAMES[k]: ms[k] / cnt[k] for k in range(len(ms)) if cnt[k]}
+        self.launches = {Q.KERNEL_NAMES[k]: cnt[k] / steps for k in range(len(ms)) if cnt[k]}
+        return {Q.KERNEL_NAMES[k]: ms[k] / steps for k in range(len(ms)) if cnt[k]}
 
 
 def measure(pb, steps, warmup, copies=1, cand_sets=None, bound="hbm"):
@@ -204,11 +207,13 @@ def measure(pb, steps, warmup, copies=1, cand_sets=None, bound="hbm"):
                 "traffic_summary": summary,
                 "alg_ops_per_launch": ops, "kernel_ms": round(kms[kern], 5),
                 "duration_source": DURATION_SOURCE}
+    launches = run.launches
+    roof["launches_per_call"] = launches.get(kern, 1.0)
     del run
     import torch
     torch.cuda.empty_cache()
     return {"keys": keys, "ms_per_step": ms, "wall_s": wall, "kernels_ms": kms, "roofline": roof,
-            "keys_per_s": keys / (ms * 1e-3)}
+            "keys_per_s": keys / (ms * 1e-3), "launches_per_call": launches}
 
 
 def source_candidates(pb):

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define QLI_ABI_VERSION 3
+#define QLI_ABI_VERSION 4
 
 /* Status codes returned by the host entry points. */
 enum qli_status {
@@ -70,8 +70,8 @@ enum qli_status {
   QLI_ERR_UNSUPPORTED = 2, /* num_heads not 32/64, head_dim not 128, quant
                               mode not INT8, sizes past the documented caps */
   QLI_ERR_NO_SOURCE = 3,   /* consumer mode without incoming candidates */
-  QLI_ERR_WORKSPACE = 4,   /* workspace missing or smaller than
-                              qli_workspace_bytes() */
+  QLI_ERR_WORKSPACE = 4,   /* workspace missing, misaligned, or too small
+                              for a slice of one query token */
   QLI_ERR_HIP = 5,         /* a kernel launch failed */
   QLI_ERR_SCRATCH_LIMIT = 6 /* qli_score_topk_noalloc: the call needs more
                                than QLI_STATIC_SCRATCH_BYTES of scratch */
@@ -160,8 +160,12 @@ typedef struct qli_params {
   uint32_t* status_out; /* optional device word receiving QLI_DEV_* bits
                            (never cleared by the library) */
 
-  /* scratch (device), caller-allocated, >= qli_workspace_bytes(p) bytes,
-     256-B aligned */
+  /* scratch (device), caller-allocated, 256-B aligned.  The call runs in
+     slices of consecutive query tokens, each reusing the whole workspace,
+     and takes the largest slice that workspace_bytes holds: the size
+     qli_workspace_bytes(p) recommends runs the call in one slice when it
+     needs at most 4 GiB and in slices of at most 4 GiB otherwise; any size
+     holding a one-token slice is accepted (smaller: QLI_ERR_WORKSPACE). */
   void* workspace;
   size_t workspace_bytes;
 } qli_params;
@@ -173,9 +177,13 @@ int qli_abi_version(void);
  * before launching anything.  Reads no device memory. Returns a qli_status. */
 int qli_validate(const qli_params* p);
 
-/* Workspace bytes a call with these scalars needs (host-only; depends on
- * mode, ratio, num_tokens, max_k_len and cand_in_blocks).  0 when p is NULL
- * or when the scalars are invalid. */
+/* Recommended workspace bytes for a call with these scalars (host-only;
+ * depends on mode, ratio, num_tokens, max_k_len, cand_blocks and
+ * cand_in_blocks): the whole call when its workspace is at most 4 GiB,
+ * otherwise the largest token slice within 4 GiB (an 8192-token chunk at
+ * 1M raw context then needs 4 GiB instead of 17-34 GB).  A larger
+ * workspace lets a call run in fewer slices.  0 when p is NULL or when the
+ * scalars are invalid. */
 size_t qli_workspace_bytes(const qli_params* p);
 
 /* Enqueue the whole indexer on `stream` (a hipStream_t; NULL = the null
@@ -197,10 +205,10 @@ int qli_score_topk(const qli_params* p, void* stream);
  * scratch is the library's own static device array
  * (QLI_STATIC_SCRATCH_BYTES per GPU); p->workspace and p->workspace_bytes
  * are ignored.  Every other field, the validation and the outputs are those
- * of qli_score_topk.  A call whose workspace (qli_workspace_bytes) exceeds
- * the array returns QLI_ERR_SCRATCH_LIMIT before anything is launched;
- * decode-sized calls fit (64 tokens over 32768 positions in source mode
- * need 9.5 MB).  Nothing here allocates: the first call on a device looks
+ * of qli_score_topk.  The call runs in token slices that fit the array
+ * (decode-sized calls in one: 64 tokens over 32768 positions in source mode
+ * need 9.5 MB); a call whose one-token slice exceeds it returns
+ * QLI_ERR_SCRATCH_LIMIT before anything is launched.  Nothing here allocates: the first call on a device looks
  * the array up once (hipGetSymbolAddress), no hipMalloc/hipFree and no
  * timing events.  Every call on one GPU shares that GPU's array: calls that
  * overlap in time on one GPU (other streams, other threads) race and give

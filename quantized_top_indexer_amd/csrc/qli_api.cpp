@@ -38,7 +38,7 @@ int check_scalars(const qli_params* p) {
   if (p->s_page_stride < static_cast<int64_t>(p->page_rows) * 2 || p->s_page_stride % 16)
     return QLI_ERR_INVALID_ARG;
   // one workgroup per (token, 256-slot chunk) must fit a 31-bit grid
-  const qli::WsLayout w = qli::ws_layout(p);
+  const qli::WsLayout w = qli::ws_layout(p, p->num_tokens);
   if (static_cast<int64_t>(p->num_tokens) * (w.ncap / qli::kChunk) >= (int64_t(1) << 31))
     return QLI_ERR_UNSUPPORTED;
   return QLI_OK;
@@ -133,30 +133,31 @@ int qli_abi_version(void) { return QLI_ABI_VERSION; }
 int qli_validate(const qli_params* p) {
   const int rc = check_args(p);
   if (rc != QLI_OK || p->num_tokens == 0) return rc;
-  const qli::WsLayout w = qli::ws_layout(p);
-  if (w.total > 0 && (!p->workspace || !aligned(p->workspace, 256))) return QLI_ERR_WORKSPACE;
-  if (p->workspace_bytes < w.total) return QLI_ERR_WORKSPACE;
+  // the workspace must hold a slice of at least one token
+  if (!p->workspace || !aligned(p->workspace, 256)) return QLI_ERR_WORKSPACE;
+  if (qli::slice_layout(p, p->workspace_bytes).tokens < 1) return QLI_ERR_WORKSPACE;
   return QLI_OK;
 }
 
 size_t qli_workspace_bytes(const qli_params* p) {
   if (check_scalars(p) != QLI_OK) return 0;
-  return qli::ws_layout(p).total;
+  return qli::default_layout(p).total;
 }
 
 int qli_score_topk(const qli_params* p, void* stream) {
   int rc = qli_validate(p);
   if (rc != QLI_OK) return rc;
   if (p->num_tokens == 0) return QLI_OK;
-  return qli::launch(p, qli::ws_layout(p), stream, true);
+  return qli::launch(p, qli::slice_layout(p, p->workspace_bytes), stream, true);
 }
 
 int qli_score_topk_noalloc(const qli_params* p, void* stream) {
   int rc = check_args(p);
   if (rc != QLI_OK) return rc;
-  const qli::WsLayout w = qli::ws_layout(p);
-  if (w.total > QLI_STATIC_SCRATCH_BYTES) return QLI_ERR_SCRATCH_LIMIT;
   if (p->num_tokens == 0) return QLI_OK;
+  // slices of as many tokens as the static array holds
+  const qli::WsLayout w = qli::slice_layout(p, QLI_STATIC_SCRATCH_BYTES);
+  if (w.tokens < 1) return QLI_ERR_SCRATCH_LIMIT;
   void* scratch = nullptr;
   rc = qli::static_scratch(&scratch);
   if (rc != QLI_OK) return rc;

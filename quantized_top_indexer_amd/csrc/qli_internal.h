@@ -8,7 +8,9 @@
 
 namespace qli {
 
-// Carve-up of the caller's workspace.
+// Carve-up of the caller's workspace for slices of `tokens` query tokens
+// (T below): a call is processed slice by slice, each slice reusing the
+// whole workspace, so its size is bounded by the slice, not by the call.
 //   keys   [T, ncap]    u32 order-preserving score keys by slot (0 = not eligible)
 //   bkeys  [T, nbcap]   u32 block-max keys (source mode)
 //   plan   header (group counts, work units), groups [2][T] x 32 B, ustart [2][T+1]:
@@ -19,6 +21,7 @@ namespace qli {
 //   srow   [T, cand_in_blocks] page*page_rows + row of each slot block (consumer)
 //   ncount [T]          eligible positions per token (consumer)
 struct WsLayout {
+  int64_t tokens = 0;  // query tokens per slice
   int64_t ncap = 0;
   int64_t nbcap = 0;
   size_t keys_off = 0;
@@ -41,9 +44,14 @@ constexpr int kWgStartBytes = 64;
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-inline WsLayout ws_layout(const qli_params* p) {
+// Default budget of a slice's workspace: the call is cut into slices of as
+// many tokens as fit in it (at least one token per slice).
+constexpr int64_t kSliceBudgetBytes = int64_t(4) << 30;
+
+inline WsLayout ws_layout(const qli_params* p, int64_t slice_tokens) {
   WsLayout w;
-  const size_t T = static_cast<size_t>(p->num_tokens);
+  w.tokens = slice_tokens;
+  const size_t T = static_cast<size_t>(slice_tokens);
   if (p->mode == QLI_MODE_CONSUMER)
     w.ncap = static_cast<int64_t>(p->cand_in_blocks) * 8;
   else
@@ -81,8 +89,33 @@ inline WsLayout ws_layout(const qli_params* p) {
   return w;
 }
 
-// Enqueue the kernels (arguments already validated).  timed: record the
-// optional timing events (when the timing facility is on).
+// The layout of the largest slice (at most num_tokens, at least one token)
+// whose workspace fits in `bytes`; tokens = 0 when not even one token fits.
+inline WsLayout slice_layout(const qli_params* p, size_t bytes) {
+  const int64_t T = p->num_tokens;
+  if (T <= 0 || ws_layout(p, T).total <= bytes) return ws_layout(p, T > 0 ? T : 0);
+  if (ws_layout(p, 1).total > bytes) return WsLayout{};
+  int64_t lo = 1, hi = T;  // ws_layout(lo) fits, ws_layout(hi) does not
+  while (hi - lo > 1) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (ws_layout(p, mid).total <= bytes) lo = mid;
+    else hi = mid;
+  }
+  return ws_layout(p, lo);
+}
+
+// The workspace qli_workspace_bytes() recommends: the whole call when it
+// fits in kSliceBudgetBytes, otherwise the largest slice that does.
+inline WsLayout default_layout(const qli_params* p) {
+  const WsLayout full = ws_layout(p, p->num_tokens);
+  if (full.total <= static_cast<size_t>(kSliceBudgetBytes)) return full;
+  const WsLayout w = slice_layout(p, static_cast<size_t>(kSliceBudgetBytes));
+  return w.tokens > 0 ? w : ws_layout(p, 1);
+}
+
+// Enqueue the kernels (arguments already validated), slice by slice of
+// w.tokens query tokens.  timed: record the optional timing events (when
+// the timing facility is on).
 int launch(const qli_params* p, const WsLayout& w, void* stream, bool timed);
 
 // Device address of the library's static scratch array on the current

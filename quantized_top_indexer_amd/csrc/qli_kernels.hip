@@ -86,6 +86,11 @@ static_assert(sizeof(WgStart) == kWgStartBytes, "WgStart size");
 struct KArgs {
   float one;  // 1.0f
   int mode, ratio, rshift, B, T, topk, cb, cb_in, R, rlog, bt_stride, num_pages, max_k_len;
+  // A call runs in slices of consecutive query tokens: T tokens from global
+  // token t_base.  Workspace arrays are indexed by the local token (0..T);
+  // the per-token inputs and outputs below point at the slice's first
+  // token; the request metadata (qsl) keeps global token indices.
+  int t_base;
   int score_grid;
   int nxcd;            // XCDs of the device (accelerator dies, each with its own L2)
   int sel_lo, sel_hi;  // this select launch takes the rows whose length n has sel_lo <= n <= sel_hi
@@ -326,14 +331,14 @@ constexpr int kPrepBitmapThreads = 256; // lean bitmap preparation (up to 8 ids 
 constexpr int kPrepBitmapWords = 8192;  // bitmap of up to 2^18 block ids (32 KB of LDS)
 constexpr int kPrepLeanMinTokens = 1024;  // consumer batches this large plan in a launch of their own
 
-// The request holding token t, found by all threads at once (one round of
-// loads instead of a dependent binary search); every thread gets it.
+// The request holding global token tg, found by all threads at once (one
+// round of loads instead of a dependent binary search); every thread gets it.
 template <int PT>
-__device__ __forceinline__ int prep_request(const KArgs& a, int t, int* s_req) {
+__device__ __forceinline__ int prep_request(const KArgs& a, int tg, int* s_req) {
   if (threadIdx.x == 0) *s_req = 0;
   __syncthreads();
   for (int i = threadIdx.x; i < a.B; i += PT)
-    if (a.qsl[i] <= t && t < a.qsl[i + 1]) *s_req = i;
+    if (a.qsl[i] <= tg && tg < a.qsl[i + 1]) *s_req = i;
   __syncthreads();
   return *s_req;
 }
@@ -385,10 +390,11 @@ template <int PT>
 __device__ __forceinline__ void prep_bitmap_token(const KArgs& a, int t, uint32_t* bm, int32_t* sl,
                                                   uint32_t* sh, int* s_req) {
   const int tid = threadIdx.x;
-  const int b = prep_request<PT>(a, t, s_req);
+  const int tg = t + a.t_base;
+  const int b = prep_request<PT>(a, tg, s_req);
   const ReqView r = request_view(a, global_meta(a), b, tid == 0);
-  const int V = (t >= r.q0 && t < r.q1)
-                    ? visible(a, r.S - (r.q1 - r.q0) + (t - r.q0), r.L) : 0;
+  const int V = (tg >= r.q0 && tg < r.q1)
+                    ? visible(a, r.S - (r.q1 - r.q0) + (tg - r.q0), r.L) : 0;
   const int nblocks = (V + 7) / 8;
   const int nwords = (nblocks + 31) / 32;  // within the bitmap: V <= max_k_len (checked at launch)
   for (int i = tid; i < nwords; i += PT) bm[i] = 0;
@@ -452,11 +458,12 @@ __global__ __launch_bounds__(kPrepThreads) void consumer_prep_sort_kernel(KArgs 
   uint32_t* sh = lds + 2 * QLI_MAX_CAND_BLOCKS;
   int* s_req = reinterpret_cast<int*>(sh + 64);
   const int t = blockIdx.x - 1;
+  const int tg = t + a.t_base;
   const int tid = threadIdx.x;
-  const int b = prep_request<kPrepThreads>(a, t, s_req);
+  const int b = prep_request<kPrepThreads>(a, tg, s_req);
   const ReqView r = request_view(a, global_meta(a), b, tid == 0);
-  const int V = (t >= r.q0 && t < r.q1)
-                    ? visible(a, r.S - (r.q1 - r.q0) + (t - r.q0), r.L) : 0;
+  const int V = (tg >= r.q0 && tg < r.q1)
+                    ? visible(a, r.S - (r.q1 - r.q0) + (tg - r.q0), r.L) : 0;
   const int nblocks = (V + 7) / 8;
   const int cbi = a.cb_in;
   int n2 = 64;
@@ -506,24 +513,29 @@ __global__ __launch_bounds__(kPrepThreads) void consumer_prep_sort_kernel(KArgs 
 // ---------------------------------------------------------------------------
 constexpr int kPlanThreads = 1024;
 
-// 0: token t belongs to a multi group it does not start; 1: starts a multi
-// group; 2: forms a single group.
-__device__ __forceinline__ int group_kind(const KArgs& a, const ReqView& r, int t) {
+// 0: global token tg belongs to a multi group it does not start; 1: starts
+// a multi group; 2: forms a single group.  A quadruple that the slice
+// [t_base, t_base + T) cuts is scored as single tokens (same results).
+__device__ __forceinline__ int group_kind(const KArgs& a, const ReqView& r, int tg) {
   if (a.mode == QLI_MODE_CONSUMER) return 2;
-  const int i = t - r.q0;
+  const int i = tg - r.q0;
   const int full = (r.q1 - r.q0) / kGroupTokens * kGroupTokens;
-  if (i < full) return i % kGroupTokens == 0 ? 1 : 0;
+  if (i < full) {
+    const int g0 = tg - i % kGroupTokens;  // the quadruple's first token
+    if (g0 >= a.t_base && g0 + kGroupTokens <= a.t_base + a.T) return tg == g0 ? 1 : 0;
+  }
   return 2;
 }
 
-__device__ __forceinline__ Group make_group(const KArgs& a, int b, const ReqView& r, int t,
+// Group of ntok tokens starting at local token t (global tg).
+__device__ __forceinline__ Group make_group(const KArgs& a, int b, const ReqView& r, int t, int tg,
                                             int ntok) {
   Group g;
   g.t0 = t;
   g.ntok = ntok;
   g.b = b;
   g.L = r.L;
-  const int64_t p0 = r.S - (r.q1 - r.q0) + (t - r.q0);
+  const int64_t p0 = r.S - (r.q1 - r.q0) + (tg - r.q0);
   g.p0 = static_cast<int>(p0);
   if (a.mode == QLI_MODE_CONSUMER) {
     // a bound on the eligible slots (the prepared count may not exist yet):
@@ -650,15 +662,16 @@ __device__ __forceinline__ void plan_body(const KArgs& a, const Meta& m, uint32_
   int kind1 = 0, tv1 = 0;
   Group g1c{};
   if (t_lo < t_hi) {
-    int b = request_of(m, a.B, t_lo);
+    int b = request_of(m, a.B, t_lo + a.t_base);
     ReqView r = request_view(a, m, b, true);
     for (int t = t_lo; t < t_hi; ++t) {
-      while (t >= r.q1 && b + 1 < a.B) r = request_view(a, m, ++b, true);
-      if (t < r.q0 || t >= r.q1) continue;
-      if (per == 1) tv1 = visible(a, r.S - (r.q1 - r.q0) + (t - r.q0), r.L);
-      const int kind = group_kind(a, r, t);
+      const int tg = t + a.t_base;
+      while (tg >= r.q1 && b + 1 < a.B) r = request_view(a, m, ++b, true);
+      if (tg < r.q0 || tg >= r.q1) continue;
+      if (per == 1) tv1 = visible(a, r.S - (r.q1 - r.q0) + (tg - r.q0), r.L);
+      const int kind = group_kind(a, r, tg);
       if (kind == 0) continue;
-      const Group g = make_group(a, b, r, t, kind == 1 ? kGroupTokens : 1);
+      const Group g = make_group(a, b, r, t, tg, kind == 1 ? kGroupTokens : 1);
       if (per == 1) {
         kind1 = kind;
         g1c = g;
@@ -705,17 +718,18 @@ __device__ __forceinline__ void plan_body(const KArgs& a, const Meta& m, uint32_
   } else if (t_lo < t_hi) {
     // running group index and first unit of list 0, then of list 1
     uint32_t g0 = cnt[0], u0 = cnt[1], g1 = cnt[2], u1 = cnt[3];
-    int b = request_of(m, a.B, t_lo);
+    int b = request_of(m, a.B, t_lo + a.t_base);
     ReqView r = request_view(a, m, b, false);
     for (int t = t_lo; t < t_hi; ++t) {
-      while (t >= r.q1 && b + 1 < a.B) r = request_view(a, m, ++b, false);
-      const bool in = t >= r.q0 && t < r.q1;
-      a.tokv[t] = in ? visible(a, r.S - (r.q1 - r.q0) + (t - r.q0), r.L) : 0;
+      const int tg = t + a.t_base;
+      while (tg >= r.q1 && b + 1 < a.B) r = request_view(a, m, ++b, false);
+      const bool in = tg >= r.q0 && tg < r.q1;
+      a.tokv[t] = in ? visible(a, r.S - (r.q1 - r.q0) + (tg - r.q0), r.L) : 0;
       if (!in) continue;
-      const int kind = group_kind(a, r, t);
+      const int kind = group_kind(a, r, tg);
       if (kind == 0) continue;
       const int l = kind - 1;
-      const Group g = make_group(a, b, r, t, kind == 1 ? kGroupTokens : 1);
+      const Group g = make_group(a, b, r, t, tg, kind == 1 ? kGroupTokens : 1);
       const uint32_t gi = l == 0 ? g0 : g1, ui = l == 0 ? u0 : u1;
       a.groups[l * T + gi] = g;
       a.ustart[l * (T + 1) + gi] = static_cast<int32_t>(ui);
@@ -2185,6 +2199,9 @@ void launch_score(int heads, int mode, bool dbg, bool cached, unsigned grid, hip
   else launch_score_mode<32>(mode, dbg, cached, grid, st, a);
 }
 
+void launch_slice(const qli_params* p, const WsLayout& w, KArgs a, bool cached, hipStream_t st,
+                  bool timed);
+
 int launch(const qli_params* p, const WsLayout& w, void* stream, bool timed) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // an earlier failure elsewhere on this thread is not ours to report
@@ -2194,7 +2211,6 @@ int launch(const qli_params* p, const WsLayout& w, void* stream, bool timed) {
   a.ratio = p->ratio;
   a.rshift = p->ratio == 2 ? 1 : 0;
   a.B = p->batch;
-  a.T = p->num_tokens;
   a.topk = p->topk;
   a.cb = p->cand_blocks;
   a.cb_in = p->cand_in_blocks;
@@ -2207,20 +2223,12 @@ int launch(const qli_params* p, const WsLayout& w, void* stream, bool timed) {
   a.sstride = p->s_page_stride;
   a.ncap = w.ncap;
   a.nbcap = w.nbcap;
-  a.q = p->q;
-  a.qs = p->q_scale;
-  a.w = p->weights;
   a.k = p->k_cache;
   a.ks = static_cast<const uint8_t*>(p->k_scale);
   a.bt = p->block_table;
   a.qsl = p->query_start_loc;
   a.klen = p->k_lens;
   a.smod = p->seq_mod;
-  a.cand_in = p->cand_in;
-  a.topk_out = p->topk_out;
-  a.cand_out = p->cand_out;
-  a.dbg = p->dbg_scores;
-  a.dbg_qk = p->dbg_qk;
   a.status = p->status_out;
   char* ws = static_cast<char*>(p->workspace);
   const bool consumer = p->mode == QLI_MODE_CONSUMER;
@@ -2238,7 +2246,32 @@ int launch(const qli_params* p, const WsLayout& w, void* stream, bool timed) {
   a.ncount = consumer ? reinterpret_cast<int32_t*>(ws + w.ncount_off) : nullptr;
   a.tokv = reinterpret_cast<int32_t*>(ws + w.tokv_off);
 
-  const unsigned T = static_cast<unsigned>(p->num_tokens);
+  // some request holds several query tokens (consumer mode: each reads its
+  // own candidate rows of the request's K, so the rows are read repeatedly)
+  const bool cached = p->num_tokens > p->batch;
+  const int64_t NH = p->num_heads;
+  for (int64_t t0 = 0; t0 < p->num_tokens; t0 += w.tokens) {
+    a.t_base = static_cast<int>(t0);
+    a.T = static_cast<int>(std::min<int64_t>(w.tokens, p->num_tokens - t0));
+    a.q = p->q + t0 * NH * 128;
+    a.qs = p->q_scale + t0 * NH;
+    a.w = p->weights + t0 * NH;
+    a.cand_in = p->cand_in ? p->cand_in + t0 * p->cand_in_blocks : nullptr;
+    a.topk_out = p->topk_out + t0 * p->topk;
+    a.cand_out = p->cand_out ? p->cand_out + t0 * p->cand_blocks : nullptr;
+    a.dbg = p->dbg_scores ? p->dbg_scores + t0 * p->max_k_len : nullptr;
+    a.dbg_qk = p->dbg_qk ? p->dbg_qk + t0 * NH * p->max_k_len : nullptr;
+    launch_slice(p, w, a, cached, st, timed);
+  }
+  return hipGetLastError() == hipSuccess ? QLI_OK : QLI_ERR_HIP;
+}
+
+// The kernels of one slice (a.T tokens from a.t_base).
+void launch_slice(const qli_params* p, const WsLayout& w, KArgs a, bool cached, hipStream_t st,
+                  bool timed) {
+  const bool consumer = p->mode == QLI_MODE_CONSUMER;
+  const bool source = p->mode == QLI_MODE_SOURCE;
+  const unsigned T = static_cast<unsigned>(a.T);
   const int64_t max_blocks = (static_cast<int64_t>(p->max_k_len) + 7) / 8;
   const bool bitmap = max_blocks <= 32 * static_cast<int64_t>(kPrepBitmapWords);
   if (consumer && bitmap && T >= static_cast<unsigned>(kPrepLeanMinTokens)) {
@@ -2261,14 +2294,11 @@ int launch(const qli_params* p, const WsLayout& w, void* stream, bool timed) {
   } else {
     Stamp s(QLI_KERNEL_PLAN, st, timed);
     // a decode-sized batch is planned by one wave
-    if (p->num_tokens <= 64 && p->batch <= 256) plan_kernel<64><<<1, 64, 0, st>>>(a);
+    if (a.T <= 64 && p->batch <= 256) plan_kernel<64><<<1, 64, 0, st>>>(a);
     else plan_kernel<kPlanThreads><<<1, kPlanThreads, 0, st>>>(a);
   }
   if (w.ncap > 0) {
     Stamp s(QLI_KERNEL_SCORE, st, timed);
-    // some request holds several query tokens (consumer mode: each reads its
-    // own candidate rows of the request's K, so the rows are read repeatedly)
-    const bool cached = p->num_tokens > p->batch;
     launch_score(p->num_heads, p->mode, p->dbg_scores != nullptr, cached, static_cast<unsigned>(a.score_grid),
                  st, a);
   }
@@ -2313,7 +2343,6 @@ int launch(const qli_params* p, const WsLayout& w, void* stream, bool timed) {
     else if (longest <= sel_chunk(1024)) select_kernel<1024, false><<<grid, 1024, 0, st>>>(a);
     else select_kernel<1024, true><<<grid, 1024, 0, st>>>(a);
   }
-  return hipGetLastError() == hipSuccess ? QLI_OK : QLI_ERR_HIP;
 }
 
 }  // namespace qli

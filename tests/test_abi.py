@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert Q.qli_abi_version() == 3
+    assert Q.qli_abi_version() == 4
 
 
 @pytest.mark.parametrize("struct", ["qli_params", "qli_quant_params", "qli_kwrite_params"])
@@ -306,12 +306,60 @@ def test_noalloc_rejections(lib):
         bad = base_params(mode=2, ratio=2)
         setattr(bad, field, value)
         assert lib.qli_score_topk_noalloc(C.byref(bad), None) == Q.qli_validate(bad) != Q.QLI_OK
-    p.num_tokens = 40000                              # 40000 x 256 key slots x 4 B > 32 MiB
+    # the call runs in slices of as many tokens as the array holds; only a
+    # single token that does not fit is rejected: 2^24 positions need 64 MiB
+    # of keys per token
+    p.max_k_len, p.bt_stride = 1 << 24, (1 << 24) // 64
     assert Q.qli_workspace_bytes(p) > Q.QLI_STATIC_SCRATCH_BYTES
     assert lib.qli_score_topk_noalloc(C.byref(p), None) == Q.QLI_ERR_SCRATCH_LIMIT
     assert "static scratch" in Q.qli_status_string(Q.QLI_ERR_SCRATCH_LIMIT)
     p.num_tokens = 0                                  # a no-op, nothing looked up
     assert lib.qli_score_topk_noalloc(C.byref(p), None) == Q.QLI_OK
+
+
+def long_prefill_params(ratio=2, mode=2, T=8192):
+    """An 8192-token chunk at 1M raw context (524288 compressed positions at
+    ratio 2), fake pointers."""
+    p = base_params(mode=mode, ratio=ratio, T=T)
+    p.num_heads = 64
+    p.max_k_len = (1 << 20) // ratio
+    p.bt_stride = p.max_k_len // p.page_rows
+    p.topk, p.cand_blocks, p.cand_in_blocks = 2048, 2048, 2048
+    return p
+
+
+@pytest.mark.parametrize("ratio,mode", [(2, 2), (1, 2), (2, 1), (2, 3)])
+def test_workspace_bounded_by_slices(lib, ratio, mode):
+    """Long-context prefill calls run in token slices that reuse one bounded
+    workspace: the recommended size stays within the 4 GiB slice budget
+    instead of growing with tokens x context (17-34 GB unsliced), a
+    workspace of one token's slice is accepted, and anything smaller is
+    rejected before any launch."""
+    p = long_prefill_params(ratio, mode)
+    need = Q.qli_workspace_bytes(p)
+    per_token = p.max_k_len * 4 if mode != 3 else 2048 * 8 * 4
+    if mode != 3:
+        assert p.num_tokens * per_token > 16e9       # what an unsliced call would need
+        assert need <= (4 << 30)
+        assert need >= (4 << 30) - 2 * (per_token + (p.max_k_len // 8) * 4)
+    p.workspace, p.workspace_bytes = 0x7F0000000000, need
+    assert Q.qli_validate(p) == Q.QLI_OK
+    one = base_params(mode=mode, ratio=ratio, T=1)     # same scalars, one token
+    for f in ("num_heads", "max_k_len", "bt_stride", "topk", "cand_blocks", "cand_in_blocks"):
+        setattr(one, f, getattr(p, f))
+    p.workspace_bytes = Q.qli_workspace_bytes(one)
+    assert Q.qli_validate(p) == Q.QLI_OK
+    p.workspace_bytes -= 256
+    assert Q.qli_validate(p) == Q.QLI_ERR_WORKSPACE
+
+
+def test_workspace_unsliced_when_it_fits(lib):
+    """Calls within the budget get the whole-call workspace (one slice):
+    doubling the tokens of a small call doubles its token-indexed parts."""
+    p = base_params(mode=2, ratio=2, T=100)
+    q = base_params(mode=2, ratio=2, T=200)
+    a, b = Q.qli_workspace_bytes(p), Q.qli_workspace_bytes(q)
+    assert b > a and b - a >= 100 * (256 + 64) * 4
 
 
 def test_debug_qk_alignment(lib):

@@ -442,3 +442,46 @@ def test_select_length_classes(mode, policy):
     tok = sample_tokens(pb, 12, seed=pb.seed, include=include)
     orc = oracle_rows(pb, tokens=tok, scores=False)
     compare(pb, gpu, orc, tokens=tok, scores=False)
+
+
+@pytest.mark.parametrize("mode,ratio,N,slice_tokens", [(2, 2, 32, 3), (1, 1, 64, 5), (3, 2, 32, 2),
+                                                       (2, 1, 64, 7)])
+def test_sliced_workspace(mode, ratio, N, slice_tokens):
+    """A workspace that holds a slice of only a few tokens: the call runs
+    slice by slice (4-token groups cut by a slice boundary are scored as
+    single tokens) and gives the oracle's outputs and scores bit for bit,
+    the same as the unsliced call."""
+    import torch
+
+    import quantized_top_indexer_amd as Q
+    from qli_workloads.device import call_kwargs, to_device
+    pb = small_problem(370 + mode + ratio + N, ratio=ratio, N=N, mode=mode, topk=120, cb=64, cb_in=128,
+                       requests=((9, 3000), (5, 1100), (1, 1), (6, 2049), (2, 40)))
+    say(f"sliced {pb.name}: T={pb.num_tokens} L={pb.max_k_len} slice={slice_tokens}")
+    whole = run_gpu(pb, debug=True)
+    dev = to_device(pb, "cuda")
+    kw = call_kwargs(pb, dev)
+    T = pb.num_tokens
+    shp_i, shp_c = Q.output_shapes(T, pb.topk, pb.cand_blocks, pb.mode)
+    topk = torch.full(shp_i, -7, dtype=torch.int32, device="cuda")
+    cand = torch.full(shp_c, -7, dtype=torch.int32, device="cuda") if shp_c else None
+    dbg = torch.full((T, pb.max_k_len), float("nan"), dtype=torch.float32, device="cuda")
+    args = {k: v for k, v in kw.items() if k != "cand_blocks"}
+    p = Q.make_params(**args, cand_blocks=pb.cand_blocks, topk_out=topk, cand_out=cand, dbg_scores=dbg)
+    p.num_tokens = slice_tokens
+    small = Q.qli_workspace_bytes(p)          # the layout of a slice of that many tokens
+    p.num_tokens = T
+    assert small < Q.qli_workspace_bytes(p)
+    ws = torch.empty(small, dtype=torch.uint8, device="cuda")
+    p.workspace, p.workspace_bytes = ws.data_ptr(), small
+    rc = Q.qli_score_topk(p)
+    assert rc == Q.QLI_OK, Q.qli_status_string(rc)
+    torch.cuda.synchronize()
+    got = {"topk": topk[:, 0].cpu().numpy(), "cand": None if cand is None else cand[:, 0].cpu().numpy(),
+           "scores": dbg.cpu().numpy()}
+    assert np.array_equal(got["topk"], whole["topk"])
+    if mode == 2:
+        assert np.array_equal(got["cand"], whole["cand"])
+    assert np.array_equal(got["scores"], whole["scores"], equal_nan=True)
+    compare(pb, got, oracle_rows(pb, scores=True))
+    check_invariants(pb, got)
