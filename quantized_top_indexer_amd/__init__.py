@@ -74,9 +74,12 @@ class qli_kwrite_params(C.Structure):
 
 
 EXPORTS = ("qli_abi_version", "qli_validate", "qli_workspace_bytes", "qli_score_topk",
-           "qli_score_topk_noalloc", "qli_status_string", "qli_timing_enable", "qli_timing_read", "qli_quantize_query",
-           "qli_write_index_k", "qli_probe_hbm_read", "qli_probe_int8_mfma",
-           "qli_probe_int8_mfma_ops")
+           "qli_score_topk_noalloc", "qli_status_string", "qli_timing_enable", "qli_timing_read",
+           "qli_quantize_query", "qli_write_index_k")
+# the ceiling probes (include/qli_probe.h): a library of their own, for
+# measurement only
+PROBE_LIB_PATH = os.path.join(_HERE, "libqli_probe.so")
+PROBE_EXPORTS = ("qli_probe_hbm_read", "qli_probe_int8_mfma", "qli_probe_int8_mfma_ops")
 QLI_KERNEL_CONSUMER_PREP, QLI_KERNEL_PLAN, QLI_KERNEL_SCORE, QLI_KERNEL_SELECT, \
     QLI_KERNEL_QUANTIZE, QLI_KERNEL_WRITE_K, QLI_NUM_KERNELS = range(7)
 KERNEL_NAMES = ("consumer_prep_kernel", "plan_kernel", "score_kernel", "select_kernel",
@@ -118,15 +121,30 @@ def load_library(path: str = LIB_PATH):
     L.qli_quantize_query.argtypes = [C.POINTER(qli_quant_params), C.c_void_p]
     L.qli_write_index_k.restype = C.c_int
     L.qli_write_index_k.argtypes = [C.POINTER(qli_kwrite_params), C.c_void_p]
-    L.qli_probe_hbm_read.restype = C.c_int
-    L.qli_probe_hbm_read.argtypes = [C.c_void_p, C.c_size_t, C.c_int, C.c_void_p, C.c_void_p]
-    L.qli_probe_int8_mfma.restype = C.c_int
-    L.qli_probe_int8_mfma.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p]
-    L.qli_probe_int8_mfma_ops.restype = C.c_double
-    L.qli_probe_int8_mfma_ops.argtypes = [C.c_int, C.c_int]
     if path == LIB_PATH:
         _lib = L
     return L
+
+
+_probe_lib = None
+
+
+def load_probe_library():
+    """Load libqli_probe.so, the measured-ceiling probes (raises if not built)."""
+    global _probe_lib
+    if _probe_lib is None:
+        if not os.path.exists(PROBE_LIB_PATH):
+            raise RuntimeError(f"probe library not built ({PROBE_LIB_PATH}); run __graft_entry__.build()")
+        import torch  # noqa: F401  (one HIP runtime: torch's)
+        L = C.CDLL(PROBE_LIB_PATH)
+        L.qli_probe_hbm_read.restype = C.c_int
+        L.qli_probe_hbm_read.argtypes = [C.c_void_p, C.c_size_t, C.c_int, C.c_void_p, C.c_void_p]
+        L.qli_probe_int8_mfma.restype = C.c_int
+        L.qli_probe_int8_mfma.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p]
+        L.qli_probe_int8_mfma_ops.restype = C.c_double
+        L.qli_probe_int8_mfma_ops.argtypes = [C.c_int, C.c_int]
+        _probe_lib = L
+    return _probe_lib
 
 
 def qli_abi_version() -> int:
@@ -175,17 +193,18 @@ def qli_write_index_k(p: qli_kwrite_params, stream=None) -> int:
 
 def qli_probe_hbm_read(buf, nbytes: int, grid: int, sink, stream=None) -> int:
     """Enqueue the streaming-read ceiling probe (include/qli_probe.h)."""
-    return load_library().qli_probe_hbm_read(C.c_void_p(buf), C.c_size_t(nbytes), grid,
+    return load_probe_library().qli_probe_hbm_read(C.c_void_p(buf), C.c_size_t(nbytes), grid,
                                              C.c_void_p(sink), _stream(stream))
 
 
 def qli_probe_int8_mfma(grid: int, iterations: int, sink, stream=None) -> int:
     """Enqueue the INT8 MFMA ceiling probe (include/qli_probe.h)."""
-    return load_library().qli_probe_int8_mfma(grid, iterations, C.c_void_p(sink), _stream(stream))
+    return load_probe_library().qli_probe_int8_mfma(grid, iterations, C.c_void_p(sink),
+                                                    _stream(stream))
 
 
 def qli_probe_int8_mfma_ops(grid: int, iterations: int) -> float:
-    return load_library().qli_probe_int8_mfma_ops(grid, iterations)
+    return load_probe_library().qli_probe_int8_mfma_ops(grid, iterations)
 
 
 def _dtype_code(t):

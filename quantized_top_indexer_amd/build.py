@@ -11,7 +11,10 @@ OUT = os.path.join(HERE, "libqli.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = [os.path.join(CSRC, "qli_api.cpp"), os.path.join(CSRC, "qli_kernels.hip"),
-           os.path.join(CSRC, "qli_quant.hip"), os.path.join(CSRC, "qli_probe.hip")]
+           os.path.join(CSRC, "qli_quant.hip")]
+# the ceiling probes (measurement only) are a library of their own
+PROBE_SOURCES = [os.path.join(CSRC, "qli_probe.hip")]
+PROBE_OUT = os.path.join(HERE, "libqli_probe.so")
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -23,16 +26,22 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into quantized_top_indexer_amd/libqli.so."""
-    tmp = OUT + ".tmp"
-    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+def _compile(sources, out, verbose):
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *sources, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     if verbose:
         print(r.stderr)
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the indexer into quantized_top_indexer_amd/libqli.so and the
+    ceiling probes into libqli_probe.so."""
+    _compile(SOURCES, OUT, verbose)
+    _compile(PROBE_SOURCES, PROBE_OUT, verbose)
     return OUT
 
 

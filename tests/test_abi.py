@@ -23,21 +23,33 @@ def lib():
     return Q.load_library()
 
 
-def declared_functions():
-    src = open(HEADER).read() + open(os.path.join(ROOT, "include", "qli_probe.h")).read()
+def declared_functions(header=HEADER):
+    src = open(header).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(qli_\w+)\s*\(", src, flags=re.M)
+
+
+def exported(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True,
+                         text=True, check=True).stdout
+    return set(re.findall(r" T (qli_\w+)$", out, flags=re.M))
 
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == set(Q.EXPORTS)
-    out = subprocess.run(["nm", "-D", "--defined-only", Q.LIB_PATH], capture_output=True,
-                         text=True, check=True).stdout
-    exported = set(re.findall(r" T (qli_\w+)$", out, flags=re.M))
-    assert set(names) <= exported
+    assert set(names) <= exported(Q.LIB_PATH)
     for n in names:
         assert hasattr(lib, n)
+
+
+def test_probes_live_in_their_own_library(lib):
+    """The ceiling probes (measurement only) are not part of the indexer
+    library: libqli_probe.so exports what include/qli_probe.h declares."""
+    names = declared_functions(os.path.join(ROOT, "include", "qli_probe.h"))
+    assert set(names) == set(Q.PROBE_EXPORTS)
+    assert set(names) <= exported(Q.PROBE_LIB_PATH)
+    assert not (set(names) & exported(Q.LIB_PATH))
 
 
 def test_abi_version(lib):
