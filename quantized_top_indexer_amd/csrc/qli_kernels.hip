@@ -91,7 +91,11 @@ struct KArgs {
   // the per-token inputs and outputs below point at the slice's first
   // token; the request metadata (qsl) keeps global token indices.
   int t_base;
-  int score_grid;
+  int score_grid;      // workgroups of the score kernel that walks the single list (all lists
+                       // when multi_grid == 0)
+  int multi_grid;      // > 0: the multi list runs in a kernel of its own with this many
+                       // workgroups, whose start entries come first
+  int entry_base;      // first start entry of the launched score kernel
   int nxcd;            // XCDs of the device (accelerator dies, each with its own L2)
   int sel_lo, sel_hi;  // this select launch takes the rows whose length n has sel_lo <= n <= sel_hi
   int64_t kstride, sstride, ncap, nbcap;
@@ -688,8 +692,11 @@ __device__ __forceinline__ void plan_body(const KArgs& a, const Meta& m, uint32_
   }
   uint32_t tot[4];
   block_exclusive_scan_n<PT, 4>(cnt, tot, sh);  // also orders the clears below
-  const int W = a.score_grid;
-  const int Wm = multi_workgroups(W, static_cast<int>(tot[1]), static_cast<int>(tot[3]));
+  // one grid shared by the lists in proportion to their units, or (when the
+  // multi list has a kernel of its own) one grid per list
+  const int W = a.multi_grid > 0 ? a.multi_grid + a.score_grid : a.score_grid;
+  const int Wm = a.multi_grid > 0 ? a.multi_grid
+                                  : multi_workgroups(W, static_cast<int>(tot[1]), static_cast<int>(tot[3]));
   auto split = [&](int l) {
     Split sp;
     sp.list = l;
@@ -768,7 +775,7 @@ __device__ void plan_role(const KArgs& a, uint32_t* lds) {
   // every start entry begins as "no work" (the barriers below order these
   // stores before the ones the plan writes); workgroups whose range starts
   // past the last item of their list keep it
-  for (int w = tid; w < a.score_grid; w += PT) {
+  for (int w = tid; w < a.multi_grid + a.score_grid; w += PT) {
     WgStart st = {};
     st.g = -1;
     a.wgs[w] = st;
@@ -1345,6 +1352,204 @@ __device__ void run_multi(const KArgs& a, const ListView& L, Cursor cur, int hi,
   }
 }
 
+// The dispatcher hands workgroup i to XCD i mod nxcd, and each XCD has its
+// own L2.  The plan splits the work lists into contiguous ranges in token
+// order (the tokens of a request are neighbours), so workgroup i takes
+// start entry (i mod nxcd) * (grid / nxcd) + i / nxcd: every XCD walks one
+// contiguous stretch of the lists, and the tokens of a request that read
+// the same K rows share an L2 instead of fetching them through all of them.
+__device__ __forceinline__ int start_entry(int i, int grid, int nxcd) {
+  if (nxcd <= 1 || grid % nxcd) return i;
+  return (i % nxcd) * (grid / nxcd) + i / nxcd;
+}
+
+// ---------------------------------------------------------------------------
+// Multi groups at three or four workgroups per CU (prefill shapes)
+// ---------------------------------------------------------------------------
+// Each 256-slot item is scored as two 128-slot halves through a two-buffer
+// LDS ring of 16 KB halves.  K rows go straight from global memory into the
+// ring (global_load_lds, 1 KB per instruction, the tile swizzle applied on
+// the global side), so no K data waits in registers; one accumulator set
+// per wave.  That fits 168 VGPRs and 33 KB of LDS per workgroup: three
+// workgroups per CU (four with 32 heads), the extra waves per SIMD taking
+// over the overlap of matrix and vector work that two accumulator sets gave
+// one wave.
+// Each half: the block-table lookup of the half after next, the loads of
+// the next half, then the scoring of this one; at its end every wave waits
+// for its loads (the compiler does not order LDS reads after these loads,
+// so the wait is explicit) and the workgroup meets at one barrier.
+constexpr int kHalf = kChunk / 2;  // slots per half item
+
+// A half item: item cursor + which half.
+struct HalfCursor {
+  Cursor cu;
+  int h;
+};
+
+__device__ __forceinline__ HalfCursor next_half(const ListView& L, HalfCursor x, int hi) {
+  if (!x.cu.valid) return x;
+  if (x.h == 0) {
+    x.h = 1;
+    return x;
+  }
+  x.cu = next_item(L, x.cu, hi);
+  x.h = 0;
+  return x;
+}
+
+// Wave w stages rows [32w, 32w + 32) of a half (blocks 4w..4w+3, one page
+// at both ratios).  The lookup of that page (one block-table entry per wave).
+struct HalfAddr {
+  int raw;   // loaded block-table entry
+  int pos0;  // first position of the wave's 32 rows
+  bool idx_ok, want;
+};
+
+__device__ __forceinline__ void half_addr(const KArgs& a, const HalfCursor& x, int wave, HalfAddr& ad) {
+  const Group& g = x.cu.grp;
+  ad.pos0 = x.cu.c * kChunk + x.h * kHalf + 32 * wave;
+  const int idx = ad.pos0 >> a.rlog;
+  ad.idx_ok = idx < a.bt_stride;
+  ad.want = x.cu.valid && ad.pos0 < g.nlast;
+  ad.raw = a.bt[static_cast<int64_t>(g.b) * a.bt_stride + min(idx, a.bt_stride - 1)];
+}
+
+// page * page_rows + row of the wave's first row, or -1 (no K rows: the
+// loads then read page 0, which always exists, and the scales mark the
+// blocks as not eligible).
+__device__ __forceinline__ int half_resolve(const KArgs& a, const HalfCursor& x, const HalfAddr& ad,
+                                            bool& bad) {
+  if (!ad.want) return -1;
+  const bool ok = ad.idx_ok && ad.raw >= 0 && ad.raw < a.num_pages;
+  if (!ok) {  // rare: mark every token of the group
+    bad = true;
+    if ((threadIdx.x & 63) == 0)
+      for (int i = 0; i < x.cu.grp.ntok; ++i) atomicOr(&a.tokv[x.cu.grp.t0 + i], kTokBad);
+    return -1;
+  }
+  return ad.raw * a.R + (ad.pos0 & (a.R - 1));
+}
+
+// Loads of the wave's 32 rows into the half tile (4 x 1 KB, straight into
+// LDS) and, in lanes 0..3, the scales of its 4 blocks into sc.
+__device__ __forceinline__ void half_stage(const KArgs& a, int v, int wave, int lane, int8_t* tile,
+                                           i32x4& sc) {
+  const int row = v < 0 ? 0 : v;
+  const int8_t* base = a.k + static_cast<int64_t>(row >> a.rlog) * a.kstride +
+                       static_cast<int64_t>(row & (a.R - 1)) * 128;
+  // the scales first: they are read from registers before the half is scored
+  sc = *reinterpret_cast<const i32x4*>(a.ks + static_cast<int64_t>(row >> a.rlog) * a.sstride +
+                                       static_cast<int64_t>((row & (a.R - 1)) + 8 * (lane & 3)) * 2);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = 32 * wave + 8 * u + (lane >> 3);  // tile row
+    const int gcol = (lane & 7) ^ ((r >> 1) & 7);   // the column group LDS slot (lane & 7) holds
+    const int8_t* src = base + (8 * u + (lane >> 3)) * 128 + gcol * 16;
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(tile + (32 * wave + 8 * u) * 128),
+                                     16, 0, 0);
+  }
+}
+
+template <int NH, int MODE, bool DBG>
+__device__ void run_multi_half(const KArgs& a, const ListView& L, Cursor cur0, int hi,
+                               int8_t (*tile)[kHalf * 128], uint16_t (*ksc)[kHalf], int wave, int lane,
+                               const i32x16& seed, bool& bad) {
+  constexpr int P = NH / 32;  // passes per sub-tile
+  HalfCursor cur{cur0, 0};
+  HalfCursor n1 = next_half(L, cur, hi);
+  HalfAddr ad;
+  i32x4 sc;
+  auto store_scales = [&](int b, int v, int wave_, const HalfCursor& x) {
+    // block 4 wave + lane of the half: eligible rows start below nlast
+    if (lane < 4) {
+      const bool ok = v >= 0 && x.cu.c * kChunk + x.h * kHalf + 32 * wave_ + 8 * lane < x.cu.grp.nlast;
+      const i32x4 none = {-1, -1, -1, -1};
+      *reinterpret_cast<i32x4*>(ksc[b] + 8 * (4 * wave_ + lane)) = ok ? sc : none;
+    }
+  };
+  // prologue: half 0 into buffer 0
+  half_addr(a, cur, wave, ad);
+  int v = half_resolve(a, cur, ad, bad);
+  half_stage(a, v, wave, lane, tile[0], sc);
+  half_addr(a, n1, wave, ad);  // lookup of half 1
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  store_scales(0, v, wave, cur);
+  __syncthreads();
+  QState<NH, true> qs;
+  qs.tok = -1;
+  int buf = 0;
+  const float one = a.one;
+  while (cur.cu.valid) {
+    const HalfCursor n2 = next_half(L, n1, hi);
+    // half n1 into the other buffer (its lookup completed at the last wait)
+    const int v1 = half_resolve(a, n1, ad, bad);
+    if (n1.cu.valid) half_stage(a, v1, wave, lane, tile[buf ^ 1], sc);
+    half_addr(a, n2, wave, ad);  // lookup of the half after next
+    const Group& gr = cur.cu.grp;
+    const int t = gr.t0 + wave;
+    const int n_i = visible(a, static_cast<int64_t>(gr.p0) + wave, gr.L);
+    if (t != qs.tok) load_q<NH, true>(a, t, lane, qs);
+    const QRegs<NH, true> q{qs};
+    const int8_t* tl = tile[buf];
+    const int s0h = cur.cu.c * kChunk + cur.h * kHalf;  // first slot of the half
+    uint32_t* kp = a.keys + static_cast<int64_t>(t) * a.ncap + s0h;
+    uint32_t* bp = MODE == QLI_MODE_SOURCE ? a.bkeys + static_cast<int64_t>(t) * a.nbcap + s0h / 8 : nullptr;
+#pragma unroll 1
+    for (int sub = 0; sub < 2; ++sub) {
+      // 32 heads: the sub-tile's B fragments once in registers; 64 heads:
+      // read from LDS per pass (fits the register budget of three waves)
+      i32x4 bf[2][4];
+      if (P == 1) load_b(tl, sub, lane, bf);
+      float sum = 0.0f;
+#pragma unroll
+      for (int ps = 0; ps < P; ++ps) {
+        i32x16 acc[2];
+        if (P == 1) mfma_pass_b(q, bf, ps, lane, seed, acc);
+        else mfma_pass(q, tl, sub, ps, lane, seed, acc);
+        if (DBG) dbg_store_qk<NH, MODE>(a, acc, ps, t, s0h + 64 * sub, n_i, ksc[buf], sub, lane);
+        if (qs.scaled) epi_pass<true, true>(q, acc, ps, lane, one, sum);
+        else epi_pass<true, false>(q, acc, ps, lane, one, sum);
+      }
+      finish_subtile<MODE, DBG>(a, ksc[buf], sub, t, s0h + 64 * sub, n_i, lane, sum, kp, bp);
+    }
+    // the next half's rows and lookups have landed; its scales go to LDS
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (n1.cu.valid) store_scales(buf ^ 1, v1, wave, n1);
+    __syncthreads();
+    cur = n1;
+    n1 = n2;
+    buf ^= 1;
+  }
+}
+
+// The multi list in a kernel of its own: four workgroups per CU with 32
+// heads (127 VGPRs; 4 x 33 KB of LDS), three with 64 (157 VGPRs; the host
+// launches it for 32 heads only).
+__host__ __device__ constexpr int multi_wgs_per_cu(int nh) { return nh == 32 ? 4 : 3; }
+
+template <int NH, int MODE, bool DBG>
+__global__ __launch_bounds__(kScoreThreads, multi_wgs_per_cu(NH)) void score_multi_kernel(KArgs a) {
+  __shared__ __attribute__((aligned(16))) int8_t tile[2][kHalf * 128];
+  __shared__ __attribute__((aligned(16))) uint16_t ksc[2][kHalf];
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const WgStart st = a.wgs[start_entry(blockIdx.x, gridDim.x, a.nxcd)];
+  if (st.g < 0 || st.unit >= st.hi || st.list != 0) return;
+  const ListView L{a.groups, a.ustart, st.ng};
+  Cursor cu;
+  cu.g = st.g;
+  cu.c = st.c;
+  cu.unit = st.unit;
+  cu.grp = st.grp;
+  cu.valid = true;
+  i32x16 seed;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) seed[i] = kSeedBits;
+  bool bad = false;
+  run_multi_half<NH, MODE, DBG>(a, L, cu, st.hi, tile, ksc, wave, lane, seed, bad);
+  if (bad) raise_flag(a, QLI_DEV_BAD_PAGE);
+}
+
 // Single-token groups (decode shapes): wave w stages and scores sub-tile w
 // of every item in its own LDS rows, so inside a token segment the waves
 // run independently (an LDS write and a later read of the same wave are
@@ -1461,16 +1666,6 @@ __device__ void run_single(const KArgs& a, const ListView& L, Cursor cu, int hi,
   if (ne > 0) flush_keys<MODE>(a, stage, meta, ne);
 }
 
-// The dispatcher hands workgroup i to XCD i mod nxcd, and each XCD has its
-// own L2.  The plan splits the work lists into contiguous ranges in token
-// order (the tokens of a request are neighbours), so workgroup i takes
-// start entry (i mod nxcd) * (grid / nxcd) + i / nxcd: every XCD walks one
-// contiguous stretch of the lists, and the tokens of a request that read
-// the same K rows share an L2 instead of fetching them through all of them.
-__device__ __forceinline__ int start_entry(int i, int grid, int nxcd) {
-  if (nxcd <= 1 || grid % nxcd) return i;
-  return (i % nxcd) * (grid / nxcd) + i / nxcd;
-}
 
 // Each workgroup takes its list, first item and unit range from the plan.
 // STREAM: K rows of single-token groups are read with non-temporal loads
@@ -1502,7 +1697,7 @@ __global__ __launch_bounds__(kScoreThreads, score_wgs_per_cu(MODE, NH)) void sco
 
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
-  const WgStart st = a.wgs[start_entry(blockIdx.x, gridDim.x, a.nxcd)];
+  const WgStart st = a.wgs[a.entry_base + start_entry(blockIdx.x, gridDim.x, a.nxcd)];
   if (st.g < 0 || st.unit >= st.hi) return;
   const int l = st.list;
   const ListView L{a.groups + static_cast<int64_t>(l) * a.T,
@@ -2194,6 +2389,23 @@ void launch_score_mode(int mode, bool dbg, bool cached, unsigned grid, hipStream
   else launch_score_dbg<NH, QLI_MODE_CONSUMER>(dbg, grid, st, a);
 }
 
+template <int NH>
+void launch_score_multi_nh(int mode, bool dbg, unsigned grid, hipStream_t st, const KArgs& a) {
+  static_assert(NH == 32, "the separate multi kernel serves 32 heads");
+  if (mode == QLI_MODE_PLAIN) {
+    if (dbg) score_multi_kernel<NH, QLI_MODE_PLAIN, true><<<grid, kScoreThreads, 0, st>>>(a);
+    else score_multi_kernel<NH, QLI_MODE_PLAIN, false><<<grid, kScoreThreads, 0, st>>>(a);
+  } else {
+    if (dbg) score_multi_kernel<NH, QLI_MODE_SOURCE, true><<<grid, kScoreThreads, 0, st>>>(a);
+    else score_multi_kernel<NH, QLI_MODE_SOURCE, false><<<grid, kScoreThreads, 0, st>>>(a);
+  }
+}
+
+void launch_score_multi(int heads, int mode, bool dbg, unsigned grid, hipStream_t st, const KArgs& a) {
+  (void)heads;  // 32 (see launch())
+  launch_score_multi_nh<32>(mode, dbg, grid, st, a);
+}
+
 void launch_score(int heads, int mode, bool dbg, bool cached, unsigned grid, hipStream_t st, const KArgs& a) {
   if (heads == 64) launch_score_mode<64>(mode, dbg, cached, grid, st, a);
   else launch_score_mode<32>(mode, dbg, cached, grid, st, a);
@@ -2240,6 +2452,19 @@ int launch(const qli_params* p, const WsLayout& w, void* stream, bool timed) {
   a.ustart = reinterpret_cast<int32_t*>(ws + w.ustart_off);
   a.wgs = reinterpret_cast<WgStart*>(ws + w.wgs_off);
   a.score_grid = std::min(kMaxScoreWGs, std::max(2, score_wgs_per_cu(p->mode, p->num_heads) * cu_count()));
+  // batches of prefill shape with 32 heads (at least four query tokens per
+  // request on average, so groups of four exist): the multi list runs in a
+  // kernel of its own at four workgroups per CU, then the single list
+  // (mixed batch source score kernels 3.01 -> 2.83 ms and 1.66 -> 1.38 ms
+  // on one box).  With 64 heads the half-item path at three workgroups per
+  // CU measured slower than the two-wave path (prefill chunk 752 -> 841 us:
+  // the B fragments re-read per pass and the single accumulator set cost
+  // more than the third wave gains), so 64-head batches keep the latter.
+  a.multi_grid = 0;
+  a.entry_base = 0;
+  if (p->mode != QLI_MODE_CONSUMER && p->num_heads == 32 &&
+      static_cast<int64_t>(p->num_tokens) >= 4 * static_cast<int64_t>(p->batch))
+    a.multi_grid = std::min(kMaxScoreWGs - a.score_grid, multi_wgs_per_cu(p->num_heads) * cu_count());
   a.nxcd = xcd_count();
   a.slots = consumer ? reinterpret_cast<int32_t*>(ws + w.slots_off) : nullptr;
   a.srow = consumer ? reinterpret_cast<int32_t*>(ws + w.srow_off) : nullptr;
@@ -2299,6 +2524,11 @@ void launch_slice(const qli_params* p, const WsLayout& w, KArgs a, bool cached, 
   }
   if (w.ncap > 0) {
     Stamp s(QLI_KERNEL_SCORE, st, timed);
+    if (a.multi_grid > 0) {
+      launch_score_multi(p->num_heads, p->mode, p->dbg_scores != nullptr, static_cast<unsigned>(a.multi_grid),
+                         st, a);
+      a.entry_base = a.multi_grid;
+    }
     launch_score(p->num_heads, p->mode, p->dbg_scores != nullptr, cached, static_cast<unsigned>(a.score_grid),
                  st, a);
   }
