@@ -42,10 +42,15 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+# kernels the library's timing facility reports under one name
+KERNEL_GROUPS = {"score_kernel": ("score_kernel", "score_multi_kernel")}
+
+
 def recorded_traffic(workload, kernel, source="qli_kernels.hip"):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary (profiles/traffic.json), or None when the kernel source changed
-    since the counters were taken."""
+    """HBM bytes per call of `kernel` (all its launches in one call; the
+    score kernel's name covers both score kernels) from the committed
+    rocprofv3 counter summary (profiles/traffic.json), or None when the
+    kernel source changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     src = os.path.join(ROOT, "quantized_top_indexer_amd", "csrc", source)
@@ -55,10 +60,10 @@ def recorded_traffic(workload, kernel, source="qli_kernels.hip"):
     entry = json.load(open(path)).get(workload)
     if not entry or entry.get("source_hash") != h:
         return None, None
-    for k, v in entry["hbm_bytes_per_launch"].items():
-        if k.split("<")[0] == kernel:
-            return v, entry.get("summary")
-    return None, None
+    per = entry.get("hbm_bytes_per_call") or entry.get("hbm_bytes_per_launch", {})
+    names = KERNEL_GROUPS.get(kernel, (kernel,))
+    hits = [v for k, v in per.items() if k.split("<")[0] in names]
+    return (sum(hits), entry.get("summary")) if hits else (None, None)
 
 
 def algorithmic(pb, cand_in=None):
