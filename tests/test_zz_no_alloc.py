@@ -2,7 +2,7 @@
 outputs equal those of qli_score_topk with a caller workspace, bit for bit,
 on two calls in a row through the C ABI, the second on a smaller input (the
 static scratch keeps the first call's contents), in source and in consumer
-mode."""
+mode, and on a call larger than the static array (run in slices)."""
 import numpy as np
 import pytest
 
@@ -28,7 +28,6 @@ def _both(pb, cand_in=None):
         args = {k: v for k, v in kw.items() if k not in ("cand_blocks",)}
         p = Q.make_params(**args, cand_blocks=pb.cand_blocks, topk_out=topk, cand_out=cand)
         if noalloc:
-            assert Q.qli_workspace_bytes(p) <= Q.QLI_STATIC_SCRATCH_BYTES
             rc = Q.qli_score_topk_noalloc(p)
             ws = None
         else:
@@ -57,3 +56,22 @@ def test_noalloc_matches_workspace_call(mode):
         assert np.all(tn != -7)
         if mode == 2:
             assert np.array_equal(ci, cn), pb.name
+
+
+def test_noalloc_slices_a_call_beyond_its_array():
+    """A call whose workspace exceeds the 32 MiB static array runs in token
+    slices that fit it (4-token groups cut at slice boundaries are scored as
+    single tokens): the same outputs as the workspace call."""
+    import quantized_top_indexer_amd as Q
+    # 1500 tokens of two long requests: 1500 x 6400 key slots x 4 B > 32 MiB
+    pb = small_problem(920, ratio=2, N=32, mode=2, topk=300, cb=128,
+                       requests=((1000, 12800), (499, 9000), (1, 300)))
+    from qli_workloads.device import call_kwargs, to_device
+    p = Q.make_params(**{k: v for k, v in call_kwargs(pb, to_device(pb, "cuda")).items()
+                         if k != "cand_blocks"}, cand_blocks=pb.cand_blocks)
+    assert Q.qli_workspace_bytes(p) > Q.QLI_STATIC_SCRATCH_BYTES
+    say(f"no-alloc sliced {pb.name}: T={pb.num_tokens} L={pb.max_k_len}")
+    (ti, ci), (tn, cn) = _both(pb)
+    assert np.array_equal(ti, tn)
+    assert np.array_equal(ci, cn)
+
