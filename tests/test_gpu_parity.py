@@ -321,6 +321,41 @@ def test_device_status_flags():
     assert torch.all(idx == -1)
 
 
+@pytest.mark.parametrize("N", [32, 64])
+def test_bad_page_in_four_token_groups(N):
+    """A block-table entry past the pool read by 4-token groups (the prefill
+    paths: with 32 heads the group kernel of its own, with 64 the two-wave
+    path): the status flag is raised, the page's positions and blocks are
+    excluded for every token of the request, and every token still equals
+    the oracle run on the same table with that page's positions removed."""
+    import torch
+
+    import quantized_top_indexer_amd as Q
+    pb = small_problem(308 + N, ratio=2, N=N, mode=2, topk=300, cb=64,
+                       requests=((8, 2000), (4, 900)))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    clean = run_gpu(pb, debug=True)
+    pb.block_table = pb.block_table.copy()
+    pb.block_table[0, 2] = pb.num_pages + 5          # positions 128..191 of request 0
+    res = run_gpu(pb, debug=True, status=status)
+    assert int(status.item()) & Q.QLI_DEV_BAD_PAGE
+    sc = res["scores"]
+    assert np.all(np.isnan(sc[:8, 128:192]))          # never scored
+    for t in range(8):
+        row = res["topk"][t]
+        assert not np.any((row >= 128) & (row < 192))
+        assert not np.any((res["cand"][t] >= 16) & (res["cand"][t] < 24))
+        # the other positions keep their scores; the selection is the best of them
+        keep = ~np.isnan(sc[t])
+        assert np.array_equal(sc[t][keep], clean["scores"][t][keep])
+        order = np.lexsort((np.arange(sc.shape[1])[keep], -sc[t][keep].astype(np.float64)))
+        want = np.sort(np.flatnonzero(keep)[order[:300]])
+        assert np.array_equal(row[row >= 0], want)
+    for t in range(8, 12):                            # request 1 is untouched
+        assert np.array_equal(res["topk"][t], clean["topk"][t])
+        assert np.array_equal(res["cand"][t], clean["cand"][t])
+
+
 def test_bad_page_when_everything_fits():
     """When top-k and the candidate width cover every visible position and
     block, the selection is everything visible; a block-table entry past the
