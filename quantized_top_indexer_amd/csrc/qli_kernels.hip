@@ -1893,7 +1893,7 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n, int cap
   uint32_t* ci = ck + sel_cand(BS);
   uint32_t* rk = ci + sel_cand(BS);     // boundary-bin keys for exact ranking, then indices
   uint32_t* ri = rk + kSelRank;
-  int32_t* ol = reinterpret_cast<int32_t*>(ri + kSelRank);  // winners' key indices (<= 2048)
+  int32_t* ol = reinterpret_cast<int32_t*>(ri + kSelRank);  // winners' key indices, in order (<= k)
   auto refine = [&](auto each, uint32_t lo, uint32_t hi, uint32_t kr_, uint32_t& t_, uint32_t& n_) {
     refine_threshold<BS>(each, lo, hi, kr_, t_, n_, hist, sh, misc, rk, ri);
   };
@@ -1909,60 +1909,85 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n, int cap
   auto index_of = [&](int ch, int j, int e) {
     return ch * CHUNK + wave * kpw + 256 * j + 4 * lane + e;
   };
+  const bool pinned = pin >= 0 && pin < n;
   auto load = [&](int ch) {  // every load is issued before the first use
     i32x4 x[VPT];
 #pragma unroll
     for (int j = 0; j < VPT; ++j)
       x[j] = *reinterpret_cast<const i32x4*>(keys + min(index_of(ch, j, 0), cap - 4));
-#pragma unroll
-    for (int j = 0; j < VPT; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // vectors past nvec may reach into the next wave's keys: zero
-        const int idx = index_of(ch, j, e);
-        const bool own = j < nvec && idx < n;
-        const uint32_t v = own ? static_cast<uint32_t>(x[j][e]) : 0u;
-        kr[4 * j + e] = own && idx == pin ? kPinKey : v;
-      }
-  };
-
-  // range and count of the scores (keys other than 0 and the pin)
-  uint32_t mn = 0xFFFFFFFFu, mx = 0, cnt = 0;
-  for (int ch = 0; ch < nch; ++ch) {
-    load(ch);
+    const int vb = ch * CHUNK + wave * kpw;  // first index of this wave's share
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-      if (j >= nvec) continue;
+      if (j < nvec && vb + 256 * (j + 1) <= n) {  // the whole vector lies in the row
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t v = kr[4 * j + e];
-        const bool s = v != 0 && v != kPinKey;
-        mn = s ? min(mn, v) : mn;
-        mx = s ? max(mx, v) : mx;
-        cnt += s ? 1u : 0u;
+        for (int e = 0; e < 4; ++e) kr[4 * j + e] = static_cast<uint32_t>(x[j][e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // vectors past nvec may reach into the next wave's keys: zero
+          const bool own = j < nvec && index_of(ch, j, e) < n;
+          kr[4 * j + e] = own ? static_cast<uint32_t>(x[j][e]) : 0u;
+        }
       }
     }
-  }
-  mn = wave_allreduce(mn, MinOp{});
-  mx = wave_allreduce(mx, MaxOp{});
+    // the pin, if this wave holds it: one lane's element of one vector
+    const int po = pin - vb;
+    if (pinned && po >= 0 && po < 256 * nvec) {
+#pragma unroll
+      for (int j = 0; j < VPT; ++j)
+        if (j == (po >> 8)) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (lane == ((po >> 2) & 63) && e == (po & 3)) kr[4 * j + e] = kPinKey;
+        }
+    }
+  };
+
+  // range and count of the scores (keys other than 0 and the pin): the
+  // minimum is taken over key - 1, which sends the zero keys to the top;
+  // with a pin the maximum is taken over key + 1, which sends it to 0
+  uint32_t mn1 = 0xFFFFFFFFu, mx1 = 0, cnt = 0;
+  auto range = [&](const bool P) {
+    const uint32_t o = P ? 1u : 0u;
+    for (int ch = 0; ch < nch; ++ch) {
+      load(ch);
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        if (j >= nvec) continue;
+        const uint32_t v0 = kr[4 * j], v1 = kr[4 * j + 1], v2 = kr[4 * j + 2], v3 = kr[4 * j + 3];
+        mx1 = max(max(mx1, v0 + o), v1 + o);
+        mx1 = max(max(mx1, v2 + o), v3 + o);
+        mn1 = min(min(mn1, v0 - 1u), v1 - 1u);
+        mn1 = min(min(mn1, v2 - 1u), v3 - 1u);
+        cnt += min(v0, 1u) + min(v1, 1u);
+        cnt += min(v2, 1u) + min(v3, 1u);
+      }
+    }
+  };
+  if (pinned) range(true);
+  else range(false);
+  mn1 = wave_allreduce(mn1, MinOp{});
+  mx1 = wave_allreduce(mx1, MaxOp{});
   cnt = wave_allreduce(cnt, AddOp{});
   if (lane == 0) {
-    sh[wave] = mn;
-    sh[16 + wave] = mx;
+    sh[wave] = mn1;
+    sh[16 + wave] = mx1;
     sh[32 + wave] = cnt;
   }
   __syncthreads();
-  mn = sh[0];
-  mx = sh[16];
+  mn1 = sh[0];
+  mx1 = sh[16];
   cnt = sh[32];
 #pragma unroll
   for (int w = 1; w < NW; ++w) {
-    mn = min(mn, sh[w]);
-    mx = max(mx, sh[16 + w]);
+    mn1 = min(mn1, sh[w]);
+    mx1 = max(mx1, sh[16 + w]);
     cnt += sh[32 + w];
   }
   __syncthreads();
-  const bool pinned = pin >= 0 && pin < n;
+  cnt -= pinned ? 1u : 0u;  // the pin was counted as a key
+  const uint32_t mn = cnt == 0 ? 0xFFFFFFFFu : mn1 + 1u;
+  const uint32_t mx = cnt == 0 ? 0u : mx1 - (pinned ? 1u : 0u);
 
   // threshold: keys > thr are taken, then the first `need` keys == thr
   uint32_t thr = 0, need = 0;
@@ -2053,16 +2078,17 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n, int cap
             min(static_cast<uint64_t>(mx), static_cast<uint64_t>(mn) + ((static_cast<uint64_t>(b_top) + 1) << sft0) - 1));
         // keys above the bracket and inside it, packed above << 16 | inside
         // (a chunk holds at most 32768 keys); the prefix places the gather
-        uint32_t cnt2 = 0;
+        // (the pin, if any, lies above bhi and is not counted)
+        uint32_t above = 0, inb = 0;
 #pragma unroll
         for (int r = 0; r < 4 * VPT; ++r) {
           const uint32_t key = kr[r];
-          cnt2 += (key > bhi && key != kPinKey) ? (1u << 16) : 0u;
-          cnt2 += (key - blo <= bhi - blo) ? 1u : 0u;
+          above += key > bhi ? 1u : 0u;
+          inb += key - blo <= bhi - blo ? 1u : 0u;
         }
         uint32_t tot2;
-        uint32_t at = block_exclusive_scan<BS>(cnt2, &tot2, sh) & 0xFFFFu;
-        const uint32_t n_above = tot2 >> 16, n_in = tot2 & 0xFFFFu;
+        uint32_t at = block_exclusive_scan<BS>((above << 16) | inb, &tot2, sh) & 0xFFFFu;
+        const uint32_t n_above = (tot2 >> 16) - (pinned ? 1u : 0u), n_in = tot2 & 0xFFFFu;
         if (n_above < krem && n_above + n_in >= krem && n_in <= static_cast<uint32_t>(sel_cand(BS))) {
           // gather the bracket's keys and search them alone
 #pragma unroll
@@ -2090,100 +2116,106 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n, int cap
     }
   }
 
-  // ordered compaction: a key's output slot is (keys > thr before it) +
-  // min(need, keys == thr before it), both counted in index order (packed
-  // as gt << 16 | eq; a chunk holds at most 32768 keys).  The winners' key
-  // indices are staged in LDS and written out in order.
+  // ordered compaction over a bitmask of the winners (keys > thr, then the
+  // first `need` keys == thr in index order): lane l's four keys of vector
+  // j fill one nibble of word (wave * kpw + 256 j) / 32 + l / 8 of the
+  // chunk, OR-ed over the 8 lanes of the word on DPP; each thread then takes
+  // one word, a block prefix sum of the words' counts places it, and it
+  // places the winners (see `sparse`) in LDS, from where they are written
+  // out in order.  Words holding no index below n are never read (every
+  // word with one is written).
+  constexpr int NWD = CHUNK / 32;
+  static_assert(NWD <= BS && 2 * NWD <= 2048, "two bitmasks of a chunk in the histogram's place");
+  uint32_t* gtw = hist;
+  uint32_t* eqw = hist + NWD;
   uint32_t run_gt = 0, run_eq = 0;
-  static_assert(4 * VPT <= 32, "one winner bit per key of a chunk");
-  if (need == 0) {
-    // no tie at the threshold: the winners are the keys > thr; one mask bit
-    // per key (vector j, element e -> bit 4j + e) is computed once
-    for (int ch = 0; ch < nch; ++ch) {
-      if (MULTI && nch > 1) load(ch);
-      uint32_t gm = 0;
+  // few winners per word (at most one in eight keys): each word's thread
+  // writes them; otherwise every lane writes its own
+  const bool sparse = 8 * static_cast<int64_t>(k) <= n;
+  for (int ch = 0; ch < nch; ++ch) {
+    if (MULTI && nch > 1) load(ch);
 #pragma unroll
-      for (int j = 0; j < VPT; ++j) {
-        if (j >= nvec) continue;
+    for (int j = 0; j < VPT; ++j) {
+      if (j >= nvec) continue;
+      uint32_t g = 0, q = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) gm |= (kr[4 * j + e] > thr ? 1u : 0u) << (4 * j + e);
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = kr[4 * j + e];
+        g |= (key > thr ? 1u : 0u) << e;
+        q |= (key == thr ? 1u : 0u) << e;
       }
-      uint32_t excl[VPT];
-      uint32_t wsum = 0;
-#pragma unroll
-      for (int j = 0; j < VPT; ++j) {
-        excl[j] = wsum;
-        if (j >= nvec) continue;
-        const uint32_t c = static_cast<uint32_t>(__popc((gm >> (4 * j)) & 0xFu));
-        const uint32_t inc = wave_inclusive_scan(c);
-        excl[j] = wsum + inc - c;
-        wsum += static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(inc), 63));
+      const int sft = 4 * (lane & 7);
+      g <<= sft;
+      g |= dpp_all<0xB1>(g);   // quad_perm [1, 0, 3, 2]
+      g |= dpp_all<0x4E>(g);   // quad_perm [2, 3, 0, 1]
+      g |= dpp_all<0x141>(g);  // row_half_mirror
+      const int w = ((wave * kpw + 256 * j) >> 5) + (lane >> 3);
+      if ((lane & 7) == 0) gtw[w] = g;
+      if (need != 0) {
+        q <<= sft;
+        q |= dpp_all<0xB1>(q);
+        q |= dpp_all<0x4E>(q);
+        q |= dpp_all<0x141>(q);
+        if ((lane & 7) == 0) eqw[w] = q;
       }
-      if (lane == 0) sh[wave] = wsum;
+    }
+    __syncthreads();
+    const int nwd = (min(CHUNK, n - ch * CHUNK) + 31) >> 5;
+    uint32_t gw = 0, qw = 0;
+    if (tid < nwd) {
+      gw = gtw[tid];
+      qw = need != 0 ? eqw[tid] : 0u;
+    }
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan<BS>((static_cast<uint32_t>(__popc(gw)) << 16) |
+                                                     static_cast<uint32_t>(__popc(qw)),
+                                                 &tot, sh);  // ends with a barrier: the words may be rewritten
+    if (tid < nwd) {
+      const uint32_t eq_before = run_eq + (ex & 0xFFFFu);
+      uint32_t m = gw;
+      if (qw != 0 && eq_before < need) {
+        uint32_t take = qw;  // its lowest need - eq_before ties
+        const uint32_t room = need - eq_before;
+        while (static_cast<uint32_t>(__popc(take)) > room) take &= ~(0x80000000u >> __clz(take));
+        m |= take;
+      }
+      uint32_t at = run_gt + (ex >> 16) + min(need, eq_before);
+      if (sparse) {
+        const int base = ch * CHUNK + 32 * tid;
+        while (m != 0) {
+          const int b = __ffs(m) - 1;
+          if (at < static_cast<uint32_t>(k)) ol[at] = base + b;
+          ++at;
+          m &= m - 1;
+        }
+      } else {
+        gtw[tid] = m;  // the word's winners and its first output slot
+        eqw[tid] = at;
+      }
+    }
+    if (!sparse) {
+      // each lane writes its own winners: slot = the word's first slot +
+      // the winners below the lane's nibble + those before it in the nibble
       __syncthreads();
-      uint32_t wbase = 0, tot = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const uint32_t x = sh[w];
-        wbase += w < wave ? x : 0u;
-        tot += x;
-      }
-      __syncthreads();  // sh is reused
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
         if (j >= nvec) continue;
-        uint32_t at = run_gt + wbase + excl[j];
+        const int w = ((wave * kpw + 256 * j) >> 5) + (lane >> 3);
+        const uint32_t m = gtw[w];
+        const int sft = 4 * (lane & 7);
+        const uint32_t nib = (m >> sft) & 0xFu;
+        if (nib != 0) {
+          uint32_t at = eqw[w] + static_cast<uint32_t>(__popc(m & ((1u << sft) - 1u)));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if ((gm >> (4 * j + e)) & 1u) {
-            ol[at] = index_of(ch, j, e);
-            ++at;
+          for (int e = 0; e < 4; ++e) {
+            if ((nib >> e) & 1u) {
+              if (at < static_cast<uint32_t>(k)) ol[at] = index_of(ch, j, e);
+              ++at;
+            }
           }
         }
       }
-      run_gt += tot;
-    }
-  }
-  for (int ch = 0; ch < (need == 0 ? 0 : nch); ++ch) {
-    if (MULTI && nch > 1) load(ch);
-    auto flag = [&](uint32_t key) {
-      return key > thr ? (1u << 16) : ((key == thr && need != 0) ? 1u : 0u);
-    };
-    uint32_t excl[VPT];  // this lane's prefix within its wave, per vector
-    uint32_t wsum = 0;   // running wave total over the vectors
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      excl[j] = wsum;
-      if (j >= nvec) continue;
-      uint32_t c = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) c += flag(kr[4 * j + e]);
-      const uint32_t inc = wave_inclusive_scan(c);
-      excl[j] = wsum + inc - c;
-      wsum += static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(inc), 63));
-    }
-    if (lane == 0) sh[wave] = wsum;
-    __syncthreads();
-    uint32_t wbase = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const uint32_t x = sh[w];
-      wbase += w < wave ? x : 0u;
-      tot += x;
-    }
-    __syncthreads();  // sh is reused
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      if (j >= nvec) continue;
-      uint32_t before = wbase + excl[j];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t f = flag(kr[4 * j + e]);
-        const uint32_t eq_rank = run_eq + (before & 0xFFFFu);
-        const bool sel = f == (1u << 16) || (f == 1u && eq_rank < need);
-        if (sel) ol[run_gt + (before >> 16) + min(need, eq_rank)] = index_of(ch, j, e);
-        before += f;
-      }
+      __syncthreads();  // the words are rewritten for the next chunk
     }
     run_gt += tot >> 16;
     run_eq += tot & 0xFFFFu;
@@ -2197,6 +2229,8 @@ struct MapIdentity {
   __device__ __forceinline__ int32_t operator()(int i) const { return i; }
 };
 
+// Candidate slot i -> position: slot i is position i & 7 of incoming block
+// slots[i >> 3].
 struct MapSlots {
   const int32_t* slots;
   __device__ __forceinline__ int32_t operator()(int i) const { return slots[i >> 3] * 8 + (i & 7); }
