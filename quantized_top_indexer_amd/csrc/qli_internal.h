@@ -16,7 +16,8 @@ namespace qli {
 //   plan   header (group counts, work units), groups [2][T] x 32 B, ustart [2][T+1]:
 //          the two work lists the plan kernel builds for the persistent score kernel
 //   wgs    [kMaxScoreWGs] x 64 B: each score workgroup's list, first item and range
-//   tokv   [T]          visible compressed count per token (written by the plan)
+//   tokv   [T, 2]       per token: visible compressed count (written by the plan), and
+//                       the launch's epoch where the token met an out-of-contract page
 //   slots  [T, cand_in_blocks] sorted unique visible incoming block ids (consumer)
 //   srow   [T, cand_in_blocks] page*page_rows + row of each slot block (consumer)
 //   ncount [T]          eligible positions per token (consumer)
@@ -75,7 +76,7 @@ inline WsLayout ws_layout(const qli_params* p, int64_t slice_tokens) {
   w.wgs_off = off;
   off = align256(off + static_cast<size_t>(kMaxScoreWGs) * kWgStartBytes);
   w.tokv_off = off;
-  off = align256(off + T * 4);
+  off = align256(off + T * 8);
   if (p->mode == QLI_MODE_CONSUMER) {
     const size_t cb = static_cast<size_t>(p->cand_in_blocks);
     w.slots_off = off;

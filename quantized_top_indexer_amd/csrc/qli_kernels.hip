@@ -38,6 +38,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 #include <vector>
@@ -123,7 +124,12 @@ struct KArgs {
   int32_t* slots;
   int32_t* srow;
   int32_t* ncount;
-  int32_t* tokv;    // [T] visible compressed count per token (plan), | kTokBad (score)
+  // [T][2] per token: [0] visible compressed count (plan); [1] == epoch: a
+  // block the token may read had an out-of-contract page (score)
+  int32_t* tokv;
+  uint32_t epoch;   // this launch's stamp (another value in tokv[t][1] is stale)
+  int fused;        // the score kernel plans for itself (no plan launch; small batches)
+  int plan_wg;      // >= 0: the plan keeps only this workgroup's start entry, in wgs[0]
 };
 
 __device__ __forceinline__ void raise_flag(const KArgs& a, uint32_t bit) {
@@ -377,9 +383,9 @@ __device__ __forceinline__ void prep_write(const KArgs& a, int t, int b, int V, 
 // is bounded by min(cb_in, visible blocks) * 8 slots, and the score kernel
 // reads the exact eligible count), blocks 1..T prepare token blockIdx.x - 1.
 // Both roles carve their LDS from one buffer.
-template <int PT>
-__device__ void plan_role(const KArgs& a, uint32_t* lds);
 constexpr int kPlanLdsRequests = 4096;  // metadata of up to this many requests is staged in LDS
+template <int PT, int NREQ = kPlanLdsRequests>
+__device__ void plan_role(const KArgs& a, uint32_t* lds);
 constexpr int kPlanLdsWords = 3 * kPlanLdsRequests + 1 + 64;
 constexpr int kPrepLdsWords = kPrepBitmapWords + QLI_MAX_CAND_BLOCKS + 64 + 1;
 constexpr int kConsumerLdsWords = kPrepLdsWords > kPlanLdsWords ? kPrepLdsWords : kPlanLdsWords;
@@ -557,8 +563,11 @@ __device__ __forceinline__ Group make_group(const KArgs& a, int b, const ReqView
 
 // floor(p / q) for 0 <= p < 2^53 and 0 < q < 2^31: the correctly rounded
 // double quotient is within one of the floor, and one integer check fixes it
-// (the integer divide would be a long software sequence).
+// (a 64-bit integer divide would be a long software sequence); operands
+// below 2^32 take one unsigned 32-bit division.
 __device__ __forceinline__ int64_t floor_div(int64_t p, int64_t q) {
+  if (((p | q) >> 32) == 0)  // both below 2^32: one unsigned 32-bit division
+    return static_cast<uint32_t>(p) / static_cast<uint32_t>(q);
   int64_t f = static_cast<int64_t>(static_cast<double>(p) / static_cast<double>(q));
   if (f * q > p) --f;
   else if ((f + 1) * q <= p) ++f;
@@ -627,10 +636,17 @@ __device__ void write_starts(const KArgs& a, const Split& sp, int gidx, const Gr
   const int w0 = static_cast<int>(ceil_div((static_cast<int64_t>(unit0) - NT + 1) * nw, sp.U));
   const int w1 = static_cast<int>(min(static_cast<int64_t>(nw), ceil_div((e + 1) * nw, sp.U)));
   if (w0 >= w1) return;
-  const int64_t p0 = static_cast<int64_t>(w0) * sp.U;
+  int wa = w0, wb = w1;
+  if (a.plan_wg >= 0) {  // only workgroup plan_wg's entry is wanted
+    const int w = a.plan_wg - sp.base;
+    if (w < w0 || w >= w1) return;
+    wa = w;
+    wb = w + 1;
+  }
+  const int64_t p0 = static_cast<int64_t>(wa) * sp.U;
   int lo = static_cast<int>(floor_div(p0, nw));
   int rem = static_cast<int>(p0 - static_cast<int64_t>(lo) * nw);
-  for (int w = w0; w < w1; ++w) {
+  for (int w = wa; w < wb; ++w) {
     const int carry = rem + sp.r >= nw ? 1 : 0;
     const int hi = lo + sp.q + carry;
     rem = rem + sp.r - carry * nw;
@@ -645,7 +661,8 @@ __device__ void write_starts(const KArgs& a, const Split& sp, int gidx, const Gr
     st.unit = unit0 + c * NT;
     st.hi = hi;
     st.pad[0] = st.pad[1] = 0;
-    a.wgs[sp.base + w] = st;
+    if (a.plan_wg < 0) a.wgs[sp.base + w] = st;
+    else if (sp.base + w == a.plan_wg) a.wgs[0] = st;
     lo = hi;
   }
 }
@@ -711,7 +728,7 @@ __device__ __forceinline__ void plan_body(const KArgs& a, const Meta& m, uint32_
   };
   const Split sp0 = split(0), sp1 = split(1);
   if (per == 1 && t_lo < t_hi) {
-    a.tokv[t_lo] = tv1;
+    a.tokv[2 * t_lo] = tv1;
     if (kind1 != 0) {
       const int l = kind1 - 1;
       const uint32_t gi = l == 0 ? cnt[0] : cnt[2], ui = l == 0 ? cnt[1] : cnt[3];
@@ -731,7 +748,7 @@ __device__ __forceinline__ void plan_body(const KArgs& a, const Meta& m, uint32_
       const int tg = t + a.t_base;
       while (tg >= r.q1 && b + 1 < a.B) r = request_view(a, m, ++b, false);
       const bool in = tg >= r.q0 && tg < r.q1;
-      a.tokv[t] = in ? visible(a, r.S - (r.q1 - r.q0) + (tg - r.q0), r.L) : 0;
+      a.tokv[2 * t] = in ? visible(a, r.S - (r.q1 - r.q0) + (tg - r.q0), r.L) : 0;
       if (!in) continue;
       const int kind = group_kind(a, r, tg);
       if (kind == 0) continue;
@@ -756,31 +773,36 @@ __device__ __forceinline__ void plan_body(const KArgs& a, const Meta& m, uint32_
   }
   if (tid == 0) {
     for (int l = 0; l < 2; ++l) {
-      a.hdr->ngroups[l] = static_cast<int32_t>(tot[2 * l]);
-      a.hdr->units[l] = static_cast<int32_t>(tot[2 * l + 1]);
+      if (a.hdr) {
+        a.hdr->ngroups[l] = static_cast<int32_t>(tot[2 * l]);
+        a.hdr->units[l] = static_cast<int32_t>(tot[2 * l + 1]);
+      }
       a.ustart[l * (T + 1) + tot[2 * l]] = static_cast<int32_t>(tot[2 * l + 1]);
     }
   }
 }
 
-// PT threads (a consumer-prep workgroup, a plan workgroup, or one wave for
-// small batches, where no cross-wave barrier is needed).
-template <int PT>
+// PT threads (a consumer-prep workgroup, a plan workgroup, one wave for
+// small batches, where no cross-wave barrier is needed, or a score
+// workgroup planning for itself).  The metadata of up to NREQ requests is
+// staged in LDS (3 NREQ + 65 words).
+template <int PT, int NREQ>
 __device__ void plan_role(const KArgs& a, uint32_t* lds) {
   int32_t* s_qsl = reinterpret_cast<int32_t*>(lds);
-  int32_t* s_klen = s_qsl + kPlanLdsRequests + 1;
-  int32_t* s_smod = s_klen + kPlanLdsRequests;
-  uint32_t* sh = reinterpret_cast<uint32_t*>(s_smod + kPlanLdsRequests);
+  int32_t* s_klen = s_qsl + NREQ + 1;
+  int32_t* s_smod = s_klen + NREQ;
+  uint32_t* sh = reinterpret_cast<uint32_t*>(s_smod + NREQ);
   const int tid = threadIdx.x;
   // every start entry begins as "no work" (the barriers below order these
   // stores before the ones the plan writes); workgroups whose range starts
   // past the last item of their list keep it
-  for (int w = tid; w < a.multi_grid + a.score_grid; w += PT) {
+  const int nent = a.plan_wg >= 0 ? 1 : a.multi_grid + a.score_grid;
+  for (int w = tid; w < nent; w += PT) {
     WgStart st = {};
     st.g = -1;
     a.wgs[w] = st;
   }
-  if (a.B <= kPlanLdsRequests) {
+  if (a.B <= NREQ) {
     for (int i = tid; i <= a.B; i += PT) {
       s_qsl[i] = a.qsl[i];
       if (i < a.B) {
@@ -805,6 +827,8 @@ __global__ __launch_bounds__(PT) void plan_kernel(KArgs a) {
 // score: persistent, pipelined
 // ---------------------------------------------------------------------------
 constexpr int kScoreThreads = 256;
+// batches of at most this many tokens and requests plan inside the score kernel
+constexpr int kFusedTokens = 64;
 
 // Work-item cursor over one list (wave-uniform).
 struct Cursor {
@@ -821,8 +845,16 @@ struct ListView {
 
 __device__ __forceinline__ void load_group(const ListView& L, int g, Cursor& cu) {
   cu.g = g;
-  cu.grp = L.groups[g];
-  cu.unit = L.ustart[g];
+  const Group gr = L.groups[g];  // wave-uniform (LDS reads land in vector registers)
+  cu.grp.t0 = __builtin_amdgcn_readfirstlane(gr.t0);
+  cu.grp.ntok = __builtin_amdgcn_readfirstlane(gr.ntok);
+  cu.grp.b = __builtin_amdgcn_readfirstlane(gr.b);
+  cu.grp.nch = __builtin_amdgcn_readfirstlane(gr.nch);
+  cu.grp.p0 = __builtin_amdgcn_readfirstlane(gr.p0);
+  cu.grp.L = __builtin_amdgcn_readfirstlane(gr.L);
+  cu.grp.n0 = __builtin_amdgcn_readfirstlane(gr.n0);
+  cu.grp.nlast = __builtin_amdgcn_readfirstlane(gr.nlast);
+  cu.unit = __builtin_amdgcn_readfirstlane(L.ustart[g]);
   cu.c = 0;
 }
 
@@ -859,9 +891,11 @@ struct Addr {
   int t0, ntok;  // the tokens sharing the block (marked when its page is out of contract)
 };
 
-// Set in a token's visible count (tokv) when some block it may read had an
-// out-of-contract page: its selection then takes the general path.
-constexpr int32_t kTokBad = 1 << 30;
+// A token with a block on an out-of-contract page gets tokv[t][1] = the
+// launch's epoch: its selection then takes the general path, which leaves
+// out its zero keys.  Plain stores of one value by every writer; a stale
+// entry that happens to equal the epoch only sends a token down the
+// general path, which returns the same selection when every key is valid.
 
 template <bool CONSUMER, bool OWN>
 __device__ __forceinline__ void stage_addr(const KArgs& a, const Group& gr, int c, bool valid,
@@ -891,7 +925,7 @@ __device__ __forceinline__ int resolve(const KArgs& a, const Addr& ad, bool& bad
   const bool ok = want && (ad.meta & (1 << 30)) && ad.raw >= 0 && ad.raw < a.num_pages;
   if (want && !ok) {  // rare: mark every token of the group
     bad = true;
-    for (int i = 0; i < ad.ntok; ++i) atomicOr(&a.tokv[ad.t0 + i], kTokBad);
+    for (int i = 0; i < ad.ntok; ++i) a.tokv[2 * (ad.t0 + i) + 1] = static_cast<int32_t>(a.epoch);
   }
   return ok ? ad.raw * a.R + (ad.meta & (a.R - 1)) : -1;
 }
@@ -1424,7 +1458,7 @@ __device__ __forceinline__ int half_resolve(const KArgs& a, const HalfCursor& x,
   if (!ok) {  // rare: mark every token of the group
     bad = true;
     if ((threadIdx.x & 63) == 0)
-      for (int i = 0; i < x.cu.grp.ntok; ++i) atomicOr(&a.tokv[x.cu.grp.t0 + i], kTokBad);
+      for (int i = 0; i < x.cu.grp.ntok; ++i) a.tokv[2 * (x.cu.grp.t0 + i) + 1] = static_cast<int32_t>(a.epoch);
     return -1;
   }
   return ad.raw * a.R + (ad.pos0 & (a.R - 1));
@@ -1682,9 +1716,11 @@ __host__ __device__ constexpr int score_wgs_per_cu(int mode, int nh) {
   return mode == QLI_MODE_CONSUMER && nh == 32 ? 3 : 2;
 }
 
-template <int NH, int MODE, bool DBG, bool STREAM = true>
+// FUSED: the workgroup plans for itself (small plain/source batches).
+template <int NH, int MODE, bool DBG, bool STREAM = true, bool FUSED = false>
 __global__ __launch_bounds__(kScoreThreads, score_wgs_per_cu(MODE, NH)) void score_kernel(KArgs a) {
   constexpr bool SINGLE_ONLY = MODE == QLI_MODE_CONSUMER;
+  static_assert(!(FUSED && SINGLE_ONLY), "consumer batches are planned by their preparation");
   constexpr int NTILE = SINGLE_ONLY ? 1 : 2;
   constexpr int STAGE = SINGLE_ONLY ? key_stage_single(NH) : kKeyStage;
   __shared__ __attribute__((aligned(16))) int8_t tile[NTILE][kChunk * 128];
@@ -1695,13 +1731,42 @@ __global__ __launch_bounds__(kScoreThreads, score_wgs_per_cu(MODE, NH)) void sco
   // stages keys in its second K buffer)
   __shared__ __attribute__((aligned(16))) uint32_t kstage[SINGLE_ONLY ? STAGE * kKeyEntry + 2 * STAGE : 4];
 
+  // small batches plan here (every workgroup the same plan, kept in LDS)
+  constexpr int FT = FUSED ? kFusedTokens : 1;
+  __shared__ Group fgroups[2 * FT];
+  __shared__ int32_t fustart[2 * (FT + 1)];
+  __shared__ int32_t ftokv[2 * FT];
+  __shared__ WgStart fstart;
+
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
-  const WgStart st = a.wgs[a.entry_base + start_entry(blockIdx.x, gridDim.x, a.nxcd)];
+  const int entry = a.entry_base + start_entry(blockIdx.x, gridDim.x, a.nxcd);
+  const Group* groups = a.groups;
+  const int32_t* ustart = a.ustart;
+  WgStart st;
+  if constexpr (FUSED) {
+    KArgs b = a;
+    b.groups = fgroups;
+    b.ustart = fustart;
+    b.wgs = &fstart;
+    b.hdr = nullptr;
+    if (blockIdx.x != 0) b.tokv = ftokv;  // workgroup 0 writes the selection's counts
+    b.plan_wg = entry;
+    plan_role<kScoreThreads, kFusedTokens>(b, reinterpret_cast<uint32_t*>(tile[NTILE - 1]));
+    __syncthreads();  // the plan's LDS scratch is the K buffer
+    // wave-uniform values (LDS reads land in vector registers)
+    const int32_t* sp = reinterpret_cast<const int32_t*>(&fstart);
+    int32_t* dp = reinterpret_cast<int32_t*>(&st);
+#pragma unroll
+    for (int i = 0; i < static_cast<int>(sizeof(WgStart) / 4); ++i) dp[i] = __builtin_amdgcn_readfirstlane(sp[i]);
+    groups = fgroups;
+    ustart = fustart;
+  } else {
+    st = a.wgs[entry];
+  }
   if (st.g < 0 || st.unit >= st.hi) return;
   const int l = st.list;
-  const ListView L{a.groups + static_cast<int64_t>(l) * a.T,
-                   a.ustart + static_cast<int64_t>(l) * (a.T + 1), st.ng};
+  const ListView L{groups + static_cast<int64_t>(l) * a.T, ustart + static_cast<int64_t>(l) * (a.T + 1), st.ng};
   Cursor cu;
   cu.g = st.g;
   cu.c = st.c;
@@ -2271,18 +2336,18 @@ __global__ __launch_bounds__(BS, sel_min_waves(BS, CH)) void select_kernel(KArgs
       select_topk<BS, MULTI, CH>(keys, n, cap, a.topk, -1, out,
                       MapSlots{a.slots + static_cast<int64_t>(t) * a.cb_in}, sel_lds);
     } else {
-      const int32_t tv = a.tokv[t];
-      const int V = tv & ~kTokBad;
+      const int2 tv = reinterpret_cast<const int2*>(a.tokv)[t];  // count and bad-page stamp, one load
+      const int V = tv.x;
       if (!mine(V)) return;
-      if (!(tv & kTokBad) && V <= a.topk) all_of(out, V, a.topk);
+      if (tv.y != static_cast<int32_t>(a.epoch) && V <= a.topk) all_of(out, V, a.topk);
       else select_topk<BS, MULTI, CH>(keys, V, cap, a.topk, -1, out, MapIdentity{}, sel_lds);
     }
   } else {
-    const int32_t tv = a.tokv[t];
-    const int nb = ((tv & ~kTokBad) + 7) / 8;
+    const int2 tv = reinterpret_cast<const int2*>(a.tokv)[t];
+    const int nb = (tv.x + 7) / 8;
     if (!mine(nb)) return;
     int32_t* out = a.cand_out + static_cast<int64_t>(t) * a.cb;
-    if (!(tv & kTokBad) && nb <= a.cb) all_of(out, nb, a.cb);
+    if (tv.y != static_cast<int32_t>(a.epoch) && nb <= a.cb) all_of(out, nb, a.cb);
     else select_topk<BS, MULTI, CH>(a.bkeys + static_cast<int64_t>(t) * a.nbcap, nb, static_cast<int>(a.nbcap), a.cb,
                            nb - 1, out, MapIdentity{}, sel_lds);
   }
@@ -2305,6 +2370,8 @@ double g_ms[QLI_NUM_KERNELS];
 int64_t g_count[QLI_NUM_KERNELS];
 
 int g_cu_count[64];
+// per-launch stamps of the bad-page flags (distinct for 2^32 consecutive slices)
+std::atomic<uint32_t> g_epoch{0x9E3779B9u};
 int g_xcd_count[64];
 
 // Scratch of the entry point that allocates nothing.  In host code the name
@@ -2404,6 +2471,13 @@ int timing_read(double* ms, int64_t* count, int reset) {
 
 template <int NH, int MODE>
 void launch_score_dbg(bool dbg, unsigned grid, hipStream_t st, const KArgs& a) {
+  if constexpr (MODE != QLI_MODE_CONSUMER) {
+    if (a.fused) {
+      if (dbg) score_kernel<NH, MODE, true, true, true><<<grid, kScoreThreads, 0, st>>>(a);
+      else score_kernel<NH, MODE, false, true, true><<<grid, kScoreThreads, 0, st>>>(a);
+      return;
+    }
+  }
   if (dbg) score_kernel<NH, MODE, true><<<grid, kScoreThreads, 0, st>>>(a);
   else score_kernel<NH, MODE, false><<<grid, kScoreThreads, 0, st>>>(a);
 }
@@ -2504,6 +2578,8 @@ int launch(const qli_params* p, const WsLayout& w, void* stream, bool timed) {
   a.srow = consumer ? reinterpret_cast<int32_t*>(ws + w.srow_off) : nullptr;
   a.ncount = consumer ? reinterpret_cast<int32_t*>(ws + w.ncount_off) : nullptr;
   a.tokv = reinterpret_cast<int32_t*>(ws + w.tokv_off);
+  a.fused = 0;
+  a.plan_wg = -1;
 
   // some request holds several query tokens (consumer mode: each reads its
   // own candidate rows of the request's K, so the rows are read repeatedly)
@@ -2520,6 +2596,7 @@ int launch(const qli_params* p, const WsLayout& w, void* stream, bool timed) {
     a.cand_out = p->cand_out ? p->cand_out + t0 * p->cand_blocks : nullptr;
     a.dbg = p->dbg_scores ? p->dbg_scores + t0 * p->max_k_len : nullptr;
     a.dbg_qk = p->dbg_qk ? p->dbg_qk + t0 * NH * p->max_k_len : nullptr;
+    a.epoch = g_epoch.fetch_add(1, std::memory_order_relaxed);
     launch_slice(p, w, a, cached, st, timed);
   }
   return hipGetLastError() == hipSuccess ? QLI_OK : QLI_ERR_HIP;
@@ -2550,9 +2627,12 @@ void launch_slice(const qli_params* p, const WsLayout& w, KArgs a, bool cached, 
       consumer_prep_kernel<<<T + 1, kPrepThreads, 0, st>>>(a);
     else
       consumer_prep_sort_kernel<<<T + 1, kPrepThreads, 0, st>>>(a);
+  } else if (w.ncap > 0 && a.multi_grid == 0 && a.T <= kFusedTokens && p->batch <= kFusedTokens) {
+    // a decode-sized batch: every score workgroup plans for itself
+    a.fused = 1;
   } else {
     Stamp s(QLI_KERNEL_PLAN, st, timed);
-    // a decode-sized batch is planned by one wave
+    // a small batch is planned by one wave
     if (a.T <= 64 && p->batch <= 256) plan_kernel<64><<<1, 64, 0, st>>>(a);
     else plan_kernel<kPlanThreads><<<1, kPlanThreads, 0, st>>>(a);
   }
