@@ -389,6 +389,69 @@ def test_bad_page_when_everything_fits():
         assert np.array_equal(res["cand"][t], clean["cand"][t])
 
 
+def _expect_fits(pb, res, vis, bad=None):
+    """Everything visible is selected, in order, except the positions 64..127
+    and blocks 8..15 of request `bad` (a block-table entry past the pool)."""
+    q = pb.query_start_loc
+    for t, V in enumerate(vis):
+        V = int(V)
+        b = int(np.searchsorted(q, t, side="right")) - 1
+        hit = bad is not None and b == bad
+        want = np.array([j for j in range(V) if not (hit and 64 <= j < 128)], np.int64)
+        assert np.array_equal(res["topk"][t, :len(want)], want), (t, bad)
+        assert np.all(res["topk"][t, len(want):] == -1), (t, bad)
+        nb = -(-V // 8)
+        wb = np.array([c for c in range(nb) if not (hit and 8 <= c < 16)], np.int64)
+        assert np.array_equal(res["cand"][t, :len(wb)], wb), (t, bad)
+        assert np.all(res["cand"][t, len(wb):] == -1), (t, bad)
+
+
+def test_bad_page_marks_across_calls_on_one_workspace():
+    """Calls sharing one workspace, with an out-of-contract page and without
+    it in turn: each call's marks are its own (a clean call after a bad one
+    selects everything again; a bad call after clean ones takes the page's
+    positions and blocks out), whether the plan runs in its own launch or in
+    the score kernel (5 tokens, and 66 tokens with groups of four)."""
+    import torch
+
+    import quantized_top_indexer_amd as Q
+    from qli_workloads.device import call_kwargs, to_device
+    for requests in (((3, 1200), (2, 700)), ((30, 1400), (36, 1500))):
+        pb = small_problem(306, ratio=2, N=32, mode=2, topk=2048, cb=512, requests=requests)
+        vis = visible(pb)
+        clean_bt = pb.block_table.copy()
+        ws = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        for bad in (0, None, 1, None, 0):
+            pb.block_table = clean_bt.copy()
+            if bad is not None:
+                pb.block_table[bad, 1] = pb.num_pages + 7   # positions 64..127
+            say(f"tokens {pb.num_tokens}, bad page in request {bad}")
+            dev = to_device(pb, "cuda")
+            status = torch.zeros(1, dtype=torch.int32, device="cuda")
+            idx, cand, _ = Q.score_topk(**call_kwargs(pb, dev), status_out=status, workspace=ws)
+            torch.cuda.synchronize()
+            res = {"topk": idx[:, 0].cpu().numpy(), "cand": cand[:, 0].cpu().numpy()}
+            assert bool(int(status.item()) & Q.QLI_DEV_BAD_PAGE) == (bad is not None)
+            _expect_fits(pb, res, vis, bad)
+            del dev
+
+
+@pytest.mark.parametrize("shape", ["tokens64_requests64", "tokens65", "requests65"])
+def test_plan_inside_score_kernel_limits(shape):
+    """Batches of at most 64 tokens and 64 requests plan inside the score
+    kernel, larger ones in a launch of their own: batches just inside and
+    just outside both limits equal the oracle on every token and score."""
+    single = tuple((1, 300 + 37 * i) for i in range(63))
+    requests = {"tokens64_requests64": single + ((1, 2700),),
+                "tokens65": single + ((2, 2700),),
+                "requests65": single + ((1, 2700), (0, 40))}[shape]
+    pb = small_problem(331, ratio=1, N=64, mode=2, topk=128, cb=64, requests=requests)
+    say(f"{shape}: {pb.num_tokens} tokens, {pb.batch} requests")
+    res = run_gpu(pb, debug=True)
+    orc = oracle_rows(pb, scores=True)
+    compare(pb, res, orc)
+
+
 def test_consumer_mostly_invalid_candidates():
     """Consumer tokens whose incoming lists are mostly -1: the plan bounds the
     work by the list width, the prepared eligible count is far smaller, and
