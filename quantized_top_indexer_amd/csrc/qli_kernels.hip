@@ -782,6 +782,64 @@ __device__ __forceinline__ void plan_body(const KArgs& a, const Meta& m, uint32_
   }
 }
 
+// Every request holds exactly one query token (qsl[b] = b for b <= B, B <=
+// 64) and the slice's tokens are requests' tokens (t_base + T <= B): the
+// usual decode batch.  Every wave evaluates it (same result).
+__device__ __forceinline__ bool plan_one_token_per_request(const KArgs& a, const Meta& m) {
+  const int lane = threadIdx.x & 63;
+  const bool ok = (lane > a.B || m.qsl[lane] == lane) && (a.B < 64 || m.qsl[64] == 64);
+  return __ballot(ok) == ~0ull && a.t_base + a.T <= a.B;
+}
+
+// The plan of a batch whose requests hold one token each, for the one
+// workgroup plan_wg (the same lists and start entry as plan_body): token t
+// (lane t of wave 0) is request t_base + t, a single group of ceil(V/256)
+// units; the unit prefix is one wave scan, and the group holding unit
+// floor(w U / W) is found with one ballot.
+__device__ void plan_single_tokens(const KArgs& a, const Meta& m) {
+  if (threadIdx.x >= 64) return;
+  const int t = threadIdx.x;
+  const int T = a.T;
+  const bool in = t < T;
+  Group g{};
+  uint32_t units = 0;
+  if (in) {
+    const int b = t + a.t_base;
+    const ReqView r = request_view(a, m, b, true);
+    g = make_group(a, b, r, t, b, 1);
+    units = static_cast<uint32_t>(g.nch);
+    a.tokv[2 * t] = g.n0;
+  }
+  const uint32_t incl = wave_inclusive_scan(units);
+  const uint32_t excl = incl - units;
+  const uint32_t U = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
+  if (in) {
+    a.groups[T + t] = g;                        // list 1 (single groups)
+    a.ustart[(T + 1) + t] = static_cast<int32_t>(excl);
+  }
+  if (t == 0) {
+    a.ustart[0] = 0;                            // list 0 is empty
+    a.ustart[(T + 1) + T] = static_cast<int32_t>(U);
+  }
+  const int W = a.score_grid;
+  const int w = a.plan_wg;
+  const int64_t lo = floor_div(static_cast<int64_t>(w) * U, W);
+  const bool holds = in && units > 0 && excl <= lo && lo < excl + units;
+  const uint64_t mask = __ballot(holds);
+  if (mask != 0 && t == __builtin_ctzll(mask)) {
+    WgStart st;
+    st.grp = g;
+    st.list = 1;
+    st.ng = T;
+    st.g = t;
+    st.c = static_cast<int>(lo - excl);
+    st.unit = static_cast<int>(lo);
+    st.hi = static_cast<int>(floor_div(static_cast<int64_t>(w + 1) * U, W));
+    st.pad[0] = st.pad[1] = 0;
+    a.wgs[0] = st;
+  }
+}
+
 // PT threads (a consumer-prep workgroup, a plan workgroup, one wave for
 // small batches, where no cross-wave barrier is needed, or a score
 // workgroup planning for itself).  The metadata of up to NREQ requests is
@@ -811,7 +869,12 @@ __device__ void plan_role(const KArgs& a, uint32_t* lds) {
       }
     }
     __syncthreads();
-    plan_body<PT>(a, Meta{s_qsl, s_klen, a.smod ? s_smod : nullptr}, sh);
+    const Meta m{s_qsl, s_klen, a.smod ? s_smod : nullptr};
+    if (a.plan_wg >= 0 && a.multi_grid == 0 && a.B <= 64 && plan_one_token_per_request(a, m)) {
+      plan_single_tokens(a, m);  // wave 0; the caller's barrier publishes the lists
+      return;
+    }
+    plan_body<PT>(a, m, sh);
   } else {
     plan_body<PT>(a, global_meta(a), sh);
   }
