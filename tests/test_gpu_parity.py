@@ -542,19 +542,24 @@ def test_select_length_classes(mode, policy):
     compare(pb, gpu, orc, tokens=tok, scores=False)
 
 
-@pytest.mark.parametrize("mode,ratio,N,slice_tokens", [(2, 2, 32, 3), (1, 1, 64, 5), (3, 2, 32, 2),
-                                                       (2, 1, 64, 7)])
-def test_sliced_workspace(mode, ratio, N, slice_tokens):
+@pytest.mark.parametrize("mode,ratio,N,slice_tokens,shape", [(2, 2, 32, 3, "mixed"), (1, 1, 64, 5, "mixed"),
+                                                             (3, 2, 32, 2, "mixed"), (2, 1, 64, 7, "mixed"),
+                                                             (2, 1, 64, 7, "one_token_each"),
+                                                             (1, 2, 32, 6, "one_token_each")])
+def test_sliced_workspace(mode, ratio, N, slice_tokens, shape):
     """A workspace that holds a slice of only a few tokens: the call runs
     slice by slice (4-token groups cut by a slice boundary are scored as
-    single tokens) and gives the oracle's outputs and scores bit for bit,
-    the same as the unsliced call."""
+    single tokens; with one token per request, every slice after the first
+    plans for requests that start past its first token) and gives the
+    oracle's outputs and scores bit for bit, the same as the unsliced call."""
     import torch
 
     import quantized_top_indexer_amd as Q
     from qli_workloads.device import call_kwargs, to_device
+    requests = (((9, 3000), (5, 1100), (1, 1), (6, 2049), (2, 40)) if shape == "mixed"
+                else tuple((1, 300 + 97 * i) for i in range(20)))
     pb = small_problem(370 + mode + ratio + N, ratio=ratio, N=N, mode=mode, topk=120, cb=64, cb_in=128,
-                       requests=((9, 3000), (5, 1100), (1, 1), (6, 2049), (2, 40)))
+                       requests=requests)
     say(f"sliced {pb.name}: T={pb.num_tokens} L={pb.max_k_len} slice={slice_tokens}")
     whole = run_gpu(pb, debug=True)
     dev = to_device(pb, "cuda")
