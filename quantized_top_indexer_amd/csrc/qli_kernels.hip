@@ -298,6 +298,18 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
   return v;
 }
 
+// Running maximum over the lanes of a wave (values >= 0), in the steps of
+// the prefix sum above.
+__device__ __forceinline__ uint32_t wave_inclusive_max(uint32_t v) {
+  v = max(v, dpp_or0<0x111, 0xF>(v));
+  v = max(v, dpp_or0<0x112, 0xF>(v));
+  v = max(v, dpp_or0<0x114, 0xF>(v));
+  v = max(v, dpp_or0<0x118, 0xF>(v));
+  v = max(v, dpp_or0<0x142, 0xA>(v));
+  v = max(v, dpp_or0<0x143, 0xC>(v));
+  return v;
+}
+
 // op over the 64 lanes (result in every lane): butterflies within each row,
 // then the four row values.
 template <class Op>
@@ -386,7 +398,8 @@ __device__ __forceinline__ void prep_write(const KArgs& a, int t, int b, int V, 
 constexpr int kPlanLdsRequests = 4096;  // metadata of up to this many requests is staged in LDS
 template <int PT, int NREQ = kPlanLdsRequests>
 __device__ void plan_role(const KArgs& a, uint32_t* lds);
-constexpr int kPlanLdsWords = 3 * kPlanLdsRequests + 1 + 64;
+// request metadata, scan scratch, one mark per score workgroup
+constexpr int kPlanLdsWords = 3 * kPlanLdsRequests + 1 + 64 + kMaxScoreWGs;
 constexpr int kPrepLdsWords = kPrepBitmapWords + QLI_MAX_CAND_BLOCKS + 64 + 1;
 constexpr int kConsumerLdsWords = kPrepLdsWords > kPlanLdsWords ? kPrepLdsWords : kPlanLdsWords;
 
@@ -623,55 +636,146 @@ __device__ __forceinline__ void block_exclusive_scan_n(uint32_t (&v)[N], uint32_
 // [floor(w*U/nw), floor((w+1)*U/nw)).
 struct Split {
   int list, ng, NT, nw, U, base;
-  int q, r;  // U = q*nw + r
 };
+
+// First item of a workgroup whose range starts at unit lo, in group gidx
+// (first unit unit0): the first of the group's items (starts unit0 + c*NT)
+// at or past lo.
+__device__ __forceinline__ WgStart start_entry_of(const Split& sp, int gidx, const Group& g, int unit0, int lo,
+                                                  int hi) {
+  const int off = lo - unit0;
+  const int c = off <= 0 ? 0 : (sp.NT == 1 ? off : (off + 3) >> 2);  // NT is 1 or 4
+  WgStart st;
+  st.grp = g;
+  st.list = sp.list;
+  st.ng = sp.ng;
+  st.g = gidx;
+  st.c = c;
+  st.unit = unit0 + c * sp.NT;
+  st.hi = hi;
+  st.pad[0] = st.pad[1] = 0;
+  return st;
+}
 
 // Every group of a list has the same token count NT, so group g (units
 // [a, a + nch*NT)) holds the first item of exactly the workgroups whose
-// range starts in (a - NT, a + (nch - 1)*NT]; the thread that writes g
-// writes their entries.  Consecutive range starts differ by q or q + 1.
-__device__ void write_starts(const KArgs& a, const Split& sp, int gidx, const Group& g, int unit0) {
+// range starts in (a - NT, a + (nch - 1)*NT].  A workgroup that plans for
+// itself (plan_wg) keeps its own entry, written by the thread that writes
+// the group holding it.
+__device__ void write_own_start(const KArgs& a, const Split& sp, int gidx, const Group& g, int unit0) {
+  const int w = a.plan_wg - sp.base;
+  if (w < 0 || w >= sp.nw) return;
+  const int lo = static_cast<int>(floor_div(static_cast<int64_t>(w) * sp.U, sp.nw));
+  const int64_t e = unit0 + static_cast<int64_t>(g.nch - 1) * sp.NT;
+  if (lo <= unit0 - sp.NT || lo > e) return;
+  const int hi = static_cast<int>(floor_div(static_cast<int64_t>(w + 1) * sp.U, sp.nw));
+  a.wgs[0] = start_entry_of(sp, gidx, g, unit0, lo, hi);
+}
+
+// A whole-grid plan (plan_wg < 0): the thread that writes group g (index
+// gidx in its list) also writes the entry of the first workgroup whose range
+// starts inside it, if any, and marks it: own[base + w] = rank + 1, where
+// rank orders the groups of list 0 and then those of list 1.  Ownership is
+// contiguous, so the running maximum of the marks gives every later
+// workgroup of the group its group.
+__device__ __forceinline__ void mark_start(const KArgs& a, const Split& sp, int gidx, int rank, const Group& g,
+                                           int unit0, uint32_t* own) {
   const int NT = sp.NT, nw = sp.nw;
-  const int64_t e = unit0 + static_cast<int64_t>(g.nch - 1) * NT;
   const int w0 = static_cast<int>(ceil_div((static_cast<int64_t>(unit0) - NT + 1) * nw, sp.U));
-  const int w1 = static_cast<int>(min(static_cast<int64_t>(nw), ceil_div((e + 1) * nw, sp.U)));
-  if (w0 >= w1) return;
-  int wa = w0, wb = w1;
-  if (a.plan_wg >= 0) {  // only workgroup plan_wg's entry is wanted
-    const int w = a.plan_wg - sp.base;
-    if (w < w0 || w >= w1) return;
-    wa = w;
-    wb = w + 1;
+  if (w0 >= nw) return;
+  const int lo = static_cast<int>(floor_div(static_cast<int64_t>(w0) * sp.U, nw));
+  if (lo > unit0 + static_cast<int64_t>(g.nch - 1) * NT) return;
+  const int hi = static_cast<int>(floor_div(static_cast<int64_t>(w0 + 1) * sp.U, nw));
+  a.wgs[sp.base + w0] = start_entry_of(sp, gidx, g, unit0, lo, hi);
+  own[sp.base + w0] = static_cast<uint32_t>(rank + 1);
+}
+
+// The start entries of the unmarked score workgroups (see mark_start), once
+// the lists are in memory: a running maximum over the W marks in LDS
+// (contiguous spans per thread; own[e] becomes 2 max + marked), then each
+// thread takes K entries per round, their loads of the group and its first
+// unit issued together.  A workgroup of a list (nw workgroups over U units)
+// whose range starts past the list's last item start (lo + NT > U) has no
+// work.
+template <int PT>
+__device__ void write_all_starts(const KArgs& a, const Split& s0, const Split& s1, uint32_t* own, uint32_t* sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NW = PT / 64;
+  const int W = s0.nw + s1.nw;
+  const int C = (W + PT - 1) / PT;
+  const int e_lo = min(W, tid * C), e_hi = min(W, e_lo + C);
+  uint32_t m = 0;
+  for (int e = e_lo; e < e_hi; ++e) m = max(m, own[e]);
+  // maximum over the threads before this one
+  const uint32_t inc = wave_inclusive_max(m);
+  if constexpr (NW > 1) {
+    if (lane == 63) sh[wave] = inc;
+    __syncthreads();
   }
-  const int64_t p0 = static_cast<int64_t>(wa) * sp.U;
-  int lo = static_cast<int>(floor_div(p0, nw));
-  int rem = static_cast<int>(p0 - static_cast<int64_t>(lo) * nw);
-  for (int w = wa; w < wb; ++w) {
-    const int carry = rem + sp.r >= nw ? 1 : 0;
-    const int hi = lo + sp.q + carry;
-    rem = rem + sp.r - carry * nw;
-    const int off = lo - unit0;
-    const int c = off <= 0 ? 0 : (NT == 1 ? off : (off + 3) >> 2);  // NT is 1 or 4
-    WgStart st;
-    st.grp = g;
-    st.list = sp.list;
-    st.ng = sp.ng;
-    st.g = gidx;
-    st.c = c;
-    st.unit = unit0 + c * NT;
-    st.hi = hi;
-    st.pad[0] = st.pad[1] = 0;
-    if (a.plan_wg < 0) a.wgs[sp.base + w] = st;
-    else if (sp.base + w == a.plan_wg) a.wgs[0] = st;
-    lo = hi;
+  uint32_t before = static_cast<uint32_t>(__shfl_up(static_cast<int>(inc), 1));
+  if (lane == 0) before = 0;
+#pragma unroll
+  for (int w = 0; w < NW - 1; ++w)
+    if (w < wave) before = max(before, sh[w]);
+  for (int e = e_lo; e < e_hi; ++e) {
+    const uint32_t v = own[e];
+    before = max(before, v);
+    own[e] = 2 * before + (v != 0 ? 1u : 0u);
+  }
+  __syncthreads();
+  constexpr int K = PT >= 1024 ? 2 : 8;
+  for (int e0 = tid; e0 < W; e0 += K * PT) {
+    int l[K], g[K], lo[K];
+    bool live[K], done[K];
+    Group grp[K];
+    int u0[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int e = e0 + k * PT;
+      l[k] = e >= s0.nw ? 1 : 0;
+      const Split& s = l[k] ? s1 : s0;
+      lo[k] = 0;
+      g[k] = 0;
+      live[k] = false;
+      done[k] = true;
+      if (e < W) {
+        const uint32_t x = own[e];
+        done[k] = (x & 1u) != 0;  // written with its group
+        lo[k] = static_cast<int>(floor_div(static_cast<int64_t>(e - s.base) * s.U, s.nw));
+        live[k] = !done[k] && lo[k] + s.NT <= s.U;
+        g[k] = static_cast<int>(x >> 1) - 1 - (l[k] ? s0.ng : 0);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (live[k]) {
+        grp[k] = a.groups[static_cast<int64_t>(l[k]) * a.T + g[k]];
+        u0[k] = a.ustart[static_cast<int64_t>(l[k]) * (a.T + 1) + g[k]];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int e = e0 + k * PT;
+      if (done[k]) continue;
+      const Split& s = l[k] ? s1 : s0;
+      WgStart st = {};
+      st.g = -1;
+      if (live[k]) {
+        const int hi = static_cast<int>(floor_div(static_cast<int64_t>(e - s.base + 1) * s.U, s.nw));
+        st = start_entry_of(s, g[k], grp[k], u0[k], lo[k], hi);
+      }
+      a.wgs[e] = st;
+    }
   }
 }
 
-
 // The plan proper, on request metadata m (an LDS copy or global memory), by
-// PT threads.
-template <int PT>
-__device__ __forceinline__ void plan_body(const KArgs& a, const Meta& m, uint32_t* sh) {
+// PT threads.  A plan for the whole grid (plan_wg < 0, GRID) marks the
+// workgroups' first groups in own (kMaxScoreWGs LDS words, zero on entry)
+// and writes the start entries after the lists; a workgroup planning for
+// itself (plan_wg >= 0) keeps its own entry only.
+template <int PT, bool GRID>
+__device__ __forceinline__ void plan_body(const KArgs& a, const Meta& m, uint32_t* sh, uint32_t* own) {
   const int tid = threadIdx.x;
   const int T = a.T;
   const int per = (T + PT - 1) / PT;
@@ -722,8 +826,6 @@ __device__ __forceinline__ void plan_body(const KArgs& a, const Meta& m, uint32_
     sp.nw = l == 0 ? Wm : W - Wm;
     sp.U = static_cast<int>(tot[2 * l + 1]);
     sp.base = l == 0 ? 0 : Wm;
-    sp.q = sp.nw > 0 ? sp.U / sp.nw : 0;
-    sp.r = sp.nw > 0 ? sp.U - sp.q * sp.nw : 0;
     return sp;
   };
   const Split sp0 = split(0), sp1 = split(1);
@@ -735,8 +837,11 @@ __device__ __forceinline__ void plan_body(const KArgs& a, const Meta& m, uint32_
       a.groups[l * T + gi] = g1c;
       a.ustart[l * (T + 1) + gi] = static_cast<int32_t>(ui);
       if (g1c.nch > 0) {
-        if (l == 0) write_starts(a, sp0, static_cast<int>(gi), g1c, static_cast<int>(ui));
-        else write_starts(a, sp1, static_cast<int>(gi), g1c, static_cast<int>(ui));
+        if (a.plan_wg >= 0)
+          write_own_start(a, l == 0 ? sp0 : sp1, static_cast<int>(gi), g1c, static_cast<int>(ui));
+        else if (GRID)
+          mark_start(a, l == 0 ? sp0 : sp1, static_cast<int>(gi), static_cast<int>(gi + (l == 0 ? 0u : tot[0])),
+                     g1c, static_cast<int>(ui), own);
       }
     }
   } else if (t_lo < t_hi) {
@@ -758,8 +863,11 @@ __device__ __forceinline__ void plan_body(const KArgs& a, const Meta& m, uint32_
       a.groups[l * T + gi] = g;
       a.ustart[l * (T + 1) + gi] = static_cast<int32_t>(ui);
       if (g.nch > 0) {
-        if (l == 0) write_starts(a, sp0, static_cast<int>(gi), g, static_cast<int>(ui));
-        else write_starts(a, sp1, static_cast<int>(gi), g, static_cast<int>(ui));
+        if (a.plan_wg >= 0)
+          write_own_start(a, l == 0 ? sp0 : sp1, static_cast<int>(gi), g, static_cast<int>(ui));
+        else if (GRID)
+          mark_start(a, l == 0 ? sp0 : sp1, static_cast<int>(gi), static_cast<int>(gi + (l == 0 ? 0u : tot[0])),
+                     g, static_cast<int>(ui), own);
       }
       const uint32_t units = static_cast<uint32_t>(g.nch * g.ntok);
       if (l == 0) {
@@ -779,6 +887,10 @@ __device__ __forceinline__ void plan_body(const KArgs& a, const Meta& m, uint32_
       }
       a.ustart[l * (T + 1) + tot[2 * l]] = static_cast<int32_t>(tot[2 * l + 1]);
     }
+  }
+  if (GRID && a.plan_wg < 0) {
+    __syncthreads();  // the lists and the marks are written
+    write_all_starts<PT>(a, sp0, sp1, own, sh);
   }
 }
 
@@ -843,22 +955,27 @@ __device__ void plan_single_tokens(const KArgs& a, const Meta& m) {
 // PT threads (a consumer-prep workgroup, a plan workgroup, one wave for
 // small batches, where no cross-wave barrier is needed, or a score
 // workgroup planning for itself).  The metadata of up to NREQ requests is
-// staged in LDS (3 NREQ + 65 words).
+// staged in LDS (3 NREQ + 65 words); a plan for the whole grid (the
+// default NREQ, kPlanLdsWords words) also keeps one mark per score
+// workgroup after them (a score workgroup planning for itself does not).
 template <int PT, int NREQ>
 __device__ void plan_role(const KArgs& a, uint32_t* lds) {
+  constexpr bool kGrid = NREQ == kPlanLdsRequests;
   int32_t* s_qsl = reinterpret_cast<int32_t*>(lds);
   int32_t* s_klen = s_qsl + NREQ + 1;
   int32_t* s_smod = s_klen + NREQ;
   uint32_t* sh = reinterpret_cast<uint32_t*>(s_smod + NREQ);
+  uint32_t* own = sh + 64;
   const int tid = threadIdx.x;
-  // every start entry begins as "no work" (the barriers below order these
-  // stores before the ones the plan writes); workgroups whose range starts
-  // past the last item of their list keep it
-  const int nent = a.plan_wg >= 0 ? 1 : a.multi_grid + a.score_grid;
-  for (int w = tid; w < nent; w += PT) {
+  if (kGrid && a.plan_wg < 0)
+    for (int w = tid; w < a.multi_grid + a.score_grid; w += PT) own[w] = 0;
+  // a workgroup that plans for itself begins with "no work" (the barriers
+  // below order this store before the plan's); a plan for the whole grid
+  // writes every entry after the lists
+  if (a.plan_wg >= 0 && tid == 0) {
     WgStart st = {};
     st.g = -1;
-    a.wgs[w] = st;
+    a.wgs[0] = st;
   }
   if (a.B <= NREQ) {
     for (int i = tid; i <= a.B; i += PT) {
@@ -874,9 +991,9 @@ __device__ void plan_role(const KArgs& a, uint32_t* lds) {
       plan_single_tokens(a, m);  // wave 0; the caller's barrier publishes the lists
       return;
     }
-    plan_body<PT>(a, m, sh);
+    plan_body<PT, kGrid>(a, m, sh, own);
   } else {
-    plan_body<PT>(a, global_meta(a), sh);
+    plan_body<PT, kGrid>(a, global_meta(a), sh, own);
   }
 }
 
