@@ -2200,14 +2200,101 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n, int cap
     }
   };
 
-  // range and count of the scores (keys other than 0 and the pin): the
-  // minimum is taken over key - 1, which sends the zero keys to the top;
-  // with a pin the maximum is taken over key + 1, which sends it to 0
-  uint32_t mn1 = 0xFFFFFFFFu, mx1 = 0, cnt = 0;
-  auto range = [&](const bool P) {
-    const uint32_t o = P ? 1u : 0u;
+  // the keys of this thread, as (key, index) pairs (reloading chunks)
+  auto each_reg = [&](auto f) {
     for (int ch = 0; ch < nch; ++ch) {
-      load(ch);
+      if (MULTI && nch > 1) load(ch);
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        if (j >= nvec) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f(kr[4 * j + e], index_of(ch, j, e));
+      }
+    }
+  };
+  // Bracket [blo, bhi] around the key of rank krem (from the top) from a
+  // sample: this thread's samples (each_sample(f) calls f(key)) go into
+  // 2048 bins over [lo, hi] (zero keys and the pin skipped); the bins
+  // holding the sample ranks rexp -+ (3 sqrt(rexp) + 4) bound it, where
+  // rexp = krem * samples / row_keys is the threshold's expected rank among
+  // them.  With open ends a bracket reaching the highest (lowest) sample
+  // also takes every key above (below) it.  All threads call it.
+  auto bracket = [&](auto each_sample, uint32_t lo, uint32_t hi, uint32_t krem, float row_keys, bool open,
+                     uint32_t& blo, uint32_t& bhi) {
+    const int bits0 = hi == lo ? 0 : 32 - __clz(static_cast<int>(hi - lo));
+    const int sft0 = max(0, bits0 - 11);
+    constexpr int BPT = 2048 / BS;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) hist[tid * BPT + j] = 0;
+    if (tid == 0) misc[4] = 0;
+    __syncthreads();
+    uint32_t ns = 0;
+    each_sample([&](uint32_t key) {
+      if (key != 0 && key != kPinKey) {
+        atomicAdd(&hist[(key - lo) >> sft0], 1u);
+        ++ns;
+      }
+    });
+    ns = wave_allreduce(ns, AddOp{});
+    if (lane == 0) atomicAdd(&misc[4], ns);
+    __syncthreads();
+    const uint32_t nsamp = misc[4];
+    const float rexp = static_cast<float>(krem) * static_cast<float>(nsamp) / row_keys;
+    const float dev = 3.0f * sqrtf(rexp) + 4.0f;
+    const uint32_t r_hi = static_cast<uint32_t>(max(0.0f, rexp - dev));  // keys above the bracket
+    const uint32_t r_lo = static_cast<uint32_t>(min(static_cast<float>(nsamp), rexp + dev));
+    uint32_t c = 0;
+    uint32_t hv[BPT];
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      hv[j] = hist[tid * BPT + j];
+      c += hv[j];
+    }
+    uint32_t total;
+    const uint32_t excl = block_exclusive_scan<BS>(c, &total, sh);
+    const uint32_t above_t = total - excl - c;
+    // bin holding sample rank r (counted from the top, 0-based) -> misc[slot]
+    auto find = [&](uint32_t r, int slot) {
+      if (above_t <= r && r < above_t + c) {
+        uint32_t cum = above_t;
+        for (int j = BPT - 1; j >= 0; --j) {
+          if (cum + hv[j] > r) {
+            misc[slot] = static_cast<uint32_t>(tid * BPT + j);
+            break;
+          }
+          cum += hv[j];
+        }
+      }
+    };
+    if (tid == 0) {
+      misc[5] = 2047;  // r_hi above every sample: bracket reaches the top
+      misc[6] = 0;     // r_lo below every sample: bracket reaches lo
+    }
+    __syncthreads();
+    if (r_hi < total) find(r_hi, 5);
+    if (r_lo < total) find(r_lo, 6);
+    __syncthreads();
+    const uint32_t b_top = r_hi < total ? misc[5] : 2047u;
+    const uint32_t b_bot = r_lo < total ? misc[6] : 0u;
+    blo = lo + (b_bot << sft0);
+    bhi = static_cast<uint32_t>(
+        min(static_cast<uint64_t>(hi), static_cast<uint64_t>(lo) + ((static_cast<uint64_t>(b_top) + 1) << sft0) - 1));
+    if (open) {
+      if (r_hi == 0) bhi = kPinKey - 1;
+      if (r_lo + 1 >= total) blo = 1;
+    }
+  };
+
+  // threshold: keys > thr are taken, then the first `need` keys == thr
+  uint32_t thr = 0, need = 0;
+  if constexpr (!MULTI) {
+    // range and count of the scores (keys other than 0 and the pin): the
+    // minimum is taken over key - 1, which sends the zero keys to the top;
+    // with a pin the maximum is taken over key + 1, which sends it to 0
+    uint32_t mn1 = 0xFFFFFFFFu, mx1 = 0, cnt = 0;
+    auto range = [&](const bool P) {
+      const uint32_t o = P ? 1u : 0u;
+      load(0);
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
         if (j >= nvec) continue;
@@ -2219,157 +2306,221 @@ __device__ __forceinline__ void select_topk(const uint32_t* keys, int n, int cap
         cnt += min(v0, 1u) + min(v1, 1u);
         cnt += min(v2, 1u) + min(v3, 1u);
       }
+    };
+    if (pinned) range(true);
+    else range(false);
+    mn1 = wave_allreduce(mn1, MinOp{});
+    mx1 = wave_allreduce(mx1, MaxOp{});
+    cnt = wave_allreduce(cnt, AddOp{});
+    if (lane == 0) {
+      sh[wave] = mn1;
+      sh[16 + wave] = mx1;
+      sh[32 + wave] = cnt;
     }
-  };
-  if (pinned) range(true);
-  else range(false);
-  mn1 = wave_allreduce(mn1, MinOp{});
-  mx1 = wave_allreduce(mx1, MaxOp{});
-  cnt = wave_allreduce(cnt, AddOp{});
-  if (lane == 0) {
-    sh[wave] = mn1;
-    sh[16 + wave] = mx1;
-    sh[32 + wave] = cnt;
-  }
-  __syncthreads();
-  mn1 = sh[0];
-  mx1 = sh[16];
-  cnt = sh[32];
+    __syncthreads();
+    mn1 = sh[0];
+    mx1 = sh[16];
+    cnt = sh[32];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) {
-    mn1 = min(mn1, sh[w]);
-    mx1 = max(mx1, sh[16 + w]);
-    cnt += sh[32 + w];
-  }
-  __syncthreads();
-  cnt -= pinned ? 1u : 0u;  // the pin was counted as a key
-  const uint32_t mn = cnt == 0 ? 0xFFFFFFFFu : mn1 + 1u;
-  const uint32_t mx = cnt == 0 ? 0u : mx1 - (pinned ? 1u : 0u);
+    for (int w = 1; w < NW; ++w) {
+      mn1 = min(mn1, sh[w]);
+      mx1 = max(mx1, sh[16 + w]);
+      cnt += sh[32 + w];
+    }
+    __syncthreads();
+    cnt -= pinned ? 1u : 0u;  // the pin was counted as a key
+    const uint32_t mn = cnt == 0 ? 0xFFFFFFFFu : mn1 + 1u;
+    const uint32_t mx = cnt == 0 ? 0u : mx1 - (pinned ? 1u : 0u);
 
-  // threshold: keys > thr are taken, then the first `need` keys == thr
-  uint32_t thr = 0, need = 0;
-  if (cnt + (pinned ? 1u : 0u) > static_cast<uint32_t>(k)) {
-    uint32_t krem = static_cast<uint32_t>(k) - (pinned ? 1u : 0u);
-    if (krem == 0) {
-      thr = kPinKey - 1;
-    } else {
-      // the keys of this thread, as (key, index) pairs (reloading chunks)
-      auto each_reg = [&](auto f) {
-        for (int ch = 0; ch < nch; ++ch) {
-          if (MULTI && nch > 1) load(ch);
+    if (cnt + (pinned ? 1u : 0u) > static_cast<uint32_t>(k)) {
+      uint32_t krem = static_cast<uint32_t>(k) - (pinned ? 1u : 0u);
+      if (krem == 0) {
+        thr = kPinKey - 1;
+      } else {
+        bool done = false;
+        if (cnt >= static_cast<uint32_t>(kSelSampleMin)) {
+          // Two keys per thread bound a bracket; one counting sweep checks
+          // that the threshold lies inside; its keys (about 4 % of the row)
+          // are gathered and searched alone.
+          uint32_t blo, bhi;
+          bracket([&](auto f) {
 #pragma unroll
-          for (int j = 0; j < VPT; ++j) {
-            if (j >= nvec) continue;
+                    for (int r = 0; r < 4 * VPT; r += 2 * VPT) f(kr[r]);
+                  },
+                  mn, mx, krem, static_cast<float>(cnt), false, blo, bhi);
+          // keys above the bracket and inside it, packed above << 16 | inside
+          // (a chunk holds at most 32768 keys); the prefix places the gather
+          // (the pin, if any, lies above bhi and is not counted)
+          uint32_t above = 0, inb = 0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) f(kr[4 * j + e], index_of(ch, j, e));
+          for (int r = 0; r < 4 * VPT; ++r) {
+            const uint32_t key = kr[r];
+            above += key > bhi ? 1u : 0u;
+            inb += key - blo <= bhi - blo ? 1u : 0u;
           }
-        }
-      };
-      bool done = false;
-      if (!MULTI && cnt >= static_cast<uint32_t>(kSelSampleMin)) {
-        // Bracket from a sample: two keys per thread go into a histogram
-        // over [mn, mx]; the bins around the sample's estimate of the
-        // threshold rank (+-3 sigma) give a key range [blo, bhi].  One
-        // counting sweep checks that the threshold lies inside; its keys
-        // (about 4 % of the row) are gathered and searched alone.
-        const int bits0 = mx == mn ? 0 : 32 - __clz(static_cast<int>(mx - mn));
-        const int sft0 = max(0, bits0 - 11);
-        constexpr int BPT = 2048 / BS;
+          uint32_t tot2;
+          uint32_t at = block_exclusive_scan<BS>((above << 16) | inb, &tot2, sh) & 0xFFFFu;
+          const uint32_t n_above = (tot2 >> 16) - (pinned ? 1u : 0u), n_in = tot2 & 0xFFFFu;
+          if (n_above < krem && n_above + n_in >= krem && n_in <= static_cast<uint32_t>(sel_cand(BS))) {
+            // gather the bracket's keys and search them alone
 #pragma unroll
-        for (int j = 0; j < BPT; ++j) hist[tid * BPT + j] = 0;
-        if (tid == 0) misc[4] = 0;
-        __syncthreads();
-        uint32_t ns = 0;
+            for (int j = 0; j < VPT; ++j)
 #pragma unroll
-        for (int r = 0; r < 4 * VPT; r += 2 * VPT) {
-          const uint32_t key = kr[r];
-          if (key != 0 && key != kPinKey) {
-            atomicAdd(&hist[(key - mn) >> sft0], 1u);
-            ++ns;
-          }
-        }
-        ns = wave_allreduce(ns, AddOp{});
-        if (lane == 0) atomicAdd(&misc[4], ns);
-        __syncthreads();
-        const uint32_t nsamp = misc[4];
-        // expected rank of the threshold among the samples, from the top
-        const float rexp = static_cast<float>(krem) * static_cast<float>(nsamp) / static_cast<float>(cnt);
-        const float dev = 3.0f * sqrtf(rexp) + 4.0f;
-        const uint32_t r_hi = static_cast<uint32_t>(max(0.0f, rexp - dev));      // keys above the bracket
-        const uint32_t r_lo = static_cast<uint32_t>(min(static_cast<float>(nsamp), rexp + dev));
-        uint32_t c = 0;
-        uint32_t hv[BPT];
-#pragma unroll
-        for (int j = 0; j < BPT; ++j) {
-          hv[j] = hist[tid * BPT + j];
-          c += hv[j];
-        }
-        uint32_t total;
-        const uint32_t excl = block_exclusive_scan<BS>(c, &total, sh);
-        const uint32_t above_t = total - excl - c;
-        // bin holding sample rank r (counted from the top, 0-based) -> misc[slot]
-        auto find = [&](uint32_t r, int slot) {
-          if (above_t <= r && r < above_t + c) {
-            uint32_t cum = above_t;
-            for (int j = BPT - 1; j >= 0; --j) {
-              if (cum + hv[j] > r) {
-                misc[slot] = static_cast<uint32_t>(tid * BPT + j);
-                break;
+              for (int e = 0; e < 4; ++e) {
+                const uint32_t key = kr[4 * j + e];
+                if (key - blo <= bhi - blo) {
+                  ck[at] = key;
+                  ci[at] = static_cast<uint32_t>(index_of(0, j, e));
+                  ++at;
+                }
               }
-              cum += hv[j];
-            }
+            __syncthreads();
+            auto each_cand = [&](auto f) {
+              for (uint32_t i = tid; i < n_in; i += BS) f(ck[i], static_cast<int>(ci[i]));
+            };
+            krem -= n_above;
+            refine(each_cand, blo, bhi, krem, thr, need);
+            done = true;
           }
-        };
-        if (tid == 0) {
-          misc[5] = 2047;  // r_hi above every sample: bracket reaches the top
-          misc[6] = 0;     // r_lo below every sample: bracket reaches mn
+          __syncthreads();  // sh, misc and the candidate lists are reused
         }
-        __syncthreads();
-        if (r_hi < total) find(r_hi, 5);
-        if (r_lo < total) find(r_lo, 6);
-        __syncthreads();
-        const uint32_t b_top = r_hi < total ? misc[5] : 2047u;
-        const uint32_t b_bot = r_lo < total ? misc[6] : 0u;
-        const uint32_t blo = mn + (b_bot << sft0);
-        const uint32_t bhi = static_cast<uint32_t>(
-            min(static_cast<uint64_t>(mx), static_cast<uint64_t>(mn) + ((static_cast<uint64_t>(b_top) + 1) << sft0) - 1));
-        // keys above the bracket and inside it, packed above << 16 | inside
-        // (a chunk holds at most 32768 keys); the prefix places the gather
-        // (the pin, if any, lies above bhi and is not counted)
-        uint32_t above = 0, inb = 0;
-#pragma unroll
-        for (int r = 0; r < 4 * VPT; ++r) {
-          const uint32_t key = kr[r];
-          above += key > bhi ? 1u : 0u;
-          inb += key - blo <= bhi - blo ? 1u : 0u;
-        }
-        uint32_t tot2;
-        uint32_t at = block_exclusive_scan<BS>((above << 16) | inb, &tot2, sh) & 0xFFFFu;
-        const uint32_t n_above = (tot2 >> 16) - (pinned ? 1u : 0u), n_in = tot2 & 0xFFFFu;
-        if (n_above < krem && n_above + n_in >= krem && n_in <= static_cast<uint32_t>(sel_cand(BS))) {
-          // gather the bracket's keys and search them alone
-#pragma unroll
-          for (int j = 0; j < VPT; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const uint32_t key = kr[4 * j + e];
-              if (key - blo <= bhi - blo) {
-                ck[at] = key;
-                ci[at] = static_cast<uint32_t>(index_of(0, j, e));
-                ++at;
-              }
-            }
-          __syncthreads();
-          auto each_cand = [&](auto f) {
-            for (uint32_t i = tid; i < n_in; i += BS) f(ck[i], static_cast<int>(ci[i]));
-          };
-          krem -= n_above;
-          refine(each_cand, blo, bhi, krem, thr, need);
-          done = true;
-        }
-        __syncthreads();  // sh, misc and the candidate lists are reused
+        if (!done) refine(each_reg, mn, mx, krem, thr, need);
       }
-      if (!done) refine(each_reg, mn, mx, krem, thr, need);
+    }
+  } else {
+    // Chunked rows (every radix pass over them would read them again):
+    // (1) a sample of the row, one key of one 16-byte vector per thread in
+    // each of up to SPT chunks spread over the row (in the bracket gather's
+    // LDS), bounds a bracket; (2) one sweep over the row counts the keys
+    // above it (and the row's range and count), gathers the keys inside it
+    // and (3) the search runs on those alone when the threshold lies inside
+    // and they fit, else on the whole row.  With the compaction the row is
+    // read about 2.1 times instead of once per radix pass and twice besides.
+    constexpr int SPT = 2 * sel_cand(BS) / BS;
+    const int sstride = (nch + SPT - 1) / SPT;
+    const int nsl = (nch + sstride - 1) / sstride;
+    uint32_t* samp = ck;
+    i32x4 xs[SPT];
+#pragma unroll
+    for (int s = 0; s < SPT; ++s)  // every load issued before the first use
+      xs[s] = *reinterpret_cast<const i32x4*>(keys + min(index_of(min(s, nsl - 1) * sstride, 0, 0), cap - 4));
+    uint32_t smn = 0xFFFFFFFFu, smx = 0, sv = 0, snz = 0;
+#pragma unroll
+    for (int s = 0; s < SPT; ++s) {
+      if (s >= nsl) continue;
+      const int idx = index_of(s * sstride, 0, 0) + (s & 3);
+      uint32_t key = static_cast<uint32_t>(xs[s][s & 3]);
+      const bool valid = idx < n && idx != pin;
+      key = valid ? key : 0u;
+      sv += valid ? 1u : 0u;
+      if (key != 0) {
+        smn = min(smn, key);
+        smx = max(smx, key);
+        ++snz;
+      }
+      samp[s * BS + tid] = key;
+    }
+    smn = wave_allreduce(smn, MinOp{});
+    smx = wave_allreduce(smx, MaxOp{});
+    sv = wave_allreduce(sv, AddOp{});
+    snz = wave_allreduce(snz, AddOp{});
+    if (lane == 0) {
+      sh[wave] = smn;
+      sh[16 + wave] = smx;
+      sh[32 + wave] = sv;
+      sh[48 + wave] = snz;
+    }
+    __syncthreads();
+    smn = sh[0];
+    smx = sh[16];
+    sv = sh[32];
+    snz = sh[48];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      smn = min(smn, sh[w]);
+      smx = max(smx, sh[16 + w]);
+      sv += sh[32 + w];
+      snz += sh[48 + w];
+    }
+    __syncthreads();
+    const uint32_t krem0 = static_cast<uint32_t>(k) - (pinned ? 1u : 0u);
+    uint32_t blo = 1, bhi = kPinKey - 1;
+    if (snz > 0 && krem0 > 0)
+      bracket([&](auto f) {
+                for (int s = 0; s < nsl; ++s) f(samp[s * BS + tid]);
+              },
+              smn, smx, krem0, static_cast<float>(snz) * static_cast<float>(n) / static_cast<float>(sv), true,
+              blo, bhi);
+    // (2) the sweep
+    if (tid == 0) misc[7] = 0;
+    __syncthreads();  // the samples are consumed: the gather may overwrite them
+    const uint32_t o = pinned ? 1u : 0u;
+    uint32_t mn1 = 0xFFFFFFFFu, mx1 = 0, cnt = 0, above = 0;
+    for (int ch = 0; ch < nch; ++ch) {
+      load(ch);
+#pragma unroll
+      for (int j = 0; j < VPT; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = kr[4 * j + e];
+          mx1 = max(mx1, key + o);
+          mn1 = min(mn1, key - 1u);
+          cnt += min(key, 1u);
+          above += key > bhi ? 1u : 0u;
+          const bool in = key - blo <= bhi - blo;
+          const uint64_t mk = __ballot(in);
+          if (mk != 0) {  // one LDS counter step per wave
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&misc[7], static_cast<uint32_t>(__popcll(mk)));
+            base = static_cast<uint32_t>(__shfl(static_cast<int>(base), 0));
+            const uint32_t slot = base + static_cast<uint32_t>(__popcll(mk & ((1ull << lane) - 1ull)));
+            if (in && slot < static_cast<uint32_t>(sel_cand(BS))) {
+              ck[slot] = key;
+              ci[slot] = static_cast<uint32_t>(index_of(ch, j, e));
+            }
+          }
+        }
+    }
+    mn1 = wave_allreduce(mn1, MinOp{});
+    mx1 = wave_allreduce(mx1, MaxOp{});
+    cnt = wave_allreduce(cnt, AddOp{});
+    above = wave_allreduce(above, AddOp{});
+    if (lane == 0) {
+      sh[wave] = mn1;
+      sh[16 + wave] = mx1;
+      sh[32 + wave] = cnt;
+      sh[48 + wave] = above;
+    }
+    __syncthreads();
+    mn1 = sh[0];
+    mx1 = sh[16];
+    cnt = sh[32];
+    above = sh[48];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      mn1 = min(mn1, sh[w]);
+      mx1 = max(mx1, sh[16 + w]);
+      cnt += sh[32 + w];
+      above += sh[48 + w];
+    }
+    const uint32_t n_in = misc[7];
+    __syncthreads();
+    cnt -= pinned ? 1u : 0u;  // the pin was counted as a key and as above
+    above -= pinned ? 1u : 0u;
+    const uint32_t mn = cnt == 0 ? 0xFFFFFFFFu : mn1 + 1u;
+    const uint32_t mx = cnt == 0 ? 0u : mx1 - (pinned ? 1u : 0u);
+    // (3) the search
+    if (cnt + (pinned ? 1u : 0u) > static_cast<uint32_t>(k)) {
+      if (krem0 == 0) {
+        thr = kPinKey - 1;
+      } else if (above < krem0 && above + n_in >= krem0 && n_in <= static_cast<uint32_t>(sel_cand(BS))) {
+        auto each_cand = [&](auto f) {
+          for (uint32_t i = tid; i < n_in; i += BS) f(ck[i], static_cast<int>(ci[i]));
+        };
+        refine(each_cand, blo, bhi, krem0 - above, thr, need);
+      } else {
+        refine(each_reg, mn, mx, krem0, thr, need);
+      }
     }
   }
 
