@@ -152,6 +152,71 @@ def test_sampled_bracket_selection(mode, patterns):
             assert np.count_nonzero(row == kth) > SEL_GATHER_CAP, t
 
 
+# More than four rows per CU with rows longer than 10240 keys: one selection
+# launch per length class, rows above 16384 keys in the chunked 512-thread
+# selection (a sample read of the row bounds a bracket, one sweep gathers it,
+# the search runs on the gathered keys, or on the whole row when the bracket
+# misses or overflows).  Lengths from 600 to 60000 keys.
+CLASS_REQ = ((120, 60000), (120, 40000), (120, 24000), (120, 17000), (120, 12000), (60, 9000),
+             (40, 3000), (20, 600))
+
+
+def best_by_score(sc, n, k):
+    """Ascending indices of the best min(k, n) of sc[:n] by (value desc, index asc)."""
+    order = np.lexsort((np.arange(n), -sc[:n].astype(np.float64)))
+    return np.sort(order[: min(k, n)])
+
+
+@pytest.mark.parametrize("patterns", [0, 3, 200])
+def test_length_class_selection(patterns):
+    """Every token's positions and candidate blocks equal the exact best ones
+    by the GPU's own scores (the order the selection must reproduce, at any
+    size), and the scores equal the oracle's at sampled positions of sampled
+    tokens.  patterns = 3 and 200: K rows from that many patterns with one
+    scale (runs of thousands, or hundreds, of equal scores around the k-th
+    rank, so the chunked bracket overflows its gather or holds the boundary
+    inside a run of ties)."""
+    import oracle
+    pb = small_problem(380 + patterns, ratio=1, N=32, mode=2, topk=1500, cb=1024, requests=CLASS_REQ)
+    vis = visible(pb)
+    assert 2 * pb.num_tokens > 4 * 256 and vis.max() > 32768
+    if patterns:
+        rng = np.random.default_rng(381 + patterns)
+        pats = rng.integers(-128, 128, size=(patterns, 128), dtype=np.int64).astype(np.int8)
+        P, R, _ = pb.k_pages.shape
+        pb.k_pages = pats[rng.integers(0, patterns, size=P * R)].reshape(P, R, 128).copy()
+        pb.s_pages = np.full((P, R), 0x3C00, dtype=np.uint16)
+    say(f"length classes {pb.name} patterns={patterns}: T={pb.num_tokens} L={pb.max_k_len}")
+    gpu = run_gpu(pb, debug=True)
+    check_invariants(pb, gpu)
+    sc = gpu["scores"]
+    for t in range(pb.num_tokens):
+        V = int(vis[t])
+        assert not np.any(np.isnan(sc[t, :V])), t
+        want = best_by_score(sc[t], V, pb.topk)
+        got = gpu["topk"][t]
+        assert np.array_equal(got[: len(want)], want) and np.all(got[len(want):] == -1), t
+        nb = -(-V // 8)
+        bm = np.full(nb * 8, -np.inf)
+        bm[:V] = sc[t, :V]
+        bm = bm.reshape(nb, 8).max(axis=1)
+        if nb <= pb.cand_blocks:
+            cw = np.arange(nb)
+        else:
+            cw = np.sort(np.append(best_by_score(bm, nb - 1, pb.cand_blocks - 1), nb - 1))
+        gc = gpu["cand"][t]
+        assert np.array_equal(gc[: len(cw)], cw) and np.all(gc[len(cw):] == -1), t
+        if patterns == 3 and V > 16384:  # the chunked bracket cannot gather the k-th value's run
+            kth = np.sort(sc[t, :V])[::-1][pb.topk - 1]
+            assert np.count_nonzero(sc[t, :V] == kth) > 2048, t
+    o = oracle.OracleProblem(pb)
+    rng = np.random.default_rng(382)
+    for t in sample_tokens(pb, 4, seed=383):
+        V = int(vis[t])
+        for j in np.concatenate([rng.integers(0, V, 40), [0, V - 1]]):
+            assert sc[t, j] == o.terms(int(t), int(j))["score"], (t, j)
+
+
 @pytest.mark.parametrize("ratio,N,mode", [(2, 64, 2), (1, 32, 1), (2, 32, 3)])
 def test_head_multiplier_ranges(ratio, N, mode):
     """Head multipliers m = fp16(w * q_scale) across the ranges the score
