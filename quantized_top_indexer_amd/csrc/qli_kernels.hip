@@ -1625,7 +1625,11 @@ __device__ __forceinline__ void half_addr(const KArgs& a, const HalfCursor& x, i
   const int idx = ad.pos0 >> a.rlog;
   ad.idx_ok = idx < a.bt_stride;
   ad.want = x.cu.valid && ad.pos0 < g.nlast;
-  ad.raw = a.bt[static_cast<int64_t>(g.b) * a.bt_stride + min(idx, a.bt_stride - 1)];
+  // one entry per wave: a scalar load (the block table is not written during
+  // the call), whose wait (lgkmcnt) does not hold the wave until the K rows
+  // already in flight have landed, as a vector load's would
+  const auto* bt = (const __attribute__((address_space(4))) int32_t*)(a.bt);
+  ad.raw = bt[static_cast<int64_t>(g.b) * a.bt_stride + min(idx, a.bt_stride - 1)];
 }
 
 // page * page_rows + row of the wave's first row, or -1 (no K rows: the
@@ -1665,9 +1669,9 @@ __device__ __forceinline__ void half_stage(const KArgs& a, int v, int wave, int 
 }
 
 template <int NH, int MODE, bool DBG>
-__device__ void run_multi_half(const KArgs& a, const ListView& L, Cursor cur0, int hi,
-                               int8_t (*tile)[kHalf * 128], uint16_t (*ksc)[kHalf], int wave, int lane,
-                               const i32x16& seed, bool& bad) {
+__device__ void run_multi_half(const KArgs& a, const ListView& L, Cursor cur0, int hi, int8_t* tile0,
+                               int8_t* tile1, uint16_t (*ksc)[kHalf], int wave, int lane, const i32x16& seed,
+                               bool& bad) {
   constexpr int P = NH / 32;  // passes per sub-tile
   HalfCursor cur{cur0, 0};
   HalfCursor n1 = next_half(L, cur, hi);
@@ -1684,27 +1688,31 @@ __device__ void run_multi_half(const KArgs& a, const ListView& L, Cursor cur0, i
   // prologue: half 0 into buffer 0
   half_addr(a, cur, wave, ad);
   int v = half_resolve(a, cur, ad, bad);
-  half_stage(a, v, wave, lane, tile[0], sc);
+  half_stage(a, v, wave, lane, tile0, sc);
   half_addr(a, n1, wave, ad);  // lookup of half 1
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   store_scales(0, v, wave, cur);
   __syncthreads();
   QState<NH, true> qs;
   qs.tok = -1;
-  int buf = 0;
   const float one = a.one;
-  while (cur.cu.valid) {
+  // One half: the next one's rows go to the other buffer while this one is
+  // scored.  The two buffers are distinct LDS arrays and each call below
+  // names them as constants, so the compiler can tell that the K rows in
+  // flight (loaded straight into LDS) land in the buffer not being read and
+  // does not hold the LDS reads until they arrive.
+  auto step = [&](const int8_t* tl, int8_t* tn, int buf) {
     const HalfCursor n2 = next_half(L, n1, hi);
-    // half n1 into the other buffer (its lookup completed at the last wait)
-    const int v1 = half_resolve(a, n1, ad, bad);
-    if (n1.cu.valid) half_stage(a, v1, wave, lane, tile[buf ^ 1], sc);
-    half_addr(a, n2, wave, ad);  // lookup of the half after next
     const Group& gr = cur.cu.grp;
     const int t = gr.t0 + wave;
-    const int n_i = visible(a, static_cast<int64_t>(gr.p0) + wave, gr.L);
+    // the queries before the K rows: waiting for them waits for nothing issued later
     if (t != qs.tok) load_q<NH, true>(a, t, lane, qs);
+    // half n1 into the other buffer (its lookup completed at the last wait)
+    const int v1 = half_resolve(a, n1, ad, bad);
+    if (n1.cu.valid) half_stage(a, v1, wave, lane, tn, sc);
+    half_addr(a, n2, wave, ad);  // lookup of the half after next
+    const int n_i = visible(a, static_cast<int64_t>(gr.p0) + wave, gr.L);
     const QRegs<NH, true> q{qs};
-    const int8_t* tl = tile[buf];
     const int s0h = cur.cu.c * kChunk + cur.h * kHalf;  // first slot of the half
     uint32_t* kp = a.keys + static_cast<int64_t>(t) * a.ncap + s0h;
     uint32_t* bp = MODE == QLI_MODE_SOURCE ? a.bkeys + static_cast<int64_t>(t) * a.nbcap + s0h / 8 : nullptr;
@@ -1732,7 +1740,11 @@ __device__ void run_multi_half(const KArgs& a, const ListView& L, Cursor cur0, i
     __syncthreads();
     cur = n1;
     n1 = n2;
-    buf ^= 1;
+  };
+  while (cur.cu.valid) {
+    step(tile0, tile1, 0);
+    if (!cur.cu.valid) break;
+    step(tile1, tile0, 1);
   }
 }
 
@@ -1743,7 +1755,8 @@ __host__ __device__ constexpr int multi_wgs_per_cu(int nh) { return nh == 32 ? 4
 
 template <int NH, int MODE, bool DBG>
 __global__ __launch_bounds__(kScoreThreads, multi_wgs_per_cu(NH)) void score_multi_kernel(KArgs a) {
-  __shared__ __attribute__((aligned(16))) int8_t tile[2][kHalf * 128];
+  __shared__ __attribute__((aligned(16))) int8_t tile0[kHalf * 128];
+  __shared__ __attribute__((aligned(16))) int8_t tile1[kHalf * 128];
   __shared__ __attribute__((aligned(16))) uint16_t ksc[2][kHalf];
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
@@ -1760,7 +1773,7 @@ __global__ __launch_bounds__(kScoreThreads, multi_wgs_per_cu(NH)) void score_mul
 #pragma unroll
   for (int i = 0; i < 16; ++i) seed[i] = kSeedBits;
   bool bad = false;
-  run_multi_half<NH, MODE, DBG>(a, L, cu, st.hi, tile, ksc, wave, lane, seed, bad);
+  run_multi_half<NH, MODE, DBG>(a, L, cu, st.hi, tile0, tile1, ksc, wave, lane, seed, bad);
   if (bad) raise_flag(a, QLI_DEV_BAD_PAGE);
 }
 
