@@ -1889,13 +1889,18 @@ __device__ void run_single(const KArgs& a, const ListView& L, Cursor cu, int hi,
       stage_load<STREAM>(a, vA, lane, krA, scA);
       __builtin_amdgcn_wave_barrier();
       score_item(t, c, n);
-      if (c + 1 >= c_end) break;
+      // the second half of the step runs even past the segment's last item
+      // (its rows are then placeholders and nothing is scored): every path
+      // back to the loop head leaves the same loads in flight, so the
+      // compiler's waits before the next staging keep the other item's rows
+      // in flight (with an exit here the merged paths made that wait drain
+      // every load)
       stage_store<true>(ktile, ksc0, krB, scB, vB, wave, lane);
       vB = resolve<CONSUMER>(a, ad, bad);
       stage_addr<CONSUMER, true>(a, gr, c + 4, c + 4 < c_end, wave, lane, ad);
       stage_load<STREAM>(a, vB, lane, krB, scB);
       __builtin_amdgcn_wave_barrier();
-      score_item(t, c + 1, n);
+      if (c + 1 < c_end) score_item(t, c + 1, n);
     }
     // next token segment
     cu.c = c_end - 1;
