@@ -1771,7 +1771,13 @@ __global__ __launch_bounds__(kScoreThreads, multi_wgs_per_cu(NH)) void score_mul
   cu.valid = true;
   i32x16 seed;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) seed[i] = kSeedBits;
+  for (int i = 0; i < 16; ++i) {
+    // in vector registers for the whole kernel: the MFMAs start each
+    // accumulator chain from them instead of from copies of a scalar splat
+    int x;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(x) : "i"(kSeedBits));
+    seed[i] = x;
+  }
   bool bad = false;
   run_multi_half<NH, MODE, DBG>(a, L, cu, st.hi, tile0, tile1, ksc, wave, lane, seed, bad);
   if (bad) raise_flag(a, QLI_DEV_BAD_PAGE);
@@ -1986,7 +1992,15 @@ __global__ __launch_bounds__(kScoreThreads, score_wgs_per_cu(MODE, NH)) void sco
 
   i32x16 seed;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) seed[i] = kSeedBits;
+  for (int i = 0; i < 16; ++i) {
+    // in vector registers for the whole kernel (the MFMAs start each
+    // accumulator chain from them instead of copies of a scalar splat),
+    // where the register budget of two workgroups per CU leaves room
+    int x = kSeedBits;
+    if constexpr (score_wgs_per_cu(MODE, NH) <= 2)
+      asm volatile("v_mov_b32 %0, %1" : "=v"(x) : "i"(kSeedBits));
+    seed[i] = x;
+  }
   bool bad = false;
   if constexpr (SINGLE_ONLY) {
     run_single<NH, MODE, DBG, STREAM, STAGE, !STREAM>(a, L, cu, st.hi, tile[0], ksc[0], kstage, qfr, qml,
