@@ -357,9 +357,16 @@ constexpr int kPrepLeanMinTokens = 1024;  // consumer batches this large plan in
 // round of loads instead of a dependent binary search); every thread gets it.
 template <int PT>
 __device__ __forceinline__ int prep_request(const KArgs& a, int tg, int* s_req) {
+  const int i0 = threadIdx.x;  // the first round's loads go out before the barrier
+  int q0 = 0, q1 = 0;
+  if (i0 < a.B) {
+    q0 = a.qsl[i0];
+    q1 = a.qsl[i0 + 1];
+  }
   if (threadIdx.x == 0) *s_req = 0;
   __syncthreads();
-  for (int i = threadIdx.x; i < a.B; i += PT)
+  if (i0 < a.B && q0 <= tg && tg < q1) *s_req = i0;
+  for (int i = i0 + PT; i < a.B; i += PT)
     if (a.qsl[i] <= tg && tg < a.qsl[i + 1]) *s_req = i;
   __syncthreads();
   return *s_req;
@@ -414,6 +421,12 @@ __device__ __forceinline__ void prep_bitmap_token(const KArgs& a, int t, uint32_
                                                   uint32_t* sh, int* s_req) {
   const int tid = threadIdx.x;
   const int tg = t + a.t_base;
+  // the incoming ids are loaded first, in flight with the request lookup
+  constexpr int CPT = QLI_MAX_CAND_BLOCKS / PT;
+  const int32_t* cin = a.cand_in + static_cast<int64_t>(t) * a.cb_in;
+  int cv[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) cv[j] = tid + j * PT < a.cb_in ? cin[tid + j * PT] : -1;
   const int b = prep_request<PT>(a, tg, s_req);
   const ReqView r = request_view(a, global_meta(a), b, tid == 0);
   const int V = (tg >= r.q0 && tg < r.q1)
@@ -422,9 +435,9 @@ __device__ __forceinline__ void prep_bitmap_token(const KArgs& a, int t, uint32_
   const int nwords = (nblocks + 31) / 32;  // within the bitmap: V <= max_k_len (checked at launch)
   for (int i = tid; i < nwords; i += PT) bm[i] = 0;
   __syncthreads();
-  const int32_t* cin = a.cand_in + static_cast<int64_t>(t) * a.cb_in;
-  for (int i = tid; i < a.cb_in; i += PT) {
-    const int c = cin[i];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int c = cv[j];
     if (c >= 0 && c < nblocks) atomicOr(&bm[c >> 5], 1u << (c & 31));
   }
   __syncthreads();
@@ -903,52 +916,100 @@ __device__ __forceinline__ bool plan_one_token_per_request(const KArgs& a, const
   return __ballot(ok) == ~0ull && a.t_base + a.T <= a.B;
 }
 
-// The plan of a batch whose requests hold one token each, for the one
-// workgroup plan_wg (the same lists and start entry as plan_body): token t
-// (lane t of wave 0) is request t_base + t, a single group of ceil(V/256)
-// units; the unit prefix is one wave scan, and the group holding unit
+// The lists of a batch whose requests hold one token each (the same lists
+// as plan_body), by wave 0: token t (lane t) is request t_base + t, a single
+// group of ceil(V/256) units; the unit prefix is one wave scan.  Returns
+// the lane's group, its first unit and unit count, and the total.
+struct SingleLane {
+  Group g;
+  uint32_t excl, units, U;
+};
+__device__ __forceinline__ SingleLane single_token_lists(const KArgs& a, const Meta& m) {
+  const int t = threadIdx.x;
+  const int T = a.T;
+  const bool in = t < T;
+  SingleLane s{};
+  if (in) {
+    const int b = t + a.t_base;
+    const ReqView r = request_view(a, m, b, true);
+    s.g = make_group(a, b, r, t, b, 1);
+    s.units = static_cast<uint32_t>(s.g.nch);
+    a.tokv[2 * t] = s.g.n0;
+  }
+  const uint32_t incl = wave_inclusive_scan(s.units);
+  s.excl = incl - s.units;
+  s.U = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
+  if (in) {
+    a.groups[T + t] = s.g;                      // list 1 (single groups)
+    a.ustart[(T + 1) + t] = static_cast<int32_t>(s.excl);
+  }
+  if (t == 0) {
+    a.ustart[0] = 0;                            // list 0 is empty
+    a.ustart[(T + 1) + T] = static_cast<int32_t>(s.U);
+  }
+  return s;
+}
+
+// Start entry of workgroup w of W over the single list (U units), whose
+// range starts at unit lo inside group gi (first unit excl).
+__device__ __forceinline__ WgStart single_start(const Group& g, int gi, int ng, uint32_t excl, int64_t lo,
+                                                int w, int W, uint32_t U) {
+  WgStart st;
+  st.grp = g;
+  st.list = 1;
+  st.ng = ng;
+  st.g = gi;
+  st.c = static_cast<int>(lo - excl);
+  st.unit = static_cast<int>(lo);
+  st.hi = static_cast<int>(floor_div(static_cast<int64_t>(w + 1) * U, W));
+  st.pad[0] = st.pad[1] = 0;
+  return st;
+}
+
+// That plan for the one workgroup plan_wg: the group holding unit
 // floor(w U / W) is found with one ballot.
 __device__ void plan_single_tokens(const KArgs& a, const Meta& m) {
   if (threadIdx.x >= 64) return;
   const int t = threadIdx.x;
-  const int T = a.T;
-  const bool in = t < T;
-  Group g{};
-  uint32_t units = 0;
-  if (in) {
-    const int b = t + a.t_base;
-    const ReqView r = request_view(a, m, b, true);
-    g = make_group(a, b, r, t, b, 1);
-    units = static_cast<uint32_t>(g.nch);
-    a.tokv[2 * t] = g.n0;
-  }
-  const uint32_t incl = wave_inclusive_scan(units);
-  const uint32_t excl = incl - units;
-  const uint32_t U = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
-  if (in) {
-    a.groups[T + t] = g;                        // list 1 (single groups)
-    a.ustart[(T + 1) + t] = static_cast<int32_t>(excl);
-  }
-  if (t == 0) {
-    a.ustart[0] = 0;                            // list 0 is empty
-    a.ustart[(T + 1) + T] = static_cast<int32_t>(U);
-  }
+  const SingleLane s = single_token_lists(a, m);
   const int W = a.score_grid;
   const int w = a.plan_wg;
-  const int64_t lo = floor_div(static_cast<int64_t>(w) * U, W);
-  const bool holds = in && units > 0 && excl <= lo && lo < excl + units;
+  const int64_t lo = floor_div(static_cast<int64_t>(w) * s.U, W);
+  const bool holds = t < a.T && s.units > 0 && s.excl <= lo && lo < s.excl + s.units;
   const uint64_t mask = __ballot(holds);
-  if (mask != 0 && t == __builtin_ctzll(mask)) {
-    WgStart st;
-    st.grp = g;
-    st.list = 1;
-    st.ng = T;
-    st.g = t;
-    st.c = static_cast<int>(lo - excl);
-    st.unit = static_cast<int>(lo);
-    st.hi = static_cast<int>(floor_div(static_cast<int64_t>(w + 1) * U, W));
-    st.pad[0] = st.pad[1] = 0;
-    a.wgs[0] = st;
+  if (mask != 0 && t == __builtin_ctzll(mask)) a.wgs[0] = single_start(s.g, t, a.T, s.excl, lo, w, W, s.U);
+}
+
+// That plan for the whole grid, by PT threads: after the lists, every
+// thread takes workgroups w, w + PT, ...: the group holding unit
+// floor(w U / W) is the last token whose first unit is at most that (a
+// binary search over the 64 prefixes in LDS; tokens without units share
+// their successor's prefix and are never the last such).  A workgroup whose
+// range starts at U or beyond has no work.
+template <int PT>
+__device__ void plan_single_tokens_grid(const KArgs& a, const Meta& m, uint32_t* sh) {
+  const int tid = threadIdx.x;
+  const int T = a.T;
+  if (tid < 64) {
+    const SingleLane s = single_token_lists(a, m);
+    sh[tid] = s.excl;
+    if (tid == 0) sh[64] = s.U;  // the first word past the scan scratch (marks are unused here)
+  }
+  __syncthreads();  // the prefixes in LDS, the groups in memory
+  const uint32_t U = sh[64];
+  const int W = a.score_grid;
+  for (int w = tid; w < W; w += PT) {
+    const int64_t lo = floor_div(static_cast<int64_t>(w) * U, W);
+    WgStart st = {};
+    st.g = -1;
+    if (lo < static_cast<int64_t>(U)) {
+      int t = 0;  // sh[0] = 0 <= lo
+#pragma unroll
+      for (int step = 32; step > 0; step >>= 1)
+        if (t + step < T && sh[t + step] <= lo) t += step;
+      st = single_start(a.groups[T + t], t, T, sh[t], lo, w, W, U);
+    }
+    a.wgs[w] = st;
   }
 }
 
@@ -987,9 +1048,15 @@ __device__ void plan_role(const KArgs& a, uint32_t* lds) {
     }
     __syncthreads();
     const Meta m{s_qsl, s_klen, a.smod ? s_smod : nullptr};
-    if (a.plan_wg >= 0 && a.multi_grid == 0 && a.B <= 64 && plan_one_token_per_request(a, m)) {
-      plan_single_tokens(a, m);  // wave 0; the caller's barrier publishes the lists
-      return;
+    if (a.multi_grid == 0 && a.B <= 64 && plan_one_token_per_request(a, m)) {
+      if (a.plan_wg >= 0) {
+        plan_single_tokens(a, m);  // wave 0; the caller's barrier publishes the lists
+        return;
+      }
+      if (kGrid) {
+        plan_single_tokens_grid<PT>(a, m, sh);
+        return;
+      }
     }
     plan_body<PT, kGrid>(a, m, sh, own);
   } else {
