@@ -14,6 +14,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qli_oracle.c")
 _SRC_QUANT = os.path.join(_HERE, "qli_quant_oracle.c")
+_SRC_ATTN = os.path.join(_HERE, "qli_attn_oracle.c")
 _LIB = os.path.join(_HERE, "libqli_oracle.so")
 # an alternative build (used by the tests that plant mistakes in a copy)
 _LOAD = os.environ.get("QLI_ORACLE_LIB", _LIB)
@@ -25,7 +26,7 @@ def build(force: bool = True) -> str:
     """Compile the oracle with gcc (no GPU toolchain involved)."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
-        subprocess.run(["gcc", *CFLAGS, _SRC, _SRC_QUANT, "-o", tmp, "-lm"], check=True)
+        subprocess.run(["gcc", *CFLAGS, _SRC, _SRC_QUANT, _SRC_ATTN, "-o", tmp, "-lm"], check=True)
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -228,3 +229,64 @@ def write_k(x, slot, kpages, spages):
     L.oracle_write_k(_ptr(x), C.c_int(_dtype_code(x)), _ptr(slot), C.c_int64(slot.size),
                      C.c_int(R), C.c_int64(P), _ptr(kp), _ptr(sp))
     return kp, sp
+
+
+# ---------------------------------------------------------------------------
+# sparse attention over the indexer's positions (qli_attn_oracle.c)
+# ---------------------------------------------------------------------------
+
+class _AttnProblem(C.Structure):
+    _fields_ = [
+        ("num_heads", C.c_int32), ("head_dim", C.c_int32), ("batch", C.c_int32),
+        ("num_tokens", C.c_int32), ("topk", C.c_int32), ("window", C.c_int32),
+        ("c_page_rows", C.c_int32), ("c_bt_stride", C.c_int32),
+        ("r_page_rows", C.c_int32), ("r_bt_stride", C.c_int32),
+        ("c_page_stride", C.c_int64), ("r_page_stride", C.c_int64),
+        ("scale", C.c_double),
+        ("q", C.c_void_p), ("c_kv", C.c_void_p), ("c_bt", C.c_void_p), ("c_lens", C.c_void_p),
+        ("r_kv", C.c_void_p), ("r_bt", C.c_void_p), ("r_lens", C.c_void_p),
+        ("query_start_loc", C.c_void_p), ("indices", C.c_void_p), ("sinks", C.c_void_p),
+    ]
+
+
+def sparse_attn(ap, tokens=None, indices=None):
+    """(out float64 [n, H, D], lse float64 [n, H]) of the attention call
+    ``ap`` (a qli_workloads.attn.AttnProblem) for ``tokens`` (default: all);
+    ``indices`` overrides ap.indices."""
+    keep = []
+
+    def arr(a, dt):
+        a = np.ascontiguousarray(a, dtype=dt)
+        keep.append(a)
+        return a.ctypes.data
+
+    idx = ap.indices if indices is None else indices
+    s = _AttnProblem()
+    s.num_heads, s.head_dim, s.batch = ap.num_heads, ap.head_dim, ap.batch
+    s.num_tokens, s.topk, s.window = ap.num_tokens, int(idx.shape[1]), ap.window
+    s.c_page_rows, s.c_bt_stride = ap.c_page_rows, int(ap.c_bt.shape[1])
+    s.r_page_rows, s.r_bt_stride = ap.r_page_rows, int(ap.r_bt.shape[1])
+    s.c_page_stride, s.r_page_stride = ap.c_page_stride, ap.r_page_stride
+    s.scale = float(ap.scale)
+    s.q = arr(ap.q, np.uint16)
+    s.c_kv = ap.c_pages.ctypes.data
+    s.c_bt = arr(ap.c_bt, np.int32)
+    s.c_lens = arr(ap.c_lens, np.int32)
+    s.r_kv = ap.r_pages.ctypes.data
+    s.r_bt = arr(ap.r_bt, np.int32)
+    s.r_lens = arr(ap.r_lens, np.int32)
+    s.query_start_loc = arr(ap.query_start_loc, np.int32)
+    s.indices = arr(idx, np.int32)
+    s.sinks = None if ap.sinks is None else arr(ap.sinks, np.float32)
+    tok = np.arange(ap.num_tokens, dtype=np.int32) if tokens is None else \
+        np.ascontiguousarray(tokens, dtype=np.int32)
+    n = int(tok.size)
+    out = np.zeros((n, ap.num_heads, ap.head_dim), dtype=np.float64)
+    lse = np.zeros((n, ap.num_heads), dtype=np.float64)
+    L = lib()
+    L.oracle_sparse_attn.restype = C.c_int
+    L.oracle_sparse_attn.argtypes = [C.POINTER(_AttnProblem), C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]
+    rc = L.oracle_sparse_attn(C.byref(s), tok.ctypes.data, n, out.ctypes.data, lse.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"oracle_sparse_attn failed with {rc}")
+    return out, lse
