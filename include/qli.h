@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define QLI_ABI_VERSION 4
+#define QLI_ABI_VERSION 5
 
 /* Status codes returned by the host entry points. */
 enum qli_status {
@@ -92,10 +92,14 @@ enum qli_mode { QLI_MODE_PLAIN = 1, QLI_MODE_SOURCE = 2, QLI_MODE_CONSUMER = 3 }
 #define QLI_DEV_BAD_LENGTH 2u   /* k_lens[b] < 0 or > max_k_len */
 #define QLI_DEV_BAD_METADATA 4u /* seq_mod outside [0, ratio), or a request
                                    with more queries than raw tokens */
+#define QLI_DEV_BAD_INDEX 8u    /* qli_sparse_attention: an index at or beyond the request's
+                                   compressed length (the entry is skipped) */
 
 /* Documented caps (QLI_ERR_UNSUPPORTED beyond them). */
 #define QLI_MAX_TOPK 2048
 #define QLI_MAX_CAND_BLOCKS 2048
+#define QLI_ATTN_MAX_TOPK 2048   /* qli_sparse_attention: widest index row */
+#define QLI_ATTN_MAX_WINDOW 512  /* qli_sparse_attention: longest window */
 #define QLI_MAX_K_LEN (1 << 24)
 
 typedef struct qli_params {
@@ -286,10 +290,86 @@ typedef struct qli_kwrite_params {
  * Returns a qli_status. */
 int qli_write_index_k(const qli_kwrite_params* p, void* stream);
 
+/* ---- Consumer of the indices: sparse attention ------------------------
+ *
+ * The step after the indexer ("DeepSeek V4.1-Flash 登陆昇腾 · 需求故事（PR
+ * 16925）", section 4: the compressed positions feed the two-stage sparse
+ * attention; "DeepSeek V4.1-Flash CED·CSA2 架构拆解 × vllm-ascend 性能协助点",
+ * operator table: a sliding window over recent tokens (SWA) and the
+ * compressed global stage over the selected positions (CSA), with sinks;
+ * BF16 TND queries and PA_BBND paged caches, the only layouts the developer
+ * guide's "编译范围" builds).  The pages give no formula; this library
+ * computes, for query token t of request b and head h:
+ *   entries  E = { compressed rows indices[t][i] : 0 <= indices[t][i] < c_lens[b] }
+ *              + { raw rows s : max(0, p - window + 1) <= s <= p },
+ *              p = r_lens[b] - (q1 - q0) + (t - q0) the token's raw position
+ *              (tokens q0..q1-1 of the request);
+ *   z_j = scale * sum_d q[t][h][d] * kv_j[d]  (one latent KV head shared by
+ *         all query heads; an entry's D values are its key and its value);
+ *   out[t][h] = sum_j e^(z_j - m) kv_j / (sum_j e^(z_j - m) + e^(sink_h - m)),
+ *         m the largest logit including the sink (no sink term when sinks is
+ *         NULL); lse[t][h] = m + ln(denominator);
+ *   no entry and no sink: out = 0, lse = -inf.
+ * Products are exact, sums FP32, the softmax in base 2 on FP32 values; the
+ * weights of the value sum are rounded to BF16 (the normalizer adds the same
+ * rounded weights), and out is rounded to BF16 (RNE).  Tokens outside every
+ * request get out = 0 and lse = -inf. */
+typedef struct qli_attn_params {
+  int32_t struct_size;      /* sizeof(qli_attn_params) */
+  int32_t num_heads;        /* H: a multiple of 16, at most 128 */
+  int32_t head_dim;         /* D: must be 512 */
+  int32_t batch;            /* B >= 1 requests */
+  int32_t num_tokens;       /* T >= 0 query tokens (T == 0: no-op) */
+  int32_t topk;             /* width of an index row, 0 .. QLI_ATTN_MAX_TOPK */
+  int32_t window;           /* raw positions of the window stage, 0 .. QLI_ATTN_MAX_WINDOW */
+  int32_t c_page_rows;      /* rows per page of the compressed cache, 1 .. 256 */
+  int32_t c_bt_stride;      /* entries per request row of c_block_table, >= 1 */
+  int32_t r_page_rows;      /* rows per page of the raw cache, 1 .. 256 (window > 0) */
+  int32_t r_bt_stride;      /* entries per request row of r_block_table (window > 0) */
+  int32_t reserved0;        /* must be 0 */
+  int64_t c_num_pages;      /* pages of the compressed pool, 1 .. 2^23 - 1 */
+  int64_t r_num_pages;      /* pages of the raw pool, 1 .. 2^23 - 1 when window > 0 */
+  int64_t c_page_stride;    /* bytes between compressed pages: a multiple of 16,
+                               >= c_page_rows * D * 2; row r of page g starts at
+                               g * c_page_stride + r * D * 2 */
+  int64_t r_page_stride;    /* the same for the raw pool (window > 0) */
+  float scale;              /* softmax scale, finite */
+  int32_t reserved1;        /* must be 0 */
+  const void* q;            /* BF16 [T][H][D] (16-B aligned) */
+  const void* c_cache;      /* BF16 compressed pool, page 0 row 0 (16-B aligned) */
+  const int32_t* c_block_table; /* [B][c_bt_stride] page ids; an id outside
+                               [0, c_num_pages) drops the entry and raises
+                               QLI_DEV_BAD_PAGE */
+  const int32_t* c_lens;    /* [B] compressed lengths (>= 0) */
+  const void* r_cache;      /* BF16 raw pool (16-B aligned; NULL when window == 0) */
+  const int32_t* r_block_table; /* [B][r_bt_stride] (NULL when window == 0) */
+  const int32_t* r_lens;    /* [B] raw lengths; r_lens[b] >= q1 - q0 (else the
+                               request's tokens see no window entry and
+                               QLI_DEV_BAD_METADATA is raised) */
+  const int32_t* query_start_loc; /* [B + 1] non-decreasing, query_start_loc[0] == 0,
+                               query_start_loc[B] == T */
+  const int32_t* indices;   /* [T][topk] request-local compressed positions; < 0:
+                               padding (skipped); >= c_lens[b]: skipped and
+                               QLI_DEV_BAD_INDEX raised (NULL when topk == 0) */
+  const float* sinks;       /* [H] one logit per head, or NULL */
+  void* out;                /* BF16 [T][H][D] written (16-B aligned) */
+  float* lse;               /* [T][H] written, or NULL */
+  uint32_t* status_out;     /* optional device word receiving QLI_DEV_* bits (ORed) */
+} qli_attn_params;
+
+/* Enqueue the attention of num_tokens query tokens on `stream`: one launch,
+ * no allocation, no synchronisation.  The host checks the parameters first
+ * (QLI_ERR_INVALID_ARG / QLI_ERR_UNSUPPORTED, nothing launched); pointers
+ * must be device memory, and every integer pointer 4-byte aligned.  Device
+ * data outside the contract above is never read beyond the pools, tables
+ * and arrays described; it is reported through status_out.
+ * Returns a qli_status. */
+int qli_sparse_attention(const qli_attn_params* p, void* stream);
+
 /* Kernels, in launch order within a call (for the timing facility below). */
 enum qli_kernel { QLI_KERNEL_CONSUMER_PREP = 0, QLI_KERNEL_PLAN = 1, QLI_KERNEL_SCORE = 2,
                   QLI_KERNEL_SELECT = 3, QLI_KERNEL_QUANTIZE = 4, QLI_KERNEL_WRITE_K = 5,
-                  QLI_NUM_KERNELS = 6 };
+                  QLI_KERNEL_ATTN = 6, QLI_NUM_KERNELS = 7 };
 
 /* Optional per-kernel timing (off by default; process-wide, not thread
  * safe).  While enabled, every call of this library records a HIP event

@@ -16,6 +16,7 @@ outputs).
 from __future__ import annotations
 
 import ctypes as C
+import math
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -73,17 +74,36 @@ class qli_kwrite_params(C.Structure):
     ]
 
 
+class qli_attn_params(C.Structure):
+    """Mirror of ``struct qli_attn_params`` in include/qli.h."""
+    _fields_ = [
+        ("struct_size", C.c_int32), ("num_heads", C.c_int32), ("head_dim", C.c_int32),
+        ("batch", C.c_int32), ("num_tokens", C.c_int32), ("topk", C.c_int32),
+        ("window", C.c_int32), ("c_page_rows", C.c_int32), ("c_bt_stride", C.c_int32),
+        ("r_page_rows", C.c_int32), ("r_bt_stride", C.c_int32), ("reserved0", C.c_int32),
+        ("c_num_pages", C.c_int64), ("r_num_pages", C.c_int64),
+        ("c_page_stride", C.c_int64), ("r_page_stride", C.c_int64),
+        ("scale", C.c_float), ("reserved1", C.c_int32),
+        ("q", C.c_void_p), ("c_cache", C.c_void_p), ("c_block_table", C.c_void_p),
+        ("c_lens", C.c_void_p), ("r_cache", C.c_void_p), ("r_block_table", C.c_void_p),
+        ("r_lens", C.c_void_p), ("query_start_loc", C.c_void_p), ("indices", C.c_void_p),
+        ("sinks", C.c_void_p), ("out", C.c_void_p), ("lse", C.c_void_p),
+        ("status_out", C.c_void_p),
+    ]
+
+
 EXPORTS = ("qli_abi_version", "qli_validate", "qli_workspace_bytes", "qli_score_topk",
            "qli_score_topk_noalloc", "qli_status_string", "qli_timing_enable", "qli_timing_read",
-           "qli_quantize_query", "qli_write_index_k")
+           "qli_quantize_query", "qli_write_index_k", "qli_sparse_attention")
 # the ceiling probes (include/qli_probe.h): a library of their own, for
 # measurement only
 PROBE_LIB_PATH = os.path.join(_HERE, "libqli_probe.so")
 PROBE_EXPORTS = ("qli_probe_hbm_read", "qli_probe_int8_mfma", "qli_probe_int8_mfma_ops")
 QLI_KERNEL_CONSUMER_PREP, QLI_KERNEL_PLAN, QLI_KERNEL_SCORE, QLI_KERNEL_SELECT, \
-    QLI_KERNEL_QUANTIZE, QLI_KERNEL_WRITE_K, QLI_NUM_KERNELS = range(7)
+    QLI_KERNEL_QUANTIZE, QLI_KERNEL_WRITE_K, QLI_KERNEL_ATTN, QLI_NUM_KERNELS = range(8)
 KERNEL_NAMES = ("consumer_prep_kernel", "plan_kernel", "score_kernel", "select_kernel",
-                "quantize_kernel", "write_k_kernel")
+                "quantize_kernel", "write_k_kernel", "sparse_attn_kernel")
+QLI_ABI_VERSION = 5
 
 _lib = None
 
@@ -121,6 +141,8 @@ def load_library(path: str = LIB_PATH):
     L.qli_quantize_query.argtypes = [C.POINTER(qli_quant_params), C.c_void_p]
     L.qli_write_index_k.restype = C.c_int
     L.qli_write_index_k.argtypes = [C.POINTER(qli_kwrite_params), C.c_void_p]
+    L.qli_sparse_attention.restype = C.c_int
+    L.qli_sparse_attention.argtypes = [C.POINTER(qli_attn_params), C.c_void_p]
     if path == LIB_PATH:
         _lib = L
     return L
@@ -272,6 +294,48 @@ def write_index_k(x, slot, k_cache, k_scale, *, status_out=None, stream=None):
     rc = qli_write_index_k(p, stream)
     if rc != QLI_OK:
         raise RuntimeError(qli_status_string(rc))
+
+
+def qli_sparse_attention(p: qli_attn_params, stream=None) -> int:
+    """Raw C-ABI call (see include/qli.h)."""
+    return load_library().qli_sparse_attention(C.byref(p), _stream(stream))
+
+
+def sparse_attention(q, c_cache, c_block_table, c_lens, query_start_loc, *, indices=None,
+                     r_cache=None, r_block_table=None, r_lens=None, window=0, sinks=None,
+                     scale=None, c_page_rows, c_page_stride, r_page_rows=0, r_page_stride=0,
+                     c_num_pages, r_num_pages=0, out=None, lse=None, status_out=None, stream=None):
+    """Sparse attention over the indexer's positions (argument marshalling
+    for qli_sparse_attention): q bfloat16 [T, H, 512]; c_cache / r_cache
+    device buffers of BF16 rows paged as described in include/qli.h (any
+    tensor, passed by address with the page geometry given explicitly);
+    block tables int32 [B, stride]; lengths int32 [B]; query_start_loc
+    int32 [B + 1]; indices int32 [T, topk] or None; sinks float32 [H] or
+    None.  Returns (out bfloat16 [T, H, 512], lse float32 [T, H] or None)."""
+    import torch
+    T, H, D = q.shape
+    if out is None:
+        out = torch.empty((T, H, D), dtype=torch.bfloat16, device=q.device)
+    p = qli_attn_params()
+    p.struct_size = C.sizeof(qli_attn_params)
+    p.num_heads, p.head_dim, p.batch, p.num_tokens = H, D, c_lens.shape[0], T
+    p.topk = 0 if indices is None else indices.shape[1]
+    p.window = window
+    p.c_page_rows, p.c_bt_stride = c_page_rows, c_block_table.shape[1]
+    p.c_num_pages, p.c_page_stride = c_num_pages, c_page_stride
+    if window > 0:
+        p.r_page_rows, p.r_bt_stride = r_page_rows, r_block_table.shape[1]
+        p.r_num_pages, p.r_page_stride = r_num_pages, r_page_stride
+    p.scale = float(1.0 / math.sqrt(D) if scale is None else scale)
+    p.q, p.c_cache, p.c_block_table = q.data_ptr(), c_cache.data_ptr(), c_block_table.data_ptr()
+    p.c_lens, p.query_start_loc = c_lens.data_ptr(), query_start_loc.data_ptr()
+    p.r_cache, p.r_block_table, p.r_lens = _ptr(r_cache), _ptr(r_block_table), _ptr(r_lens)
+    p.indices, p.sinks = _ptr(indices), _ptr(sinks)
+    p.out, p.lse, p.status_out = out.data_ptr(), _ptr(lse), _ptr(status_out)
+    rc = qli_sparse_attention(p, stream)
+    if rc != QLI_OK:
+        raise RuntimeError(qli_status_string(rc))
+    return out, lse
 
 
 def qli_status_string(code: int) -> str:

@@ -11,7 +11,7 @@ OUT = os.path.join(HERE, "libqli.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = [os.path.join(CSRC, "qli_api.cpp"), os.path.join(CSRC, "qli_kernels.hip"),
-           os.path.join(CSRC, "qli_quant.hip")]
+           os.path.join(CSRC, "qli_quant.hip"), os.path.join(CSRC, "qli_attn.hip")]
 # the ceiling probes (measurement only) are a library of their own
 PROBE_SOURCES = [os.path.join(CSRC, "qli_probe.hip")]
 PROBE_OUT = os.path.join(HERE, "libqli_probe.so")

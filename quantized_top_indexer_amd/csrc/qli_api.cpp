@@ -5,6 +5,9 @@
 // ratio 1) and the contract limits of its "当前 A3 契约" section.
 #include <stdint.h>
 
+#include <cmath>
+#include <climits>
+
 #include "qli.h"
 #include "qli_internal.h"
 
@@ -110,9 +113,56 @@ int check_kwrite(const qli_kwrite_params* p) {
   return QLI_OK;
 }
 
+int check_attn(const qli_attn_params* p) {
+  if (!p || p->struct_size != sizeof(qli_attn_params)) return QLI_ERR_INVALID_ARG;
+  if (p->head_dim != 512) return QLI_ERR_UNSUPPORTED;
+  if (p->num_heads < 16 || p->num_heads > 128 || p->num_heads % 16) return QLI_ERR_UNSUPPORTED;
+  if (p->reserved0 != 0 || p->reserved1 != 0) return QLI_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->num_tokens < 0) return QLI_ERR_INVALID_ARG;
+  if (p->topk < 0 || p->topk > QLI_ATTN_MAX_TOPK) return QLI_ERR_INVALID_ARG;
+  if (p->window < 0 || p->window > QLI_ATTN_MAX_WINDOW) return QLI_ERR_INVALID_ARG;
+  if (!std::isfinite(p->scale)) return QLI_ERR_INVALID_ARG;
+  const int64_t row_bytes = int64_t(512) * 2;
+  // the kernel packs an entry as page (23 bits) and row (8 bits)
+  if (p->c_page_rows < 1 || p->c_page_rows > 256 || p->c_bt_stride < 1 || p->c_num_pages < 1 ||
+      p->c_num_pages >= (int64_t(1) << 23))
+    return QLI_ERR_INVALID_ARG;
+  if (p->c_page_stride % 16 || p->c_page_stride < p->c_page_rows * row_bytes) return QLI_ERR_INVALID_ARG;
+  // every address the kernel forms stays within 2^62 bytes of the pool base
+  if (p->c_num_pages > (int64_t(1) << 62) / p->c_page_stride) return QLI_ERR_INVALID_ARG;
+  if (int64_t(p->c_bt_stride) * p->c_page_rows > INT32_MAX) return QLI_ERR_INVALID_ARG;
+  if (p->window > 0) {
+    if (p->r_page_rows < 1 || p->r_page_rows > 256 || p->r_bt_stride < 1 || p->r_num_pages < 1 ||
+        p->r_num_pages >= (int64_t(1) << 23))
+      return QLI_ERR_INVALID_ARG;
+    if (p->r_page_stride % 16 || p->r_page_stride < p->r_page_rows * row_bytes) return QLI_ERR_INVALID_ARG;
+    if (p->r_num_pages > (int64_t(1) << 62) / p->r_page_stride) return QLI_ERR_INVALID_ARG;
+    if (int64_t(p->r_bt_stride) * p->r_page_rows > INT32_MAX) return QLI_ERR_INVALID_ARG;
+  }
+  if (p->num_tokens == 0) return QLI_OK;
+  if (!p->q || !p->c_cache || !p->c_block_table || !p->c_lens || !p->query_start_loc || !p->out)
+    return QLI_ERR_INVALID_ARG;
+  if (p->topk > 0 && !p->indices) return QLI_ERR_INVALID_ARG;
+  if (p->window > 0 && (!p->r_cache || !p->r_block_table || !p->r_lens)) return QLI_ERR_INVALID_ARG;
+  if (!aligned(p->q, 16) || !aligned(p->c_cache, 16) || !aligned(p->r_cache, 16) || !aligned(p->out, 16))
+    return QLI_ERR_INVALID_ARG;
+  if (!aligned(p->c_block_table, 4) || !aligned(p->c_lens, 4) || !aligned(p->r_block_table, 4) ||
+      !aligned(p->r_lens, 4) || !aligned(p->query_start_loc, 4) || !aligned(p->indices, 4) ||
+      !aligned(p->sinks, 4) || !aligned(p->lse, 4) || !aligned(p->status_out, 4))
+    return QLI_ERR_INVALID_ARG;
+  return QLI_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int qli_sparse_attention(const qli_attn_params* p, void* stream) {
+  const int rc = check_attn(p);
+  if (rc != QLI_OK) return rc;
+  if (p->num_tokens == 0) return QLI_OK;
+  return qli::launch_attention(p, stream);
+}
 
 int qli_quantize_query(const qli_quant_params* p, void* stream) {
   const int rc = check_quant(p);

@@ -149,5 +149,6 @@ int xcd_count();
 // Enqueue the quantization / K-write kernels (arguments already validated).
 int launch_quantize(const qli_quant_params* p, void* stream);
 int launch_write_k(const qli_kwrite_params* p, void* stream);
+int launch_attention(const qli_attn_params* p, void* stream);
 
 }  // namespace qli

@@ -53,10 +53,10 @@ def test_probes_live_in_their_own_library(lib):
 
 
 def test_abi_version(lib):
-    assert Q.qli_abi_version() == 4
+    assert Q.qli_abi_version() == Q.QLI_ABI_VERSION == 5
 
 
-@pytest.mark.parametrize("struct", ["qli_params", "qli_quant_params", "qli_kwrite_params"])
+@pytest.mark.parametrize("struct", ["qli_params", "qli_quant_params", "qli_kwrite_params", "qli_attn_params"])
 def test_struct_layout_matches_header(tmp_path, struct):
     cls = getattr(Q, struct)
     fields = [f[0] for f in cls._fields_]
@@ -392,3 +392,29 @@ def test_probe_rejections(lib):
     assert Q.qli_probe_int8_mfma(0, 10, fake, 0) == Q.QLI_ERR_INVALID_ARG
     assert Q.qli_probe_int8_mfma(16, 0, fake, 0) == Q.QLI_ERR_INVALID_ARG
     assert Q.qli_probe_int8_mfma_ops(2, 3) == 2 * 4 * 3 * 4 * 32 * 32 * 32 * 2
+
+
+def _attn_params(**kw):
+    p = Q.qli_attn_params()
+    p.struct_size = C.sizeof(Q.qli_attn_params)
+    p.num_heads, p.head_dim, p.batch, p.num_tokens = 64, 512, 1, 0
+    p.topk, p.window = 16, 0
+    p.c_page_rows, p.c_bt_stride, p.c_num_pages, p.c_page_stride = 64, 4, 8, 131072
+    p.scale = 0.04
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, 0),                                           # no tokens: a no-op
+    ({"head_dim": 576}, 2), ({"num_heads": 24}, 2), ({"num_heads": 144}, 2),
+    ({"topk": 2049}, 1), ({"window": 513}, 1), ({"window": -1}, 1), ({"batch": 0}, 1),
+    ({"c_page_stride": 131072 + 8}, 1), ({"c_page_stride": 64 * 1024 - 16}, 1),
+    ({"reserved0": 1}, 1), ({"scale": float("inf")}, 1),
+    ({"window": 8}, 1),                                 # window without raw pool geometry
+    ({"num_tokens": 1}, 1),                             # tokens but no pointers
+    ({"struct_size": 8}, 1), ({"c_page_rows": 257}, 1), ({"c_num_pages": 1 << 23}, 1),
+])
+def test_attention_host_validation(lib, kw, code):
+    assert lib.qli_sparse_attention(C.byref(_attn_params(**kw)), None) == code
