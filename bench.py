@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, published (5.0 POP/s)
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA, published (2.5 PFLOP/s)
 KEY_BYTES = 130                # one 128-byte index-K row + its 2-byte FP16 scale
 # what roofline.achieved divides by (roofline.kernel_ms)
 DURATION_SOURCE = ("duration per call of roofline.kernel (its launches in one call summed), from HIP "
@@ -352,6 +353,83 @@ def measure_producers(steps, warmup, copies=2):
     return out
 
 
+def measure_attention(steps, warmup, index_sets=4, prepared=None):
+    """The sparse-attention consumer of the indices at the decode shape
+    (attn_decode: 64 tokens x 2048 selected positions + a 128-position window,
+    64 heads, D = 512), each launch timed with HIP events on its stream,
+    against HBM.  Algorithmic bytes: every entry's 1024-byte row once per
+    token (the head groups of a token share it through their XCD's L2), the
+    queries and outputs (64 x 1 KB each per token), the index row and the
+    log-sum-exp.  ``index_sets`` rotated index sets (rows drawn for all of
+    them) keep the previous launch's rows out of the last-level cache.  The
+    matrix work (S^T and O^T, 4 * H * D flops per entry) is reported beside
+    it against the dense BF16 peak."""
+    import numpy as np
+    import torch
+
+    import quantized_top_indexer_amd as Q
+    from qli_workloads import attn as A
+    if prepared is None:
+        log("attn_decode: generating")
+        ap, sets = A.attn_decode(index_sets=index_sets)
+    else:
+        ap, sets = prepared
+    dev = lambda a, dt=None: torch.from_numpy(np.ascontiguousarray(a if dt is None else a.astype(dt))).cuda()
+    q = dev(ap.q.view(np.int16)).view(torch.bfloat16)
+    c_cache, r_cache = dev(ap.c_pages), dev(ap.r_pages)
+    c_bt, r_bt = dev(ap.c_bt, np.int32), dev(ap.r_bt, np.int32)
+    c_lens, r_lens = dev(ap.c_lens, np.int32), dev(ap.r_lens, np.int32)
+    qsl, sinks = dev(ap.query_start_loc, np.int32), dev(ap.sinks, np.float32)
+    idx = [dev(x, np.int32) for x in sets]
+    out = torch.empty((ap.num_tokens, ap.num_heads, ap.head_dim), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((ap.num_tokens, ap.num_heads), dtype=torch.float32, device="cuda")
+
+    def launch(i):
+        Q.sparse_attention(q, c_cache, c_bt, c_lens, qsl, indices=idx[i % len(idx)], r_cache=r_cache,
+                           r_block_table=r_bt, r_lens=r_lens, window=ap.window, sinks=sinks, scale=ap.scale,
+                           c_page_rows=ap.c_page_rows, c_page_stride=ap.c_page_stride,
+                           c_num_pages=ap.c_pages.shape[0], r_page_rows=ap.r_page_rows,
+                           r_page_stride=ap.r_page_stride, r_num_pages=ap.r_pages.shape[0], out=out, lse=lse)
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    Q.qli_timing_read(reset=True)
+    Q.qli_timing_enable(True)
+    t0 = time.perf_counter()
+    try:
+        for i in range(steps):
+            launch(i)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        ms, cnt = Q.qli_timing_read(reset=True)
+    finally:
+        Q.qli_timing_enable(False)
+    kms = ms[Q.QLI_KERNEL_ATTN] / cnt[Q.QLI_KERNEL_ATTN]
+    entries = int((sets[0] >= 0).sum()) + ap.num_tokens * ap.window
+    T, H, D = ap.num_tokens, ap.num_heads, ap.head_dim
+    nbytes = entries * D * 2 + T * H * D * 2 * 2 + T * ap.topk * 4 + T * H * 4
+    flops = 4 * H * D * entries
+    achieved = nbytes / (kms * 1e-3) / 1e9
+    traffic, summary = recorded_traffic("attn_decode", "sparse_attn_kernel", source="qli_attn.hip")
+    log(f"attn_decode: {kms:.5f} ms {achieved:.1f} GB/s")
+    del c_cache, r_cache, idx
+    torch.cuda.empty_cache()
+    return {"attn_decode": {
+        "config": {"tokens": T, "heads": H, "head_dim": D, "topk": ap.topk, "window": ap.window,
+                   "compressed_len": int(ap.c_lens[0]), "page_rows": ap.c_page_rows,
+                   "page_stride_bytes": ap.c_page_stride, "sinks": True, "index_sets": len(sets)},
+        "kernel_ms": round(kms, 5), "ms_per_call": round(wall * 1e3, 5),
+        "entries_per_s": round(entries / (kms * 1e-3), 1),
+        "roofline": {"bound": "hbm", "kernel": "sparse_attn_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "traffic_summary": summary, "alg_bytes_per_launch": nbytes,
+                     "duration_source": "HIP events the library records around each launch"},
+        "bf16_mfma": {"flops_per_launch": flops, "achieved_TFLOPs": round(flops / (kms * 1e-3) / 1e12, 1),
+                      "peak_TFLOPs": BF16_PEAK_TFLOPS,
+                      "frac": round(flops / (kms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+    }}
+
+
 def measure_ceilings():
     """What this GPU sustains: a 2 GiB streaming read with 16-byte
     non-temporal loads (GB/s) and back-to-back independent INT8 MFMAs on
@@ -490,6 +568,10 @@ def main():
                          "layer calls of the mixed batch)")
     ap.add_argument("--no-producers", action="store_true",
                     help="skip the query-quantization and index-K write measurements")
+    ap.add_argument("--no-attention", action="store_true",
+                    help="skip the sparse-attention consumer of the indices")
+    ap.add_argument("--attention-only", action="store_true",
+                    help="only measure the sparse-attention consumer (one JSON object, for profiling runs)")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured HBM-read and INT8-MFMA ceilings")
     ap.add_argument("--producers-only", action="store_true",
@@ -522,6 +604,9 @@ def main():
     Q.load_library()
     if args.producers_only:
         print(json.dumps({"producers": measure_producers(args.steps, args.warmup)}), flush=True)
+        return
+    if args.attention_only:
+        print(json.dumps({"consumer_attention": measure_attention(args.steps, args.warmup)}), flush=True)
         return
 
     def prepare_workload(name, copies):
@@ -598,6 +683,11 @@ def main():
         for k, v in producers.items():
             log(f"{k}: {v['kernel_ms']:.5f} ms {v['roofline']['achieved']} GB/s")
 
+    attention = {}
+    if not args.no_attention:
+        log("consumer attention: sparse attention over the decode indices")
+        attention = measure_attention(args.steps, args.warmup)
+
     ceilings = None
     if not args.no_ceilings:
         log("ceilings: streaming read and INT8 MFMA probes")
@@ -613,7 +703,7 @@ def main():
 
     if ceilings is not None:
         with_measured(main_m["roofline"], ceilings)
-        for v in list(others.values()) + list(producers.values()):
+        for v in list(others.values()) + list(producers.values()) + list(attention.values()):
             for r in ([c["roofline"] for c in v["calls"].values()] if "calls" in v
                       else [v["roofline"]]):
                 with_measured(r, ceilings)
@@ -650,6 +740,7 @@ def main():
         "kernels_ms": main_m["kernels_ms"],
         "other_workloads": others,
         "producers": producers,
+        "consumer_attention": attention,
         "measured_ceilings": ceilings,
     }
     print(json.dumps(line), flush=True)

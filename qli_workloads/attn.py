@@ -124,10 +124,15 @@ def make_indices(seed, q_counts, c_lens, topk, layer=0, pad_frac=0.0, sparse_row
 
 
 def build_attn_problem(name, seed, q_counts, c_lens, r_lens, ratio, num_heads, topk, window,
-                       sinks=True, indices=None, pad_frac=0.0, fill_all=False):
+                       sinks=True, indices=None, pad_frac=0.0, fill_all=False, extra_indices=(),
+                       window_pages_only=False):
     """An attention call over requests with q_counts[b] query tokens, compressed
     lengths c_lens[b] and raw lengths r_lens[b]; the compressed cache uses the
-    indexer's shared page layout for ``ratio``."""
+    indexer's shared page layout for ``ratio``.  The rows of ``extra_indices``
+    (other index sets of the same shape, for timing with rotated inputs) are
+    drawn too.  ``window_pages_only``: raw pages wholly before every token's
+    window (never read) all map to one poisoned page, so the raw pool holds
+    only the pages the window reaches."""
     q_counts = np.asarray(q_counts, dtype=np.int64)
     c_lens = np.asarray(c_lens, dtype=np.int64)
     r_lens = np.asarray(r_lens, dtype=np.int64)
@@ -138,7 +143,17 @@ def build_attn_problem(name, seed, q_counts, c_lens, r_lens, ratio, num_heads, t
     qsl[1:] = np.cumsum(q_counts)
     c_rows, c_stride = page_layout(ratio)[:2]
     c_bt, c_np = _shuffled_table(seed, _TID_ABT, -(-c_lens // c_rows))
-    r_bt, r_np = _shuffled_table(seed, _TID_ABT + 100, -(-r_lens // RAW_PAGE_ROWS))
+    if window_pages_only:
+        first = np.maximum(0, r_lens - q_counts - window) // RAW_PAGE_ROWS  # first page a window reaches
+        n_pages = -(-r_lens // RAW_PAGE_ROWS)
+        live, _ = _shuffled_table(seed, _TID_ABT + 100, n_pages - first)
+        r_np = int((n_pages - first).sum()) + 1
+        r_bt = np.full((B, max(int(n_pages.max()), 1)), -1, dtype=np.int32)
+        for b in range(B):
+            r_bt[b, :first[b]] = r_np - 1          # the shared poisoned page
+            r_bt[b, first[b]:n_pages[b]] = live[b, :n_pages[b] - first[b]]
+    else:
+        r_bt, r_np = _shuffled_table(seed, _TID_ABT + 100, -(-r_lens // RAW_PAGE_ROWS))
     if indices is None:
         indices = make_indices(seed, q_counts, c_lens, topk, pad_frac=pad_frac)
     indices = np.ascontiguousarray(indices, dtype=np.int32)
@@ -148,7 +163,7 @@ def build_attn_problem(name, seed, q_counts, c_lens, r_lens, ratio, num_heads, t
     if not fill_all:
         c_pos, r_pos = [], []
         for b in range(B):
-            sel = indices[qsl[b]:qsl[b + 1]].reshape(-1)
+            sel = np.concatenate([x[qsl[b]:qsl[b + 1]].reshape(-1) for x in (indices, *extra_indices)])
             c_pos.append(sel[(sel >= 0) & (sel < c_lens[b])])
             p_last = int(r_lens[b]) - 1
             p_first = int(r_lens[b]) - int(q_counts[b]) - window + 1
@@ -170,13 +185,19 @@ def build_attn_problem(name, seed, q_counts, c_lens, r_lens, ratio, num_heads, t
                        indices=indices, sinks=sk)
 
 
-def attn_decode():
+def attn_decode(index_sets=1):
     """Decode attention after the decode_source indexer call: 64 requests x
     1 token, 32768 compressed positions (ratio 1, the indexer's 128-row pages
     at 147712 B), 2048 selected positions per token, a 128-position window
-    over the raw cache, 64 heads, D = 512, sinks."""
+    over the raw cache, 64 heads, D = 512, sinks.  With index_sets > 1 the
+    rows of that many independent index sets are drawn; returns the problem
+    and the list of index sets (the problem's own first)."""
     B = 64
-    return build_attn_problem("attn_decode", 11, [1] * B, [32768] * B, [32768] * B, 1, 64, 2048, 128)
+    q, c, r = [1] * B, np.full(B, 32768), np.full(B, 32768)
+    extra = [make_indices(11 + 1000 * s, q, c, 2048) for s in range(1, index_sets)]
+    ap = build_attn_problem("attn_decode", 11, q, c, r, 1, 64, 2048, 128, extra_indices=extra,
+                            window_pages_only=True)
+    return (ap, [ap.indices] + extra) if index_sets > 1 else ap
 
 
 def attn_small():

@@ -19,8 +19,8 @@
 //      (values: A operand of O^T = V^T P^T, 16x16x16 BF16 MFMAs).  The S^T
 //      accumulator of lane l holds head l % 16 for rows 4 (l / 16) .. + 3,
 //      which is exactly the B operand P^T needs, so the weights never leave
-//      their lanes.  The next step's rows are loaded into registers while a
-//      step is scored.
+//      their lanes.  The rows of three steps ahead are in flight in
+//      registers while a step is scored.
 //   3. The two pairs' states meet in LDS; each thread writes 32 outputs of
 //      one head.
 // Keys and values are the same cache entry (one shared latent KV head).
@@ -35,11 +35,12 @@ namespace {
 
 constexpr int kD = 512;               // head dim (key and value width)
 constexpr int kHeadsWG = 16;          // heads per workgroup
-constexpr int kAttnThreads = 256;     // four waves
+constexpr int kAttnThreads = 512;     // eight waves: four pairs
 constexpr int kTile = 16;             // entries per wave tile
 constexpr int kMaxEntries = QLI_ATTN_MAX_TOPK + QLI_ATTN_MAX_WINDOW;
 constexpr int kWaveLds = 2 * kTile * kD * 2;  // one tile buffer: row-major and transposed copies, 32 KB
-constexpr int kQOff = 4 * kWaveLds;           // the 16 heads' queries after the four tile buffers
+constexpr int kPairs = kAttnThreads / 128;   // wave pairs, one tile buffer each
+constexpr int kQOff = kPairs * kWaveLds;      // the 16 heads' queries after the tile buffers
 constexpr int kEntOff = kQOff + kHeadsWG * kD * 2;  // entries (4 bytes each)
 constexpr int kMiscOff = kEntOff + kMaxEntries * 4;
 constexpr int kLdsBytes = kMiscOff + 1024;
@@ -96,7 +97,7 @@ __device__ __forceinline__ float wave_sum_heads(float x) {
   return x + __shfl_xor(x, 32);
 }
 
-// Exclusive prefix sum over the 256 threads (sh: four words of LDS).
+// Exclusive prefix sum over the workgroup's threads (sh: one word per wave).
 __device__ uint32_t block_exclusive_scan_attn(uint32_t v, uint32_t* total, uint32_t* sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t inc = v;
@@ -231,30 +232,39 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
     E = static_cast<int>(total);
   }
   __syncthreads();
+  // the last tile is padded with copies of the last entry (scored as absent),
+  // so that a wave reads its 8 entries of a tile with two vector loads
+  if (E > 0 && tid < kTile) {
+    const uint32_t last = ent[E - 1];
+    if (E + tid < (E + kTile - 1) / kTile * kTile) ent[E + tid] = last;
+  }
+  __syncthreads();
 
-  // 2. the tiles: wave pair pi = wave / 2 takes tiles pi, pi + 2, ...; both
+  // 2. the tiles: wave pair pi = wave / 2 takes tiles pi, pi + 4, ...; both
   // waves of a pair score every tile of the pair (the logits of all 16
   // heads) and each keeps the outputs of half the dims, dims
   // 256 eta .. + 255 (eta = wave % 2), so that its accumulators fit the
-  // registers.  A pair's tiles alternate between two LDS buffers; each
-  // wave stages 8 of a tile's 16 rows.  One workgroup barrier per step.
+  // registers of two waves per SIMD.  Each pair has one LDS tile buffer;
+  // each wave stages 8 of a tile's 16 rows.  Two workgroup barriers per
+  // step (tiles staged; tiles scored).
   const int pi = wave >> 1, eta = wave & 1;
   const int ntiles = (E + kTile - 1) / kTile;
-  const int nsteps = (ntiles + 1) / 2;
+  const int nsteps = (ntiles + kPairs - 1) / kPairs;
   float m_run = -INFINITY, l_run = 0.0f;
   constexpr int kOT = kD / 2 / 16;  // output tiles of a wave: 16
   f4 o[kOT];
 #pragma unroll
   for (int mt = 0; mt < kOT; ++mt) o[mt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-  auto kbuf = [&](int step) { return lds + (pi * 2 + (step & 1)) * kWaveLds; };
+  char* const kbuf = lds + pi * kWaveLds;
 
   // this wave's 8 rows of tile k (lane: 16 bytes `lane` of each row),
-  // issued together; rows past E read the last entry again (scored as absent)
+  // issued together (rows past E repeat the last entry, scored as absent)
   auto load = [&](int k, i4 (&rr)[kTile / 2]) {
+    const i4 e0 = *reinterpret_cast<const i4*>(ent + kTile * k + 8 * eta);
+    const i4 e1 = *reinterpret_cast<const i4*>(ent + kTile * k + 8 * eta + 4);
 #pragma unroll
     for (int i = 0; i < kTile / 2; ++i) {
-      const int e = min(kTile * k + 8 * eta + i, E - 1);
-      const uint32_t en = __builtin_amdgcn_readfirstlane(ent[e]);
+      const uint32_t en = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(i < 4 ? e0[i] : e1[i - 4]));
       const bool raw = (en >> 31) != 0;
       const char* base = raw ? a.r_cache : a.c_cache;
       const int64_t stride = raw ? a.r_stride : a.c_stride;
@@ -287,19 +297,22 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
   auto score = [&](const char* kt, int n) {
     const int ln = opaque_lane();
     const char* vt = kt + kTile * kD * 2;
-    f4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+    // two independent accumulator chains (even and odd k-steps) halve the
+    // dependent MFMA latency
+    f4 sa = {0.0f, 0.0f, 0.0f, 0.0f}, sb = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int kg = 0; kg < kD / 32; kg += 4) {  // four k-steps per group: bounded operand prefetch
-#pragma unroll
-      for (int ks = kg; ks < kg + 4; ++ks) {
-        const int ch = 4 * ks + (ln >> 4);
-        const i4 kv = *reinterpret_cast<const i4*>(kt + krm_offset(ln & 15, ch));
-        const i4 qv = *reinterpret_cast<const i4*>(qs + krm_offset(ln & 15, ch));
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, kv), __builtin_bit_cast(bf8, qv),
-                                                       sacc, 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int ks = 0; ks < kD / 32; ks += 2) {
+      const int ch = 4 * ks + (ln >> 4);
+      const i4 kv0 = *reinterpret_cast<const i4*>(kt + krm_offset(ln & 15, ch));
+      const i4 qv0 = *reinterpret_cast<const i4*>(qs + krm_offset(ln & 15, ch));
+      const i4 kv1 = *reinterpret_cast<const i4*>(kt + krm_offset(ln & 15, ch + 4));
+      const i4 qv1 = *reinterpret_cast<const i4*>(qs + krm_offset(ln & 15, ch + 4));
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, kv0), __builtin_bit_cast(bf8, qv0), sa,
+                                                   0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, kv1), __builtin_bit_cast(bf8, qv1), sb,
+                                                   0, 0, 0);
     }
+    const f4 sacc = sa + sb;
     // sacc[i]: head lane % 16, row 4 (lane / 16) + i
     float z[4];
     float tmax = -INFINITY;
@@ -309,18 +322,28 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
       tmax = fmaxf(tmax, z[i]);
     }
     tmax = wave_max_heads(tmax);
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = m_new == -INFINITY ? 1.0f : exp2f(m_run - m_new);
+    // The weights are taken against a reference maximum m_run that moves
+    // only when a head's logits pass it by more than 8 (weights below 2^8,
+    // exact as BF16 exponents and harmless in the FP32 sums): the output
+    // accumulators are rescaled on those few tiles only (a wave-uniform
+    // branch), so the matrix core keeps them the rest of the time.
+    const float m_cand = fmaxf(m_run, tmax);
+    if (__ballot(m_cand > m_run + 8.0f) != 0) {
+      const float alpha = m_cand == -INFINITY ? 1.0f : exp2f(m_run - m_cand);
+#pragma unroll
+      for (int mt = 0; mt < kOT; ++mt) o[mt] *= alpha;
+      l_run *= alpha;
+      m_run = m_cand;
+    }
     uint32_t pb[4];
     float psum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float pw = z[i] == -INFINITY ? 0.0f : exp2f(z[i] - m_new);
+      const float pw = z[i] == -INFINITY ? 0.0f : exp2f(z[i] - m_run);
       pb[i] = bf16_rne(pw);
       psum += __uint_as_float(pb[i] << 16);
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    l_run += psum;
     const s4 pv = {static_cast<short>(pb[0]), static_cast<short>(pb[1]), static_cast<short>(pb[2]),
                    static_cast<short>(pb[3])};
     const int r0 = 4 * (ln >> 4);
@@ -333,25 +356,38 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
         vv[j] = *reinterpret_cast<const i2*>(vt + vt_offset(d, r0 >> 3) + (r0 & 7) * 2);
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        o[mg + j] *= alpha;
+      for (int j = 0; j < 8; ++j)
         o[mg + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, vv[j]), pv, o[mg + j], 0, 0, 0);
-      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   {
-    i4 rr[kTile / 2];
-    int k = pi;  // this pair's tile of the current step
-    if (k < ntiles) load(k, rr);
-    for (int step = 0; step < nsteps; ++step) {
-      if (k < ntiles) stage(kbuf(step), rr);
-      __syncthreads();  // the step's tiles are staged (and the buffers of two steps ago are free)
-      const int kn = k + 2;
-      if (kn < ntiles) load(kn, rr);
-      if (k < ntiles) score(kbuf(step), min(kTile, E - kTile * k));
-      k = kn;
+    // a ring of two register sets: the rows of step s + 2 are loaded while
+    // step s is scored.  Every load is issued unconditionally (a tile past
+    // the end reads the last tile again), so that the compiler's memory
+    // counters stay exact and staging a set waits for that set's loads only.
+    i4 r0[kTile / 2], r1[kTile / 2];
+    auto step_body = [&](int step, i4 (&rr)[kTile / 2]) {
+      const bool live = step < nsteps;  // workgroup-uniform
+      const int k = pi + kPairs * step; // this pair's tile of the step
+      if (live && k < ntiles) stage(kbuf, rr);
+      if (live) __syncthreads();  // the step's tiles are staged
+      __builtin_amdgcn_sched_barrier(0);  // the sets' loads stay in issue order
+      load(min(k + 2 * kPairs, ntiles - 1), rr);
+      __builtin_amdgcn_sched_barrier(0);
+      if (live && k < ntiles) score(kbuf, min(kTile, E - kTile * k));
+      if (live) __syncthreads();  // the step's tiles are scored: the buffers are free
+    };
+    if (ntiles > 0) {
+      load(min(pi, ntiles - 1), r0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(min(pi + kPairs, ntiles - 1), r1);
+      __builtin_amdgcn_sched_barrier(0);
+      for (int step = 0; step < nsteps; step += 2) {
+        step_body(step, r0);
+        step_body(step + 1, r1);
+      }
     }
   }
 
@@ -360,6 +396,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
   __syncthreads();  // every wave is done with the tile buffers
   float* mo = reinterpret_cast<float*>(lds);  // [pair][head][D]
   float* ml = reinterpret_cast<float*>(lds + kMiscOff + 256);  // [pair][head]: m, then l
+  static_assert(kPairs * kHeadsWG * kD * 4 <= kQOff, "pair outputs over the tile buffers");
 #pragma unroll
   for (int mt = 0; mt < kOT; ++mt) {
     const int d0 = (kD / 2) * eta + 16 * mt + 4 * (lane >> 4);
@@ -367,30 +404,31 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
   }
   if (eta == 0 && lane < 16) {
     ml[pi * kHeadsWG + lane] = m_run;
-    ml[64 + pi * kHeadsWG + lane] = l_run;
+    ml[kPairs * kHeadsWG + pi * kHeadsWG + lane] = l_run;
   }
   __syncthreads();
   {
-    const int h = tid >> 4;          // head within the group
-    const int d0 = 32 * (tid & 15);  // 32 outputs
+    constexpr int kPer = kHeadsWG * kD / kAttnThreads;  // outputs per thread: 16
+    const int h = tid / (kD / kPer);                    // head within the group
+    const int d0 = kPer * (tid % (kD / kPer));
     const bool has_sink = a.sinks != nullptr && b >= 0;  // a token outside every request: 0, -inf
     const float sk = has_sink ? a.sinks[kHeadsWG * g + h] * kLog2e : -INFINITY;
     float M = sk;
 #pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) M = fmaxf(M, ml[q2 * kHeadsWG + h]);
-    float cw[2];
+    for (int q2 = 0; q2 < kPairs; ++q2) M = fmaxf(M, ml[q2 * kHeadsWG + h]);
+    float cw[kPairs];
     float den = 0.0f;
 #pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) {
+    for (int q2 = 0; q2 < kPairs; ++q2) {
       const float mw = ml[q2 * kHeadsWG + h];
       cw[q2] = mw == -INFINITY ? 0.0f : exp2f(mw - M);
-      den += cw[q2] * ml[64 + q2 * kHeadsWG + h];
+      den += cw[q2] * ml[kPairs * kHeadsWG + q2 * kHeadsWG + h];
     }
     if (has_sink) den += exp2f(sk - M);
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
     uint16_t* orow = a.out + (static_cast<int64_t>(t) * a.H + kHeadsWG * g + h) * kD + d0;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < kPer / 8; ++v) {
       i4 pk;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -400,14 +438,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
           const int d = d0 + 8 * v + 2 * j + u;
           float acc = 0.0f;
 #pragma unroll
-          for (int q2 = 0; q2 < 2; ++q2) acc += cw[q2] * mo[(q2 * kHeadsWG + h) * kD + d];
+          for (int q2 = 0; q2 < kPairs; ++q2) acc += cw[q2] * mo[(q2 * kHeadsWG + h) * kD + d];
           two[u] = bf16_rne(acc * inv);
         }
         pk[j] = static_cast<int>(two[0] | (two[1] << 16));
       }
       *reinterpret_cast<i4*>(orow + 8 * v) = pk;
     }
-    if (a.lse && (tid & 15) == 0)
+    if (a.lse && d0 == 0)
       a.lse[static_cast<int64_t>(t) * a.H + kHeadsWG * g + h] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
   }
 }
