@@ -11,17 +11,18 @@
 //   1. The token's entries (its valid index positions, then its window) are
 //      resolved through the block tables into row addresses, compacted in
 //      order into LDS.
-//   2. Two pairs of waves take alternate tiles of 16 entries; both waves
-//      of a pair score every tile of the pair (the 16 heads' logits) and
-//      keep their own online softmax, each for the outputs of half the
-//      dims.  A tile's rows go into LDS twice, row-major (keys: A operand
+//   2. Four pairs of waves (eight waves, two per SIMD) take every fourth
+//      tile of 16 entries; both waves of a pair score every tile of the
+//      pair (the 16 heads' logits, queries held in registers) and keep their
+//      own online softmax, each for the outputs of half the dims.  A tile's
+//      rows go into the pair's LDS buffer twice, row-major (keys: A operand
 //      of S^T = K Q^T, 16x16x32 BF16 MFMAs over D = 512) and transposed
 //      (values: A operand of O^T = V^T P^T, 16x16x16 BF16 MFMAs).  The S^T
 //      accumulator of lane l holds head l % 16 for rows 4 (l / 16) .. + 3,
 //      which is exactly the B operand P^T needs, so the weights never leave
-//      their lanes.  The rows of three steps ahead are in flight in
-//      registers while a step is scored.
-//   3. The two pairs' states meet in LDS; each thread writes 32 outputs of
+//      their lanes.  The rows of two steps ahead are in flight in registers
+//      while a step is scored.
+//   3. The four pairs' states meet in LDS; each thread writes 16 outputs of
 //      one head.
 // Keys and values are the same cache entry (one shared latent KV head).
 #include <hip/hip_runtime.h>
@@ -40,8 +41,8 @@ constexpr int kTile = 16;             // entries per wave tile
 constexpr int kMaxEntries = QLI_ATTN_MAX_TOPK + QLI_ATTN_MAX_WINDOW;
 constexpr int kWaveLds = 2 * kTile * kD * 2;  // one tile buffer: row-major and transposed copies, 32 KB
 constexpr int kPairs = kAttnThreads / 128;   // wave pairs, one tile buffer each
-constexpr int kQOff = kPairs * kWaveLds;      // the 16 heads' queries after the tile buffers
-constexpr int kEntOff = kQOff + kHeadsWG * kD * 2;  // entries (4 bytes each)
+constexpr int kQOff = kPairs * kWaveLds;      // end of the tile buffers
+constexpr int kEntOff = kQOff;                // entries (4 bytes each)
 constexpr int kMiscOff = kEntOff + kMaxEntries * 4;
 constexpr int kLdsBytes = kMiscOff + 1024;
 static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
@@ -153,20 +154,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
   const int t = x + 8 * (r / a.G);
   if (t >= a.T) return;
   uint32_t* ent = reinterpret_cast<uint32_t*>(lds + kEntOff);
-  char* qs = lds + kQOff;
   int* misc = reinterpret_cast<int*>(lds + kMiscOff);
   uint32_t* scan = reinterpret_cast<uint32_t*>(misc + 16);
 
-  // the queries of the workgroup's 16 heads (every wave scores all 16) in
-  // LDS, chunk ch (16 B) of head h at chunk ch ^ h
+  // the queries of the workgroup's 16 heads (every wave scores all 16), as
+  // B operands of S^T: lane l holds head 16 g + l % 16, dims
+  // 32 ks + 8 (l / 16) .. + 7
+  bf8 qf[kD / 32];
   {
-    const uint16_t* qg = a.q + (static_cast<int64_t>(t) * a.H + kHeadsWG * g) * kD;
+    const uint16_t* qrow = a.q + (static_cast<int64_t>(t) * a.H + kHeadsWG * g + (lane & 15)) * kD + 8 * (lane >> 4);
 #pragma unroll
-    for (int u = 0; u < kHeadsWG * kD / 8 / kAttnThreads; ++u) {
-      const int c = u * kAttnThreads + tid;  // 16-byte chunk of the group's queries
-      const int h = c >> 6, ch = c & 63;
-      *reinterpret_cast<i4*>(qs + krm_offset(h, ch)) = *reinterpret_cast<const i4*>(qg + 8 * c);
-    }
+    for (int ks = 0; ks < kD / 32; ++ks) qf[ks] = __builtin_bit_cast(bf8, *reinterpret_cast<const i4*>(qrow + 32 * ks));
   }
 
   // 1. request, raw position and the entry list
@@ -304,13 +302,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
     for (int ks = 0; ks < kD / 32; ks += 2) {
       const int ch = 4 * ks + (ln >> 4);
       const i4 kv0 = *reinterpret_cast<const i4*>(kt + krm_offset(ln & 15, ch));
-      const i4 qv0 = *reinterpret_cast<const i4*>(qs + krm_offset(ln & 15, ch));
       const i4 kv1 = *reinterpret_cast<const i4*>(kt + krm_offset(ln & 15, ch + 4));
-      const i4 qv1 = *reinterpret_cast<const i4*>(qs + krm_offset(ln & 15, ch + 4));
-      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, kv0), __builtin_bit_cast(bf8, qv0), sa,
-                                                   0, 0, 0);
-      sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, kv1), __builtin_bit_cast(bf8, qv1), sb,
-                                                   0, 0, 0);
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, kv0), qf[ks], sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, kv1), qf[ks + 1], sb, 0, 0, 0);
     }
     const f4 sacc = sa + sb;
     // sacc[i]: head lane % 16, row 4 (lane / 16) + i
