@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define QLI_ABI_VERSION 5
+#define QLI_ABI_VERSION 6
 
 /* Status codes returned by the host entry points. */
 enum qli_status {
@@ -355,10 +355,20 @@ typedef struct qli_attn_params {
   void* out;                /* BF16 [T][H][D] written (16-B aligned) */
   float* lse;               /* [T][H] written, or NULL */
   uint32_t* status_out;     /* optional device word receiving QLI_DEV_* bits (ORed) */
+  void* workspace;          /* optional device scratch (256-B aligned, no initial
+                               contents needed) for calls whose heads are a multiple
+                               of 64: a token's entries are then split over several
+                               workgroups, whose partial softmax states a second
+                               launch merges from here.  Calls that share a workspace
+                               must be ordered on one stream.  NULL (or too small for
+                               any split): one workgroup per (token, 64 heads), one
+                               launch, the same results up to FP32 rounding order */
+  int64_t workspace_bytes;  /* bytes at workspace (>= 0) */
 } qli_attn_params;
 
-/* Enqueue the attention of num_tokens query tokens on `stream`: one launch,
- * no allocation, no synchronisation.  The host checks the parameters first
+/* Enqueue the attention of num_tokens query tokens on `stream`: one launch
+ * (two when the entries are split over a workspace), no allocation, no
+ * synchronisation.  The host checks the parameters first
  * (QLI_ERR_INVALID_ARG / QLI_ERR_UNSUPPORTED, nothing launched); pointers
  * must be device memory, and every integer pointer 4-byte aligned.  Device
  * data outside the contract above is never read beyond the pools, tables
@@ -366,10 +376,18 @@ typedef struct qli_attn_params {
  * Returns a qli_status. */
 int qli_sparse_attention(const qli_attn_params* p, void* stream);
 
+/* Workspace bytes with which qli_sparse_attention splits each token's
+ * entries over the most workgroups it would use for these scalars
+ * (num_tokens, num_heads, topk, window; host-only).  0 when no split is
+ * taken (p NULL, heads not a multiple of 64, or enough tokens to fill the
+ * GPU without one). */
+int64_t qli_attn_workspace_bytes(const qli_attn_params* p);
+
 /* Kernels, in launch order within a call (for the timing facility below). */
 enum qli_kernel { QLI_KERNEL_CONSUMER_PREP = 0, QLI_KERNEL_PLAN = 1, QLI_KERNEL_SCORE = 2,
                   QLI_KERNEL_SELECT = 3, QLI_KERNEL_QUANTIZE = 4, QLI_KERNEL_WRITE_K = 5,
-                  QLI_KERNEL_ATTN = 6, QLI_NUM_KERNELS = 7 };
+                  QLI_KERNEL_ATTN = 6, QLI_KERNEL_ATTN_SPLIT = 7,
+                  QLI_KERNEL_ATTN_MERGE = 8, QLI_NUM_KERNELS = 9 };
 
 /* Optional per-kernel timing (off by default; process-wide, not thread
  * safe).  While enabled, every call of this library records a HIP event

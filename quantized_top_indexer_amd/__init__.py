@@ -88,22 +88,25 @@ class qli_attn_params(C.Structure):
         ("c_lens", C.c_void_p), ("r_cache", C.c_void_p), ("r_block_table", C.c_void_p),
         ("r_lens", C.c_void_p), ("query_start_loc", C.c_void_p), ("indices", C.c_void_p),
         ("sinks", C.c_void_p), ("out", C.c_void_p), ("lse", C.c_void_p),
-        ("status_out", C.c_void_p),
+        ("status_out", C.c_void_p), ("workspace", C.c_void_p), ("workspace_bytes", C.c_int64),
     ]
 
 
 EXPORTS = ("qli_abi_version", "qli_validate", "qli_workspace_bytes", "qli_score_topk",
            "qli_score_topk_noalloc", "qli_status_string", "qli_timing_enable", "qli_timing_read",
-           "qli_quantize_query", "qli_write_index_k", "qli_sparse_attention")
+           "qli_quantize_query", "qli_write_index_k", "qli_sparse_attention",
+           "qli_attn_workspace_bytes")
 # the ceiling probes (include/qli_probe.h): a library of their own, for
 # measurement only
 PROBE_LIB_PATH = os.path.join(_HERE, "libqli_probe.so")
 PROBE_EXPORTS = ("qli_probe_hbm_read", "qli_probe_int8_mfma", "qli_probe_int8_mfma_ops")
 QLI_KERNEL_CONSUMER_PREP, QLI_KERNEL_PLAN, QLI_KERNEL_SCORE, QLI_KERNEL_SELECT, \
-    QLI_KERNEL_QUANTIZE, QLI_KERNEL_WRITE_K, QLI_KERNEL_ATTN, QLI_NUM_KERNELS = range(8)
+    QLI_KERNEL_QUANTIZE, QLI_KERNEL_WRITE_K, QLI_KERNEL_ATTN, QLI_KERNEL_ATTN_SPLIT, \
+    QLI_KERNEL_ATTN_MERGE, QLI_NUM_KERNELS = range(10)
 KERNEL_NAMES = ("consumer_prep_kernel", "plan_kernel", "score_kernel", "select_kernel",
-                "quantize_kernel", "write_k_kernel", "sparse_attn_kernel")
-QLI_ABI_VERSION = 5
+                "quantize_kernel", "write_k_kernel", "sparse_attn_kernel", "sparse_attn_split_kernel",
+                "sparse_attn_merge_kernel")
+QLI_ABI_VERSION = 6
 
 _lib = None
 
@@ -143,6 +146,8 @@ def load_library(path: str = LIB_PATH):
     L.qli_write_index_k.argtypes = [C.POINTER(qli_kwrite_params), C.c_void_p]
     L.qli_sparse_attention.restype = C.c_int
     L.qli_sparse_attention.argtypes = [C.POINTER(qli_attn_params), C.c_void_p]
+    L.qli_attn_workspace_bytes.restype = C.c_int64
+    L.qli_attn_workspace_bytes.argtypes = [C.POINTER(qli_attn_params)]
     if path == LIB_PATH:
         _lib = L
     return L
@@ -301,17 +306,38 @@ def qli_sparse_attention(p: qli_attn_params, stream=None) -> int:
     return load_library().qli_sparse_attention(C.byref(p), _stream(stream))
 
 
+_attn_ws = {}
+
+
+def attention_workspace(nbytes: int, device):
+    """The cached attention workspace of `device` with at least nbytes (None
+    for nbytes == 0).  Calls that use it must be ordered on one stream."""
+    import torch
+    if nbytes <= 0:
+        return None
+    key = str(device)
+    ws = _attn_ws.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _attn_ws[key] = ws
+    return ws
+
+
 def sparse_attention(q, c_cache, c_block_table, c_lens, query_start_loc, *, indices=None,
                      r_cache=None, r_block_table=None, r_lens=None, window=0, sinks=None,
                      scale=None, c_page_rows, c_page_stride, r_page_rows=0, r_page_stride=0,
-                     c_num_pages, r_num_pages=0, out=None, lse=None, status_out=None, stream=None):
+                     c_num_pages, r_num_pages=0, out=None, lse=None, status_out=None, stream=None,
+                     workspace="auto"):
     """Sparse attention over the indexer's positions (argument marshalling
     for qli_sparse_attention): q bfloat16 [T, H, 512]; c_cache / r_cache
     device buffers of BF16 rows paged as described in include/qli.h (any
     tensor, passed by address with the page geometry given explicitly);
     block tables int32 [B, stride]; lengths int32 [B]; query_start_loc
     int32 [B + 1]; indices int32 [T, topk] or None; sinks float32 [H] or
-    None.  Returns (out bfloat16 [T, H, 512], lse float32 [T, H] or None)."""
+    None.  workspace: a uint8 device tensor (any contents), None for no
+    split, or "auto" for one cached per device, grown as calls need it;
+    calls sharing a workspace must be ordered on one stream.  Returns
+    (out bfloat16 [T, H, 512], lse float32 [T, H] or None)."""
     import torch
     T, H, D = q.shape
     if out is None:
@@ -332,6 +358,10 @@ def sparse_attention(q, c_cache, c_block_table, c_lens, query_start_loc, *, indi
     p.r_cache, p.r_block_table, p.r_lens = _ptr(r_cache), _ptr(r_block_table), _ptr(r_lens)
     p.indices, p.sinks = _ptr(indices), _ptr(sinks)
     p.out, p.lse, p.status_out = out.data_ptr(), _ptr(lse), _ptr(status_out)
+    if isinstance(workspace, str) and workspace == "auto":
+        workspace = attention_workspace(load_library().qli_attn_workspace_bytes(C.byref(p)), q.device)
+    if workspace is not None:
+        p.workspace, p.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     rc = qli_sparse_attention(p, stream)
     if rc != QLI_OK:
         raise RuntimeError(qli_status_string(rc))

@@ -150,6 +150,7 @@ int check_attn(const qli_attn_params* p) {
       !aligned(p->r_lens, 4) || !aligned(p->query_start_loc, 4) || !aligned(p->indices, 4) ||
       !aligned(p->sinks, 4) || !aligned(p->lse, 4) || !aligned(p->status_out, 4))
     return QLI_ERR_INVALID_ARG;
+  if (p->workspace_bytes < 0 || !aligned(p->workspace, 256)) return QLI_ERR_INVALID_ARG;
   return QLI_OK;
 }
 
@@ -162,6 +163,12 @@ int qli_sparse_attention(const qli_attn_params* p, void* stream) {
   if (rc != QLI_OK) return rc;
   if (p->num_tokens == 0) return QLI_OK;
   return qli::launch_attention(p, stream);
+}
+
+int64_t qli_attn_workspace_bytes(const qli_attn_params* p) {
+  if (!p || p->num_tokens <= 0 || p->num_heads <= 0 || p->topk < 0 || p->window < 0) return 0;
+  return qli::attention_workspace_bytes(p->num_tokens, p->num_heads, p->topk, p->window,
+                                        qli::attention_splits(p->num_tokens, p->num_heads, p->topk, p->window));
 }
 
 int qli_quantize_query(const qli_quant_params* p, void* stream) {

@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "qli.h"
 #include "qli_internal.h"
 
@@ -76,6 +78,11 @@ struct AttnArgs {
   uint16_t* out;
   float* lse;
   uint32_t* status;
+  // the split kernel: splits per token, blocks of 64 heads, partial states
+  // [T][HB][S][64] (m, l) and [T][HB][S][64][D]
+  int S, HB;
+  float* wml;
+  float* wo;
 };
 
 __device__ __forceinline__ void flag(const AttnArgs& a, uint32_t bits) {
@@ -144,36 +151,21 @@ __device__ __forceinline__ int opaque_lane() {
 // Row-major tile layout: chunk ch (16 B) of row i at chunk ch ^ i.
 __device__ __forceinline__ int krm_offset(int i, int ch) { return i * (kD * 2) + ((ch ^ i) << 4); }
 
-__global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // workgroup -> (token, head group); the head groups of a token share i mod 8
-  const int x = blockIdx.x & 7, r = blockIdx.x >> 3;
-  const int g = r % a.G;
-  const int t = x + 8 * (r / a.G);
-  if (t >= a.T) return;
-  uint32_t* ent = reinterpret_cast<uint32_t*>(lds + kEntOff);
-  int* misc = reinterpret_cast<int*>(lds + kMiscOff);
-  uint32_t* scan = reinterpret_cast<uint32_t*>(misc + 16);
-
-  // the queries of the workgroup's 16 heads (every wave scores all 16), as
-  // B operands of S^T: lane l holds head 16 g + l % 16, dims
-  // 32 ks + 8 (l / 16) .. + 7
-  bf8 qf[kD / 32];
-  {
-    const uint16_t* qrow = a.q + (static_cast<int64_t>(t) * a.H + kHeadsWG * g + (lane & 15)) * kD + 8 * (lane >> 4);
-#pragma unroll
-    for (int ks = 0; ks < kD / 32; ++ks) qf[ks] = __builtin_bit_cast(bf8, *reinterpret_cast<const i4*>(qrow + 32 * ks));
-  }
-
-  // 1. request, raw position and the entry list
+// The entries of token t, resolved through both block tables and compacted
+// in order into ent (index positions first, then the window), padded with
+// copies of the last entry to a multiple of `pad`; returns their count and
+// the token's request in *b_out (-1: outside every request).  Called by all
+// kAttnThreads threads of the workgroup.
+__device__ int token_entries(const AttnArgs& a, int t, uint32_t* ent, int* misc, uint32_t* scan, int pad,
+                             int* b_out) {
+  const int tid = threadIdx.x;
   if (tid == 0) misc[0] = -1;
   __syncthreads();
   for (int i = tid; i < a.B; i += kAttnThreads)
     if (a.qsl[i] <= t && t < a.qsl[i + 1]) misc[0] = i;
   __syncthreads();
   const int b = misc[0];
+  *b_out = b;
   int E = 0;
   if (b >= 0) {
     const int q0 = a.qsl[b], q1 = a.qsl[b + 1];
@@ -231,12 +223,41 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
   }
   __syncthreads();
   // the last tile is padded with copies of the last entry (scored as absent),
-  // so that a wave reads its 8 entries of a tile with two vector loads
-  if (E > 0 && tid < kTile) {
+  // so that a wave reads its entries of a tile with vector loads
+  if (E > 0 && tid < pad) {
     const uint32_t last = ent[E - 1];
-    if (E + tid < (E + kTile - 1) / kTile * kTile) ent[E + tid] = last;
+    if (E + tid < (E + pad - 1) / pad * pad) ent[E + tid] = last;
   }
   __syncthreads();
+  return E;
+}
+
+__global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // workgroup -> (token, head group); the head groups of a token share i mod 8
+  const int x = blockIdx.x & 7, r = blockIdx.x >> 3;
+  const int g = r % a.G;
+  const int t = x + 8 * (r / a.G);
+  if (t >= a.T) return;
+  uint32_t* ent = reinterpret_cast<uint32_t*>(lds + kEntOff);
+  int* misc = reinterpret_cast<int*>(lds + kMiscOff);
+  uint32_t* scan = reinterpret_cast<uint32_t*>(misc + 16);
+
+  // the queries of the workgroup's 16 heads (every wave scores all 16), as
+  // B operands of S^T: lane l holds head 16 g + l % 16, dims
+  // 32 ks + 8 (l / 16) .. + 7
+  bf8 qf[kD / 32];
+  {
+    const uint16_t* qrow = a.q + (static_cast<int64_t>(t) * a.H + kHeadsWG * g + (lane & 15)) * kD + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < kD / 32; ++ks) qf[ks] = __builtin_bit_cast(bf8, *reinterpret_cast<const i4*>(qrow + 32 * ks));
+  }
+
+  // 1. request, raw position and the entry list
+  int b;
+  const int E = token_entries(a, t, ent, misc, scan, kTile, &b);
 
   // 2. the tiles: wave pair pi = wave / 2 takes tiles pi, pi + 4, ...; both
   // waves of a pair score every tile of the pair (the logits of all 16
@@ -444,7 +465,321 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// All 64 heads of a block in one workgroup; a token's entries split over S
+// workgroups whose partial softmax states meet in a workspace.
+//
+// Workgroup (token t, head block hb, split s): steps of 32 entries, split s
+// taking steps [N s / S, N (s + 1) / S) of the token's N, so each row is
+// loaded and staged into LDS once for all 64 heads (the head-group kernel
+// above stages every row once per 16 heads).  Eight waves: wave w scores
+// half eta = w / 4 of a step (entries 16 eta .. + 15) for head group
+// hg = w % 4 and keeps the outputs of dims 256 eta .. + 255 of those 16
+// heads; the two waves of a head group trade their logits through LDS, so
+// both see all 32 logits of a step and take identical softmax decisions.
+// O^T = V^T P^T runs as 16x16x32 MFMAs over the whole step: k slot
+// 8 (l / 16) + j of lane l stands for entry 4 (l / 16) + j of the first
+// half (j < 4) or of the second (j >= 4), which is where the S^T
+// accumulators of the two halves hold their logits.  The step's rows sit
+// in LDS twice, row-major (keys) and transposed (values), in two buffers:
+// a step is staged while the previous one is scored, one barrier after
+// staging and one for the logit exchange.  With S > 1 each workgroup writes
+// its softmax state (outputs relative to its maximum, maximum, normalizer)
+// to the workspace and a second launch merges a token's states; with S = 1
+// the workgroup writes the outputs itself.
+
+constexpr int kStepE = 32;                        // entries per step
+constexpr int kSplitBuf = 2 * kStepE * kD * 2;   // one step: keys, then values: 64 KB
+constexpr int kSZOff = 2 * kSplitBuf;             // logits exchange: 8 waves x 64 lanes x 16 B
+constexpr int kSEntOff = kSZOff + 8 * 64 * 16;
+constexpr int kSMiscOff = kSEntOff + kMaxEntries * 4;
+constexpr int kSLdsBytes = kSMiscOff + 1024;
+constexpr int kMaxSplits = 4;
+static_assert(kSLdsBytes <= 160 * 1024, "LDS of one workgroup");
+static_assert(kMaxEntries % kStepE == 0, "padded entry lists fit");
+
+// Transposed step layout: the values of dim d for entry quads c and c + 4
+// (entries 4c .. 4c + 3 and 16 + 4c .. + 3) share a 16-byte slot; quad half
+// h sits at byte 8 (h ^ bit 6 of d).  The slots of eight consecutive dims
+// (one MFMA operand load of eight lanes) and of the dims 8 apart written by
+// one store instruction fall on distinct LDS banks.
+__device__ __forceinline__ int vts_slot(int d, int c) {
+  return ((((d >> 3) << 2) + c) << 7) + (((d ^ (d >> 3) ^ c) & 7) << 4);
+}
+
+__global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_split_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kSLdsBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // workgroup -> (token, head block, split); the workgroups of a token share
+  // i mod 8 (one XCD)
+  const int U = a.HB * a.S;
+  const int x = blockIdx.x & 7, r = blockIdx.x >> 3;
+  const int u = r % U;
+  const int t = x + 8 * (r / U);
+  if (t >= a.T) return;
+  const int hb = u / a.S, s = u % a.S;
+  const int hg = wave & 3, eta = wave >> 2;
+  const int h = 64 * hb + 16 * hg + (lane & 15);  // this lane's head
+  uint32_t* ent = reinterpret_cast<uint32_t*>(lds + kSEntOff);
+  int* misc = reinterpret_cast<int*>(lds + kSMiscOff);
+  uint32_t* scan = reinterpret_cast<uint32_t*>(misc + 16);
+  f4* zx = reinterpret_cast<f4*>(lds + kSZOff);  // [wave][lane]
+
+  // the queries of the wave's 16 heads as B operands of S^T: lane l holds
+  // dims 32 ks + 8 (l / 16) .. + 7 of head h
+  bf8 qf[kD / 32];
+  {
+    const uint16_t* qrow = a.q + (static_cast<int64_t>(t) * a.H + h) * kD + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < kD / 32; ++ks) qf[ks] = __builtin_bit_cast(bf8, *reinterpret_cast<const i4*>(qrow + 32 * ks));
+  }
+
+  int b;
+  const int E = token_entries(a, t, ent, misc, scan, kStepE, &b);
+  const int N = (E + kStepE - 1) / kStepE;
+  const int st0 = static_cast<int>(static_cast<int64_t>(N) * s / a.S);
+  const int st1 = static_cast<int>(static_cast<int64_t>(N) * (s + 1) / a.S);
+  const int ns = st1 - st0;
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  constexpr int kOT = kD / 2 / 16;  // output tiles of a wave: 16
+  f4 o[kOT];
+#pragma unroll
+  for (int mt = 0; mt < kOT; ++mt) o[mt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // this wave's 4 rows of step k (entries 32 k + 4 wave .. + 3; lane: bytes
+  // 16 lane .. + 15 of each row)
+  auto load = [&](int k, i4 (&rr)[4]) {
+    const i4 e4 = *reinterpret_cast<const i4*>(ent + kStepE * k + 4 * wave);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t en = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(e4[i]));
+      const bool raw = (en >> 31) != 0;
+      const char* base = raw ? a.r_cache : a.c_cache;
+      const int64_t stride = raw ? a.r_stride : a.c_stride;
+      const char* row = base + static_cast<int64_t>((en >> 8) & 0x7FFFFFu) * stride + (en & 0xFFu) * (kD * 2);
+      rr[i] = *reinterpret_cast<const i4*>(row + 16 * lane);
+    }
+  };
+  // the rows into both copies of a step buffer (quad `wave` of the step)
+  auto stage = [&](char* kb, const i4 (&rr)[4]) {
+    const int ln = opaque_lane();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<i4*>(kb + krm_offset(4 * wave + i, ln)) = rr[i];
+    char* vt = kb + kStepE * kD * 2;
+    const int c = wave & 3, hq = wave >> 2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = 8 * ln + e, w = e >> 1;
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      i2 hv;
+      hv[0] = static_cast<int>(__builtin_amdgcn_perm(static_cast<uint32_t>(rr[1][w]), static_cast<uint32_t>(rr[0][w]), sel));
+      hv[1] = static_cast<int>(__builtin_amdgcn_perm(static_cast<uint32_t>(rr[3][w]), static_cast<uint32_t>(rr[2][w]), sel));
+      *reinterpret_cast<i2*>(vt + vts_slot(d, c) + 8 * (hq ^ ((d >> 6) & 1))) = hv;
+    }
+  };
+  // score step k from buffer kb (holds the logit exchange barrier)
+  auto score = [&](const char* kb, int k) {
+    const int ln = opaque_lane();
+    f4 sa = {0.0f, 0.0f, 0.0f, 0.0f}, sb = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < kD / 32; ks += 2) {
+      const int ch = 4 * ks + (ln >> 4);
+      const i4 kv0 = *reinterpret_cast<const i4*>(kb + krm_offset(16 * eta + (ln & 15), ch));
+      const i4 kv1 = *reinterpret_cast<const i4*>(kb + krm_offset(16 * eta + (ln & 15), ch + 4));
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, kv0), qf[ks], sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, kv1), qf[ks + 1], sb, 0, 0, 0);
+    }
+    const f4 sacc = sa + sb;
+    // sacc[i]: head h, entry 32 k + 16 eta + 4 (lane / 16) + i
+    f4 zo;
+    const int e0 = kStepE * k + 16 * eta + 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) zo[i] = e0 + i < E ? sacc[i] * a.zscale : -INFINITY;
+    zx[wave * 64 + lane] = zo;
+    __syncthreads();  // both halves' logits are in LDS
+    const f4 zp = zx[(wave ^ 4) * 64 + lane];
+    const f4 z0 = eta == 0 ? zo : zp, z1 = eta == 0 ? zp : zo;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, fmaxf(z0[i], z1[i]));
+    tmax = wave_max_heads(tmax);
+    // the reference maximum moves only when a head's logits pass it by more
+    // than 8 (weights stay below 2^8); both waves of a head group see the
+    // same logits and move it together
+    const float m_cand = fmaxf(m_run, tmax);
+    if (__ballot(m_cand > m_run + 8.0f) != 0) {
+      const float alpha = m_cand == -INFINITY ? 1.0f : exp2f(m_run - m_cand);
+#pragma unroll
+      for (int mt = 0; mt < kOT; ++mt) o[mt] *= alpha;
+      l_run *= alpha;
+      m_run = m_cand;
+    }
+    uint32_t p0[4], p1[4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p0[i] = bf16_rne(z0[i] == -INFINITY ? 0.0f : exp2f(z0[i] - m_run));
+      p1[i] = bf16_rne(z1[i] == -INFINITY ? 0.0f : exp2f(z1[i] - m_run));
+      psum += __uint_as_float(p0[i] << 16) + __uint_as_float(p1[i] << 16);
+    }
+    l_run += psum;
+    const i4 pa = {static_cast<int>(p0[0] | (p0[1] << 16)), static_cast<int>(p0[2] | (p0[3] << 16)),
+                   static_cast<int>(p1[0] | (p1[1] << 16)), static_cast<int>(p1[2] | (p1[3] << 16))};
+    const i4 pb = {pa[2], pa[3], pa[0], pa[1]};
+    const bf8 PA = __builtin_bit_cast(bf8, pa), PB = __builtin_bit_cast(bf8, pb);
+    const char* vt = kb + kStepE * kD * 2;
+#pragma unroll
+    for (int mg = 0; mg < kOT; mg += 8) {  // eight output tiles per group
+      i4 vv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int d = (kD / 2) * eta + 16 * (mg + j) + (ln & 15);
+        vv[j] = *reinterpret_cast<const i4*>(vt + vts_slot(d, ln >> 4));
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        // bit 6 of the tile's dims says which quad the slot holds first
+        const int mt = mg + j;
+        o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, vv[j]), ((mt >> 2) & 1) ? PB : PA,
+                                                        o[mt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  if (ns > 0) {
+    // a ring of two register sets: the rows of step j + 2 are in flight
+    // while step j is scored; loads past the split's last step read that
+    // step again, so every load is unconditional
+    char* const buf0 = lds;
+    char* const buf1 = lds + kSplitBuf;
+    i4 r0[4], r1[4];
+    load(st0, r0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(min(st0 + 1, st1 - 1), r1);
+    __builtin_amdgcn_sched_barrier(0);
+    stage(buf0, r0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(min(st0 + 2, st1 - 1), r0);
+    __builtin_amdgcn_sched_barrier(0);
+    auto body = [&](int j, const char* cur, char* nxt, i4 (&rr)[4]) {
+      const bool live = j < ns;  // workgroup-uniform
+      if (live) __syncthreads();  // step j is staged; the logit buffer is free
+      if (live) score(cur, st0 + j);
+      if (j + 1 < ns) stage(nxt, rr);
+      __builtin_amdgcn_sched_barrier(0);
+      load(min(st0 + j + 3, st1 - 1), rr);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int j = 0; j < ns; j += 2) {
+      body(j, buf0, buf1, r1);
+      body(j + 1, buf1, buf0, r0);
+    }
+  }
+  l_run = wave_sum_heads(l_run);
+
+  if (a.S > 1) {
+    // this split's state for the merge launch: o relative to m_run, m_run, l_run
+    const int64_t unit = static_cast<int64_t>(t) * a.HB + hb;
+    const int hl = 16 * hg + (lane & 15);  // head within the block
+    float* wo = a.wo + ((unit * a.S + s) * 64 + hl) * kD;
+#pragma unroll
+    for (int mt = 0; mt < kOT; ++mt)
+      *reinterpret_cast<f4*>(wo + (kD / 2) * eta + 16 * mt + 4 * (lane >> 4)) = o[mt];
+    if (eta == 0 && lane < 16) {
+      float* wml = a.wml + ((unit * a.S + s) * 64 + hl) * 2;
+      wml[0] = m_run;
+      wml[1] = b >= 0 ? l_run : -1.0f;  // -1: the token is outside every request
+    }
+    return;
+  }
+
+  // 3. outputs: lane l holds dims 256 eta + 16 mt + 4 (l / 16) .. + 3 of head h
+  const bool has_sink = a.sinks != nullptr && b >= 0;  // a token outside every request: 0, -inf
+  const float sk = has_sink ? a.sinks[h] * kLog2e : -INFINITY;
+  const float M = fmaxf(m_run, sk);
+  const float c = m_run == -INFINITY ? 0.0f : exp2f(m_run - M);
+  const float den = c * l_run + (has_sink ? exp2f(sk - M) : 0.0f);
+  const float f = den > 0.0f ? c / den : 0.0f;
+  uint16_t* orow = a.out + (static_cast<int64_t>(t) * a.H + h) * kD + (kD / 2) * eta + 4 * (lane >> 4);
+#pragma unroll
+  for (int mt = 0; mt < kOT; ++mt) {
+    const i2 pk = {static_cast<int>(bf16_rne(o[mt][0] * f) | (bf16_rne(o[mt][1] * f) << 16)),
+                   static_cast<int>(bf16_rne(o[mt][2] * f) | (bf16_rne(o[mt][3] * f) << 16))};
+    *reinterpret_cast<i2*>(orow + 16 * mt) = pk;
+  }
+  if (a.lse && eta == 0 && lane < 16)
+    a.lse[static_cast<int64_t>(t) * a.H + h] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
+}
+
+
+// The merge of a token's split states: workgroup i takes (token, head
+// block) i / 16 and its heads 4 (i % 16) .. + 3; thread: head tid / 128 of
+// those, dims 4 (tid % 128) .. + 3.
+__global__ __launch_bounds__(kAttnThreads) void sparse_attn_merge_kernel(AttnArgs a) {
+  const int unit = blockIdx.x >> 4;  // t * HB + hb
+  const int t = unit / a.HB, hb = unit % a.HB;
+  const int tid = threadIdx.x;
+  const int hl = 4 * (blockIdx.x & 15) + tid / 128;  // head within the block
+  const int h = 64 * hb + hl;
+  const int d = 4 * (tid % 128);
+  const float* wml = a.wml + (static_cast<int64_t>(unit) * a.S * 64 + hl) * 2;
+  const float* wo = a.wo + (static_cast<int64_t>(unit) * a.S * 64 + hl) * kD + d;
+  float ms[kMaxSplits], ls[kMaxSplits];
+  f4 v[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < a.S) {
+      ms[s] = wml[s * 128];
+      ls[s] = wml[s * 128 + 1];
+      v[s] = *reinterpret_cast<const f4*>(wo + static_cast<int64_t>(s) * 64 * kD);
+    }
+  }
+  // a token outside every request (normalizer -1) has no sink term: out 0,
+  // lse -inf (its states hold no entry: maximum -inf, weight 0)
+  const bool has_sink = a.sinks != nullptr && ls[0] >= 0.0f;
+  const float sk = has_sink ? a.sinks[h] * kLog2e : -INFINITY;
+  float M = sk;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < a.S) M = fmaxf(M, ms[s]);
+  f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float den = has_sink ? exp2f(sk - M) : 0.0f;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < a.S) {
+      const float c = ms[s] == -INFINITY ? 0.0f : exp2f(ms[s] - M);
+      den += c * ls[s];
+      acc += v[s] * c;
+    }
+  }
+  const float f = den > 0.0f ? 1.0f / den : 0.0f;
+  const i2 pk = {static_cast<int>(bf16_rne(acc[0] * f) | (bf16_rne(acc[1] * f) << 16)),
+                 static_cast<int>(bf16_rne(acc[2] * f) | (bf16_rne(acc[3] * f) << 16))};
+  *reinterpret_cast<i2*>(a.out + (static_cast<int64_t>(t) * a.H + h) * kD + d) = pk;
+  if (a.lse && d == 0) a.lse[static_cast<int64_t>(t) * a.H + h] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
+}
+
 }  // namespace
+
+int attention_splits(int64_t tokens, int heads, int topk, int window) {
+  if (heads % 64 != 0) return 0;
+  const int64_t units = tokens * (heads / 64);
+  if (units >= 256) return 1;
+  int64_t S = std::min<int64_t>(kMaxSplits, (256 + units - 1) / std::max<int64_t>(units, 1));
+  const int64_t steps = (static_cast<int64_t>(topk) + window + kStepE - 1) / kStepE;
+  S = std::min(S, std::max<int64_t>(steps, 1));
+  return static_cast<int>(std::max<int64_t>(S, 1));
+}
+
+int64_t attention_workspace_bytes(int64_t tokens, int heads, int /*topk*/, int /*window*/, int splits) {
+  if (splits <= 1 || heads % 64 != 0) return 0;
+  const int64_t units = tokens * (heads / 64);
+  return units * splits * 64 * 2 * 4 + units * splits * 64 * kD * 4;
+}
 
 int launch_attention(const qli_attn_params* p, void* stream) {
   if (p->num_tokens == 0) return QLI_OK;
@@ -479,10 +814,31 @@ int launch_attention(const qli_attn_params* p, void* stream) {
   a.status = p->status_out;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t tpad = (static_cast<int64_t>(a.T) + 7) / 8 * 8;
-  const int64_t grid = tpad * a.G;
-  {
+  int S = attention_splits(a.T, a.H, a.topk, a.window);
+  if (S == 0) {
+    const int64_t grid = tpad * a.G;
     Stamp s(QLI_KERNEL_ATTN, st);
     hipLaunchKernelGGL(sparse_attn_kernel, dim3(static_cast<unsigned>(grid)), dim3(kAttnThreads), 0, st, a);
+  } else {
+    // as many splits as the workspace holds
+    const int64_t ws = p->workspace ? p->workspace_bytes : 0;
+    while (S > 1 && attention_workspace_bytes(a.T, a.H, a.topk, a.window, S) > ws) --S;
+    a.S = S;
+    a.HB = a.H / 64;
+    const int64_t units = static_cast<int64_t>(a.T) * a.HB;
+    if (S > 1) {
+      a.wml = static_cast<float*>(p->workspace);
+      a.wo = a.wml + units * S * 64 * 2;
+    }
+    const int64_t grid = tpad * a.HB * S;
+    {
+      Stamp s(QLI_KERNEL_ATTN_SPLIT, st);
+      hipLaunchKernelGGL(sparse_attn_split_kernel, dim3(static_cast<unsigned>(grid)), dim3(kAttnThreads), 0, st, a);
+    }
+    if (S > 1) {
+      Stamp s(QLI_KERNEL_ATTN_MERGE, st);
+      hipLaunchKernelGGL(sparse_attn_merge_kernel, dim3(static_cast<unsigned>(units * 16)), dim3(kAttnThreads), 0, st, a);
+    }
   }
   return hipGetLastError() == hipSuccess ? QLI_OK : QLI_ERR_HIP;
 }

@@ -150,5 +150,10 @@ int xcd_count();
 int launch_quantize(const qli_quant_params* p, void* stream);
 int launch_write_k(const qli_kwrite_params* p, void* stream);
 int launch_attention(const qli_attn_params* p, void* stream);
+// Workgroups over which a token's entries are split when heads are a
+// multiple of 64 (0: the head-group kernel runs; 1: no split).
+int attention_splits(int64_t tokens, int heads, int topk, int window);
+// Workspace bytes of a call with `splits` splits (0 for splits <= 1).
+int64_t attention_workspace_bytes(int64_t tokens, int heads, int topk, int window, int splits);
 
 }  // namespace qli

@@ -53,7 +53,7 @@ def test_probes_live_in_their_own_library(lib):
 
 
 def test_abi_version(lib):
-    assert Q.qli_abi_version() == Q.QLI_ABI_VERSION == 5
+    assert Q.qli_abi_version() == Q.QLI_ABI_VERSION == 6
 
 
 @pytest.mark.parametrize("struct", ["qli_params", "qli_quant_params", "qli_kwrite_params", "qli_attn_params"])
@@ -418,3 +418,34 @@ def _attn_params(**kw):
 ])
 def test_attention_host_validation(lib, kw, code):
     assert lib.qli_sparse_attention(C.byref(_attn_params(**kw)), None) == code
+
+
+def _attn_pointers(p):
+    # stand-in device addresses (never dereferenced: every case below is
+    # rejected on the host before any launch)
+    for i, f in enumerate(("q", "c_cache", "c_block_table", "c_lens", "query_start_loc", "indices", "out")):
+        setattr(p, f, 0x10000000 + 0x100000 * i)
+    return p
+
+
+@pytest.mark.parametrize("kw", [{"workspace_bytes": -1}, {"workspace": 0x20000000 + 16, "workspace_bytes": 1 << 20},
+                                {"out": 0x30000000 + 8}])
+def test_attention_workspace_validation(lib, kw):
+    p = _attn_pointers(_attn_params(num_tokens=1))
+    for k, v in kw.items():
+        setattr(p, k, v)
+    assert lib.qli_sparse_attention(C.byref(p), None) == 1
+
+
+@pytest.mark.parametrize("T,H,topk,window,nbytes", [
+    (64, 64, 2048, 128, 64 * 4 * 64 * 8 + 64 * 4 * 64 * 2048),  # four splits per token
+    (100, 128, 2048, 0, 200 * 2 * 64 * 8 + 200 * 2 * 64 * 2048),  # 200 (token, 64 heads): two
+    (64, 32, 2048, 128, 0),      # heads not a multiple of 64: the head-group kernel, no split
+    (256, 64, 2048, 128, 0),     # the tokens fill the GPU without a split
+    (1, 64, 16, 8, 0),           # one 32-entry step: nothing to split
+    (1, 64, 40, 0, 2 * 64 * 8 + 2 * 64 * 2048),  # two steps: two splits
+])
+def test_attention_workspace_bytes(lib, T, H, topk, window, nbytes):
+    p = _attn_params(num_tokens=T, num_heads=H, topk=topk, window=window)
+    assert lib.qli_attn_workspace_bytes(C.byref(p)) == nbytes
+    assert lib.qli_attn_workspace_bytes(None) == 0

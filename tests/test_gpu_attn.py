@@ -1,6 +1,9 @@
 """GPU parity of the sparse-attention consumer of the indexer's positions
 (qli_sparse_attention) against the oracle (qli_attn_oracle.c), through the
-C ABI.
+C ABI.  Heads in multiples of 64 run the split kernel (a token's entries
+over up to four workgroups whose states a merge launch combines from the
+workspace, or one workgroup per token without a workspace); other head
+counts run the head-group kernel.
 
 Tolerance, from the kernel's arithmetic: the logits are exact products
 summed in FP32 (relative error far below 1e-5 of the logit range); the
@@ -26,7 +29,7 @@ pytestmark = pytest.mark.gpu
 QLI_DEV_BAD_PAGE, QLI_DEV_BAD_LENGTH, QLI_DEV_BAD_METADATA, QLI_DEV_BAD_INDEX = 1, 2, 4, 8
 
 
-def run_attn(ap, indices=None, lse=True, status=False):
+def run_attn(ap, indices=None, lse=True, status=False, workspace="auto"):
     import torch
 
     import quantized_top_indexer_amd as Q
@@ -50,7 +53,7 @@ def run_attn(ap, indices=None, lse=True, status=False):
         window=ap.window, sinks=None if ap.sinks is None else dev(ap.sinks, np.float32), scale=ap.scale,
         c_page_rows=ap.c_page_rows, c_page_stride=ap.c_page_stride, c_num_pages=ap.c_pages.shape[0],
         r_page_rows=ap.r_page_rows, r_page_stride=ap.r_page_stride, r_num_pages=ap.r_pages.shape[0],
-        lse=lse_t, status_out=st)
+        lse=lse_t, status_out=st, workspace=workspace)
     torch.cuda.synchronize()
     o = bf16_to_f32(out.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
     return o, (lse_t.cpu().numpy() if lse else None), (int(st.item()) if status else None)
@@ -75,11 +78,11 @@ def value_bound(ap, t, idx):
     return max(vals) if vals else 0.0
 
 
-def check(ap, indices=None, tokens=None):
+def check(ap, indices=None, tokens=None, workspace="auto"):
     idx = ap.indices if indices is None else indices
     say(f"attn {ap.name}: T={ap.num_tokens} H={ap.num_heads} topk={idx.shape[1]} window={ap.window} "
-        f"sinks={ap.sinks is not None}")
-    o, lse, _ = run_attn(ap, indices=idx)
+        f"sinks={ap.sinks is not None} workspace={'auto' if isinstance(workspace, str) else workspace is not None}")
+    o, lse, _ = run_attn(ap, indices=idx, workspace=workspace)
     tok = np.arange(ap.num_tokens) if tokens is None else np.asarray(tokens)
     ref, rlse = oracle.sparse_attn(ap, tokens=tok, indices=idx)
     worst = 0.0
@@ -159,3 +162,46 @@ def test_out_of_contract_entries_flagged_and_skipped():
     ap3 = dataclasses.replace(ap, c_bt=bt)
     _, _, st3 = run_attn(ap3, indices=keep, status=True)
     assert st3 & QLI_DEV_BAD_PAGE
+
+
+def test_head_group_kernel_32_and_48_heads():
+    # heads not a multiple of 64: the head-group kernel
+    check(A.build_attn_problem("heads32", 25, [3, 2], [200, 90], [400, 180], 2, 32, 64, 24, pad_frac=0.3))
+    check(A.build_attn_problem("heads48", 26, [2, 1], [300, 50], [600, 100], 1, 48, 96, 40))
+
+
+def test_split_kernel_without_workspace():
+    # one workgroup per (token, 64 heads): no partial states
+    check(A.attn_small(), workspace=None)
+    ap = A.build_attn_problem("ragged_nows", 27, [7], [400], [800], 2, 128, 40, 8, pad_frac=0.5)
+    check(ap, workspace=None)
+
+
+def test_split_kernel_many_tokens():
+    # 260 tokens x 64 heads fill the GPU without splitting; a ragged last
+    # group of 8 tokens
+    ap = A.build_attn_problem("many", 28, [100, 1, 159], [500, 20, 300], [1000, 40, 600], 2, 64, 32, 16,
+                              pad_frac=0.2)
+    check(ap)
+
+
+def test_split_workspace_reused_without_initialisation():
+    # three calls in a row on one workspace filled with garbage first (the
+    # last call smaller, with fewer splits): each equals the oracle
+    import ctypes
+
+    import torch
+
+    import quantized_top_indexer_amd as Q
+    calls = [A.attn_small(),
+             A.build_attn_problem("ws2", 29, [5, 4], [900, 700], [1800, 1400], 1, 128, 256, 64),
+             A.build_attn_problem("ws3", 30, [2], [60], [120], 2, 64, 40, 8)]
+    need = []
+    for ap in calls:
+        p = Q.qli_attn_params()
+        p.num_tokens, p.num_heads, p.topk, p.window = ap.num_tokens, ap.num_heads, ap.indices.shape[1], ap.window
+        need.append(Q.load_library().qli_attn_workspace_bytes(ctypes.byref(p)))
+    assert min(need) > 0
+    ws = torch.full((max(need),), 0xFF, dtype=torch.uint8, device="cuda")  # NaN bit patterns
+    for ap in calls:
+        check(ap, workspace=ws)
