@@ -105,29 +105,6 @@ __device__ __forceinline__ float wave_sum_heads(float x) {
   return x + __shfl_xor(x, 32);
 }
 
-// Exclusive prefix sum over the workgroup's threads (sh: one word per wave).
-__device__ uint32_t block_exclusive_scan_attn(uint32_t v, uint32_t* total, uint32_t* sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = static_cast<uint32_t>(__shfl_up(static_cast<int>(inc), o));
-    if (lane >= o) inc += y;
-  }
-  if (lane == 63) sh[wave] = inc;
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kAttnThreads / 64; ++w) {
-    const uint32_t x = sh[w];
-    before += w < wave ? x : 0u;
-    tot += x;
-  }
-  *total = tot;
-  __syncthreads();
-  return before + inc - v;
-}
-
 // Transposed tile layout: dim d holds the 16 rows' values (32 B) at slot(d);
 // the swizzle spreads the rows written by one store instruction (dims 8
 // apart) and read by one MFMA operand load (16 consecutive dims) over the
@@ -155,10 +132,15 @@ __device__ __forceinline__ int krm_offset(int i, int ch) { return i * (kD * 2) +
 // in order into ent (index positions first, then the window), padded with
 // copies of the last entry to a multiple of `pad`; returns their count and
 // the token's request in *b_out (-1: outside every request).  Called by all
-// kAttnThreads threads of the workgroup.
+// kAttnThreads threads of the workgroup.  Virtual entry v (index slot v,
+// then window position v - topk) belongs to thread v % kAttnThreads, round
+// v / kAttnThreads: each round's index values are loaded together, then
+// their block-table entries together, and the rounds are compacted in order
+// with wave ballots (scan: 8 words per round).
+constexpr int kRounds = (kMaxEntries + kAttnThreads - 1) / kAttnThreads;
 __device__ int token_entries(const AttnArgs& a, int t, uint32_t* ent, int* misc, uint32_t* scan, int pad,
                              int* b_out) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) misc[0] = -1;
   __syncthreads();
   for (int i = tid; i < a.B; i += kAttnThreads)
@@ -182,44 +164,64 @@ __device__ int token_entries(const AttnArgs& a, int t, uint32_t* ent, int* misc,
     if (a.window > 0 && rlen < q1 - q0 && tid == 0) flag(a, QLI_DEV_BAD_METADATA);
     const int64_t s0 = max<int64_t>(0, p - a.window + 1);
     const int nwin = a.window > 0 && p >= 0 ? static_cast<int>(p - s0 + 1) : 0;
-    // virtual entries: topk index slots, then the window; each thread a run of them
     const int nv = a.topk + nwin;
-    const int per = (nv + kAttnThreads - 1) / kAttnThreads;
-    const int v0 = min(nv, tid * per), v1 = min(nv, v0 + per);
+    const int32_t* crow = a.c_bt + static_cast<int64_t>(b) * a.c_bts;
+    const int32_t* rrow = a.window > 0 ? a.r_bt + static_cast<int64_t>(b) * a.r_bts : crow;
+    // index values (slots past the row read its last slot, unused)
+    int c[kRounds];
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+      const int v = tid + kAttnThreads * i;
+      c[i] = a.topk > 0 ? a.idx[static_cast<int64_t>(t) * a.topk + min(v, a.topk - 1)] : -1;
+    }
+    // block-table entries (entries without one read the row's first)
+    int pg[kRounds];
+    bool raw[kRounds];
+    int row[kRounds];
     uint32_t bad = 0;
-    auto resolve = [&](int v) -> uint32_t {
-      if (v < a.topk) {
-        const int c = a.idx[static_cast<int64_t>(t) * a.topk + v];
-        if (c < 0) return kNoEntry;
-        if (c >= clen) {
-          bad |= QLI_DEV_BAD_INDEX;
-          return kNoEntry;
-        }
-        const int pg = a.c_bt[static_cast<int64_t>(b) * a.c_bts + c / a.c_rows];
-        if (pg < 0 || pg >= a.c_pages) {
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+      const int v = tid + kAttnThreads * i;
+      raw[i] = v >= a.topk;
+      int pos;
+      if (!raw[i]) {
+        if (c[i] >= clen) bad |= QLI_DEV_BAD_INDEX;
+        pos = c[i] >= 0 && c[i] < clen ? c[i] : -1;
+      } else {
+        pos = v < nv ? static_cast<int>(s0) + (v - a.topk) : -1;
+      }
+      const int rows = raw[i] ? a.r_rows : a.c_rows;
+      row[i] = pos >= 0 ? pos % rows : -1;
+      pg[i] = (raw[i] ? rrow : crow)[pos >= 0 ? pos / rows : 0];
+    }
+    // compaction, round by round in order
+    uint32_t base = 0;
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+      uint32_t en = kNoEntry;
+      if (row[i] >= 0) {
+        if (pg[i] < 0 || pg[i] >= (raw[i] ? a.r_pages : a.c_pages)) {
           bad |= QLI_DEV_BAD_PAGE;
-          return kNoEntry;
+        } else {
+          en = (raw[i] ? 0x80000000u : 0u) | (static_cast<uint32_t>(pg[i]) << 8) | static_cast<uint32_t>(row[i]);
         }
-        return (static_cast<uint32_t>(pg) << 8) | static_cast<uint32_t>(c % a.c_rows);
       }
-      const int s = static_cast<int>(s0) + (v - a.topk);
-      const int pg = a.r_bt[static_cast<int64_t>(b) * a.r_bts + s / a.r_rows];
-      if (pg < 0 || pg >= a.r_pages) {
-        bad |= QLI_DEV_BAD_PAGE;
-        return kNoEntry;
+      const uint64_t m = __ballot(en != kNoEntry);
+      const uint32_t within = static_cast<uint32_t>(__popcll(m & ((1ull << lane) - 1ull)));
+      if (lane == 0) scan[8 * i + wave] = static_cast<uint32_t>(__popcll(m));
+      __syncthreads();
+      uint32_t before = base, tot = 0;
+#pragma unroll
+      for (int w = 0; w < kAttnThreads / 64; ++w) {
+        const uint32_t x = scan[8 * i + w];
+        before += w < wave ? x : 0u;
+        tot += x;
       }
-      return 0x80000000u | (static_cast<uint32_t>(pg) << 8) | static_cast<uint32_t>(s % a.r_rows);
-    };
-    uint32_t cnt = 0;
-    for (int v = v0; v < v1; ++v) cnt += resolve(v) != kNoEntry ? 1u : 0u;
-    uint32_t total;
-    uint32_t at = block_exclusive_scan_attn(cnt, &total, scan);
-    for (int v = v0; v < v1; ++v) {
-      const uint32_t en = resolve(v);
-      if (en != kNoEntry) ent[at++] = en;
+      if (en != kNoEntry) ent[before + within] = en;
+      base += tot;
     }
     if (bad) flag(a, bad);
-    E = static_cast<int>(total);
+    E = static_cast<int>(base);
   }
   __syncthreads();
   // the last tile is padded with copies of the last entry (scored as absent),
