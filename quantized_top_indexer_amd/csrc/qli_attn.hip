@@ -58,6 +58,8 @@ typedef short s4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef int i4 __attribute__((ext_vector_type(4)));
 typedef int i2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
 struct AttnArgs {
   int H, B, T, topk, window;
@@ -510,6 +512,11 @@ __device__ __forceinline__ int vts_slot(int d, int c) {
   return ((((d >> 3) << 2) + c) << 7) + (((d ^ (d >> 3) ^ c) & 7) << 4);
 }
 
+// Row-major step layout: chunk ch (16 B) of row i at chunk ch ^ (i % 8).  A
+// key operand load (rows 16 eta + l % 16, chunks 8 k + 4 h + l / 16) is then
+// a per-lane base for h plus 128 k bytes, an immediate offset.
+__device__ __forceinline__ int krs_offset(int i, int ch) { return i * (kD * 2) + ((ch ^ (i & 7)) << 4); }
+
 __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_split_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kSLdsBytes];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -569,28 +576,41 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_split_kernel(Attn
   auto stage = [&](char* kb, const i4 (&rr)[4]) {
     const int ln = opaque_lane();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<i4*>(kb + krm_offset(4 * wave + i, ln)) = rr[i];
-    char* vt = kb + kStepE * kD * 2;
-    const int c = wave & 3, hq = wave >> 2;
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<i4*>(kb + krs_offset(4 * wave + i, ln)) = rr[i];
+    // dims 8 ln + e: slot base 512 ln + 128 c, position (ln ^ c ^ e) % 8
+    char* vt = kb + kStepE * kD * 2 + 512 * ln + 128 * (wave & 3) + 8 * ((wave >> 2) ^ ((ln >> 3) & 1));
+    const int ls = (ln ^ wave) & 3 | (ln & 4);  // (ln ^ c) % 8
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int d = 8 * ln + e, w = e >> 1;
+      const int w = e >> 1;
       const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
       i2 hv;
       hv[0] = static_cast<int>(__builtin_amdgcn_perm(static_cast<uint32_t>(rr[1][w]), static_cast<uint32_t>(rr[0][w]), sel));
       hv[1] = static_cast<int>(__builtin_amdgcn_perm(static_cast<uint32_t>(rr[3][w]), static_cast<uint32_t>(rr[2][w]), sel));
-      *reinterpret_cast<i2*>(vt + vts_slot(d, c) + 8 * (hq ^ ((d >> 6) & 1))) = hv;
+      *reinterpret_cast<i2*>(vt + ((ls ^ e) << 4)) = hv;
     }
   };
+  // per-lane bases of the operand loads (the rest of each address is an
+  // immediate): keys, chunk groups h = 0, 1; values, tiles with mt % 4 = k
+  int kbase[2], vbase[4];
+  {
+    const int i = 16 * eta + (lane & 15), g = lane >> 4, j = lane & 15;
+    kbase[0] = i * (kD * 2) + (((0 + g) ^ (i & 7)) << 4);
+    kbase[1] = i * (kD * 2) + (((4 + g) ^ (i & 7)) << 4);
+    const int lv = (j & 7) ^ (j >> 3) ^ g;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      vbase[k] = kStepE * kD * 2 + 16384 * eta + 512 * (j >> 3) + 128 * g + ((lv ^ (2 * k)) << 4);
+  }
   // score step k from buffer kb (holds the logit exchange barrier)
   auto score = [&](const char* kb, int k) {
-    const int ln = opaque_lane();
     f4 sa = {0.0f, 0.0f, 0.0f, 0.0f}, sb = {0.0f, 0.0f, 0.0f, 0.0f};
+    const char* k0 = kb + kbase[0];
+    const char* k1 = kb + kbase[1];
 #pragma unroll
     for (int ks = 0; ks < kD / 32; ks += 2) {
-      const int ch = 4 * ks + (ln >> 4);
-      const i4 kv0 = *reinterpret_cast<const i4*>(kb + krm_offset(16 * eta + (ln & 15), ch));
-      const i4 kv1 = *reinterpret_cast<const i4*>(kb + krm_offset(16 * eta + (ln & 15), ch + 4));
+      const i4 kv0 = *reinterpret_cast<const i4*>(k0 + 64 * ks);
+      const i4 kv1 = *reinterpret_cast<const i4*>(k1 + 64 * ks);
       sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, kv0), qf[ks], sa, 0, 0, 0);
       sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, kv1), qf[ks + 1], sb, 0, 0, 0);
     }
@@ -619,27 +639,35 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_split_kernel(Attn
       l_run *= alpha;
       m_run = m_cand;
     }
-    uint32_t p0[4], p1[4];
+    // m_run is finite here (every step holds a valid entry), so z = -inf
+    // gives weight 0 through the hardware exponential; weights below 2^-126
+    // of the maximum flush to 0
+    i4 pa;
     float psum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p0[i] = bf16_rne(z0[i] == -INFINITY ? 0.0f : exp2f(z0[i] - m_run));
-      p1[i] = bf16_rne(z1[i] == -INFINITY ? 0.0f : exp2f(z1[i] - m_run));
-      psum += __uint_as_float(p0[i] << 16) + __uint_as_float(p1[i] << 16);
+    for (int i = 0; i < 4; i += 2) {
+      const bf2 w0 = __builtin_convertvector(
+          (f2{__builtin_amdgcn_exp2f(z0[i] - m_run), __builtin_amdgcn_exp2f(z0[i + 1] - m_run)}), bf2);
+      const bf2 w1 = __builtin_convertvector(
+          (f2{__builtin_amdgcn_exp2f(z1[i] - m_run), __builtin_amdgcn_exp2f(z1[i + 1] - m_run)}), bf2);
+      const uint32_t u0 = __builtin_bit_cast(uint32_t, w0), u1 = __builtin_bit_cast(uint32_t, w1);
+      pa[i / 2] = static_cast<int>(u0);
+      pa[2 + i / 2] = static_cast<int>(u1);
+      psum += (__uint_as_float(u0 << 16) + __uint_as_float(u0 & 0xFFFF0000u)) +
+              (__uint_as_float(u1 << 16) + __uint_as_float(u1 & 0xFFFF0000u));
     }
     l_run += psum;
-    const i4 pa = {static_cast<int>(p0[0] | (p0[1] << 16)), static_cast<int>(p0[2] | (p0[3] << 16)),
-                   static_cast<int>(p1[0] | (p1[1] << 16)), static_cast<int>(p1[2] | (p1[3] << 16))};
     const i4 pb = {pa[2], pa[3], pa[0], pa[1]};
     const bf8 PA = __builtin_bit_cast(bf8, pa), PB = __builtin_bit_cast(bf8, pb);
-    const char* vt = kb + kStepE * kD * 2;
 #pragma unroll
     for (int mg = 0; mg < kOT; mg += 8) {  // eight output tiles per group
       i4 vv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int d = (kD / 2) * eta + 16 * (mg + j) + (ln & 15);
-        vv[j] = *reinterpret_cast<const i4*>(vt + vts_slot(d, ln >> 4));
+        // dims 256 eta + 16 mt + l % 16 (mt = mg + j): vts_slot written as
+        // a base per mt % 4 plus 1024 mt
+        const int mt = mg + j;
+        vv[j] = *reinterpret_cast<const i4*>(kb + vbase[mt & 3] + 1024 * mt);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
