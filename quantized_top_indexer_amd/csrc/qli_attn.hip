@@ -102,6 +102,22 @@ __device__ __forceinline__ float wave_max_heads(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));
   return fmaxf(x, __shfl_xor(x, 32));
 }
+// The same reductions with the lane swaps of gfx950 (VALU, no LDS round
+// trip): a swap of a register with itself across halves (rows) leaves each
+// lane its own value in one result and its partner's (lane ^ 32, lane ^ 16)
+// in the other.
+__device__ __forceinline__ float wave_max_heads_swap(float x) {
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+}
+__device__ __forceinline__ float wave_sum_heads_swap(float x) {
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+}
 __device__ __forceinline__ float wave_sum_heads(float x) {
   x += __shfl_xor(x, 16);
   return x + __shfl_xor(x, 32);
@@ -627,7 +643,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_split_kernel(Attn
     float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, fmaxf(z0[i], z1[i]));
-    tmax = wave_max_heads(tmax);
+    tmax = wave_max_heads_swap(tmax);
     // the reference maximum moves only when a head's logits pass it by more
     // than 8 (weights stay below 2^8); both waves of a head group see the
     // same logits and move it together
@@ -709,7 +725,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_split_kernel(Attn
       body(j + 1, buf1, buf0, r0);
     }
   }
-  l_run = wave_sum_heads(l_run);
+  l_run = wave_sum_heads_swap(l_run);
 
   if (a.S > 1) {
     // this split's state for the merge launch: o relative to m_run, m_run, l_run
