@@ -528,10 +528,11 @@ __device__ __forceinline__ int vts_slot(int d, int c) {
   return ((((d >> 3) << 2) + c) << 7) + (((d ^ (d >> 3) ^ c) & 7) << 4);
 }
 
-// Row-major step layout: chunk ch (16 B) of row i at chunk ch ^ (i % 8).  A
-// key operand load (rows 16 eta + l % 16, chunks 8 k + 4 h + l / 16) is then
-// a per-lane base for h plus 128 k bytes, an immediate offset.
-__device__ __forceinline__ int krs_offset(int i, int ch) { return i * (kD * 2) + ((ch ^ (i & 7)) << 4); }
+// Row-major step layout: chunk ch (16 B) of row i at chunk ch ^ (i % 16), so
+// the 16 rows of one key operand load fall on distinct banks.  That load
+// (rows 16 eta + l % 16, chunks 8 k + 4 h + l / 16) is a per-lane base for
+// h and the parity of k plus 128 k bytes, an immediate offset.
+__device__ __forceinline__ int krs_offset(int i, int ch) { return i * (kD * 2) + ((ch ^ (i & 15)) << 4); }
 
 __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_split_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kSLdsBytes];
@@ -608,11 +609,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_split_kernel(Attn
   };
   // per-lane bases of the operand loads (the rest of each address is an
   // immediate): keys, chunk groups h = 0, 1; values, tiles with mt % 4 = k
-  int kbase[2], vbase[4];
+  // (8 k + 4 h + g) ^ (i % 16) = 8 (k ^ b) + ((4 h + g) ^ (i % 8)) with
+  // b = bit 3 of i, and 8 (k ^ b) = 8 k + 8 b for even k, 8 k - 8 b for odd
+  int kbase[2][2], vbase[4];
   {
     const int i = 16 * eta + (lane & 15), g = lane >> 4, j = lane & 15;
-    kbase[0] = i * (kD * 2) + (((0 + g) ^ (i & 7)) << 4);
-    kbase[1] = i * (kD * 2) + (((4 + g) ^ (i & 7)) << 4);
+    const int bq = 128 * ((i >> 3) & 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int rest = i * (kD * 2) + (((4 * h + g) ^ (i & 7)) << 4);
+      kbase[0][h] = rest + bq;
+      kbase[1][h] = rest - bq;
+    }
     const int lv = (j & 7) ^ (j >> 3) ^ g;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -621,12 +629,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_split_kernel(Attn
   // score step k from buffer kb (holds the logit exchange barrier)
   auto score = [&](const char* kb, int k) {
     f4 sa = {0.0f, 0.0f, 0.0f, 0.0f}, sb = {0.0f, 0.0f, 0.0f, 0.0f};
-    const char* k0 = kb + kbase[0];
-    const char* k1 = kb + kbase[1];
 #pragma unroll
     for (int ks = 0; ks < kD / 32; ks += 2) {
-      const i4 kv0 = *reinterpret_cast<const i4*>(k0 + 64 * ks);
-      const i4 kv1 = *reinterpret_cast<const i4*>(k1 + 64 * ks);
+      const int par = (ks >> 1) & 1;  // parity of k = ks / 2
+      const i4 kv0 = *reinterpret_cast<const i4*>(kb + kbase[par][0] + 64 * ks);
+      const i4 kv1 = *reinterpret_cast<const i4*>(kb + kbase[par][1] + 64 * ks);
       sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, kv0), qf[ks], sa, 0, 0, 0);
       sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, kv1), qf[ks + 1], sb, 0, 0, 0);
     }
