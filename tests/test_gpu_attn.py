@@ -205,3 +205,30 @@ def test_split_workspace_reused_without_initialisation():
     ws = torch.full((max(need),), 0xFF, dtype=torch.uint8, device="cuda")  # NaN bit patterns
     for ap in calls:
         check(ap, workspace=ws)
+
+
+def test_maximum_entries_and_heads():
+    # topk 2048 and a 512-position window: 2560 entries per token, the most a
+    # workgroup's entry list holds; 128 heads (two head blocks); sampled tokens
+    B = 3
+    ap = A.build_attn_problem("max_entries", 31, [1, 2, 1], [4096, 3000, 2100], [9000, 600, 513], 1, 128,
+                              2048, 512)
+    assert ap.num_tokens == 4 and B == len(ap.c_lens)
+    check(ap, tokens=[0, 1, 2, 3])
+    # the same entries through the head-group kernel (48 heads)
+    ap48 = A.build_attn_problem("max_entries48", 33, [1, 2, 1], [4096, 3000, 2100], [9000, 600, 513], 1, 48,
+                                2048, 512)
+    check(ap48, tokens=[0, 2, 3])
+
+
+def test_three_splits():
+    # 100 tokens x 64 heads: three workgroups per token (72 entries: three
+    # 32-entry steps, one per split)
+    import ctypes
+
+    import quantized_top_indexer_amd as Q
+    ap = A.build_attn_problem("three_splits", 32, [60, 40], [500, 90], [1000, 180], 2, 64, 64, 8, pad_frac=0.2)
+    p = Q.qli_attn_params()
+    p.num_tokens, p.num_heads, p.topk, p.window = ap.num_tokens, ap.num_heads, 64, 8
+    assert Q.load_library().qli_attn_workspace_bytes(ctypes.byref(p)) == 100 * 3 * 64 * (2 + 512) * 4
+    check(ap)
