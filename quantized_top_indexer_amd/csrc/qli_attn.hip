@@ -152,13 +152,22 @@ __device__ __forceinline__ int krm_offset(int i, int ch) { return i * (kD * 2) +
 // the token's request in *b_out (-1: outside every request).  Called by all
 // kAttnThreads threads of the workgroup.  Virtual entry v (index slot v,
 // then window position v - topk) belongs to thread v % kAttnThreads, round
-// v / kAttnThreads: each round's index values are loaded together, then
-// their block-table entries together, and the rounds are compacted in order
-// with wave ballots (scan: 8 words per round).
+// v / kAttnThreads.  Three dependent global round trips: the token's index
+// values (with the request search); the request's lengths with the
+// block-table entries of the index values; the window's block-table entries.
+// The rounds are then compacted in order with wave ballots (scan: 8 words
+// per round).
 constexpr int kRounds = (kMaxEntries + kAttnThreads - 1) / kAttnThreads;
 __device__ int token_entries(const AttnArgs& a, int t, uint32_t* ent, int* misc, uint32_t* scan, int pad,
                              int* b_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // index values (slots past the row read its last slot, unused)
+  int c[kRounds];
+#pragma unroll
+  for (int i = 0; i < kRounds; ++i) {
+    const int v = tid + kAttnThreads * i;
+    c[i] = a.topk > 0 ? a.idx[static_cast<int64_t>(t) * a.topk + min(v, a.topk - 1)] : -1;
+  }
   if (tid == 0) misc[0] = -1;
   __syncthreads();
   for (int i = tid; i < a.B; i += kAttnThreads)
@@ -169,8 +178,14 @@ __device__ int token_entries(const AttnArgs& a, int t, uint32_t* ent, int* misc,
   int E = 0;
   if (b >= 0) {
     const int q0 = a.qsl[b], q1 = a.qsl[b + 1];
-    // lengths beyond what the request's block-table row can map are cut there
     const int64_t cmax = static_cast<int64_t>(a.c_bts) * a.c_rows, rmax = static_cast<int64_t>(a.r_bts) * a.r_rows;
+    const int32_t* crow = a.c_bt + static_cast<int64_t>(b) * a.c_bts;
+    // block-table entries of the index values that the table row maps (the
+    // length checks come after; other slots read the row's first entry)
+    int pgc[kRounds];
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) pgc[i] = crow[c[i] >= 0 && c[i] < cmax ? c[i] / a.c_rows : 0];
+    // lengths beyond what the request's block-table row can map are cut there
     int64_t clen = a.c_lens[b];
     int64_t rlen = a.window > 0 ? a.r_lens[b] : 0;
     if (clen < 0 || rlen < 0 || clen > cmax || rlen > rmax) {
@@ -183,34 +198,23 @@ __device__ int token_entries(const AttnArgs& a, int t, uint32_t* ent, int* misc,
     const int64_t s0 = max<int64_t>(0, p - a.window + 1);
     const int nwin = a.window > 0 && p >= 0 ? static_cast<int>(p - s0 + 1) : 0;
     const int nv = a.topk + nwin;
-    const int32_t* crow = a.c_bt + static_cast<int64_t>(b) * a.c_bts;
     const int32_t* rrow = a.window > 0 ? a.r_bt + static_cast<int64_t>(b) * a.r_bts : crow;
-    // index values (slots past the row read its last slot, unused)
-    int c[kRounds];
-#pragma unroll
-    for (int i = 0; i < kRounds; ++i) {
-      const int v = tid + kAttnThreads * i;
-      c[i] = a.topk > 0 ? a.idx[static_cast<int64_t>(t) * a.topk + min(v, a.topk - 1)] : -1;
-    }
-    // block-table entries (entries without one read the row's first)
-    int pg[kRounds];
+    int pg[kRounds], row[kRounds];
     bool raw[kRounds];
-    int row[kRounds];
     uint32_t bad = 0;
 #pragma unroll
     for (int i = 0; i < kRounds; ++i) {
       const int v = tid + kAttnThreads * i;
       raw[i] = v >= a.topk;
-      int pos;
       if (!raw[i]) {
         if (c[i] >= clen) bad |= QLI_DEV_BAD_INDEX;
-        pos = c[i] >= 0 && c[i] < clen ? c[i] : -1;
+        row[i] = c[i] >= 0 && c[i] < clen ? c[i] % a.c_rows : -1;
+        pg[i] = pgc[i];
       } else {
-        pos = v < nv ? static_cast<int>(s0) + (v - a.topk) : -1;
+        const int pos = v < nv ? static_cast<int>(s0) + (v - a.topk) : -1;
+        row[i] = pos >= 0 ? pos % a.r_rows : -1;
+        pg[i] = rrow[pos >= 0 ? pos / a.r_rows : 0];
       }
-      const int rows = raw[i] ? a.r_rows : a.c_rows;
-      row[i] = pos >= 0 ? pos % rows : -1;
-      pg[i] = (raw[i] ? rrow : crow)[pos >= 0 ? pos / rows : 0];
     }
     // compaction, round by round in order
     uint32_t base = 0;
