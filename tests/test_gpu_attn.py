@@ -232,3 +232,11 @@ def test_three_splits():
     p.num_tokens, p.num_heads, p.topk, p.window = ap.num_tokens, ap.num_heads, 64, 8
     assert Q.load_library().qli_attn_workspace_bytes(ctypes.byref(p)) == 100 * 3 * 64 * (2 + 512) * 4
     check(ap)
+
+
+def test_prefill_shape_without_split_sampled():
+    # 300 query tokens of one request (enough to fill the GPU without a
+    # split: one workgroup per token) with full 2048-position rows and a
+    # 128-position window; sampled tokens against the oracle
+    ap = A.build_attn_problem("prefill_like", 34, [300], [4096], [8192], 2, 64, 2048, 128)
+    check(ap, tokens=[0, 1, 149, 150, 298, 299])
