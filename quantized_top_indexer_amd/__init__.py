@@ -7,11 +7,12 @@ library is not built, importing the entry points raises.
 
 Entry points (same names as the C ABI): ``qli_score_topk``,
 ``qli_score_topk_noalloc``, ``qli_workspace_bytes``, ``qli_validate``, ``qli_status_string``,
-``qli_abi_version``, ``qli_quantize_query``, ``qli_write_index_k``; plus
-``score_topk``, ``quantize_query`` and ``write_index_k``, convenience
-wrappers that allocate the outputs (and the workspace) with torch and run
-one call on the current stream, and ``output_shapes`` (shapes of a call's
-outputs).
+``qli_abi_version``, ``qli_quantize_query``, ``qli_write_index_k``,
+``qli_sparse_attention`` (``qli_attn_workspace_bytes`` through the loaded
+library); plus ``score_topk``, ``quantize_query``, ``write_index_k`` and
+``sparse_attention``, convenience wrappers that allocate the outputs (and
+the workspace) with torch and run one call on the current stream, and
+``output_shapes`` (shapes of a call's outputs).
 """
 from __future__ import annotations
 
