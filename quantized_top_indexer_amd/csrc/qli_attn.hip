@@ -97,15 +97,10 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-__device__ __forceinline__ float wave_max_heads(float x) {
-  // lanes l, l ^ 16, l ^ 32, l ^ 48 hold one head
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
-}
-// The same reductions with the lane swaps of gfx950 (VALU, no LDS round
-// trip): a swap of a register with itself across halves (rows) leaves each
-// lane its own value in one result and its partner's (lane ^ 32, lane ^ 16)
-// in the other.
+// Maximum and sum over the lanes that hold one head (l, l ^ 16, l ^ 32,
+// l ^ 48) with the lane swaps of gfx950 (VALU, no LDS round trip): a swap of
+// a register with itself across halves (rows) leaves each lane its own value
+// in one result and its partner's (lane ^ 32, lane ^ 16) in the other.
 __device__ __forceinline__ float wave_max_heads_swap(float x) {
   const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
@@ -117,10 +112,6 @@ __device__ __forceinline__ float wave_sum_heads_swap(float x) {
   x = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
   const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
-}
-__device__ __forceinline__ float wave_sum_heads(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
 }
 
 // Transposed tile layout: dim d holds the 16 rows' values (32 B) at slot(d);
@@ -360,7 +351,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
       z[i] = 4 * (lane >> 4) + i < n ? sacc[i] * a.zscale : -INFINITY;
       tmax = fmaxf(tmax, z[i]);
     }
-    tmax = wave_max_heads(tmax);
+    tmax = wave_max_heads_swap(tmax);
     // The weights are taken against a reference maximum m_run that moves
     // only when a head's logits pass it by more than 8 (weights below 2^8,
     // exact as BF16 exponents and harmless in the FP32 sums): the output
@@ -374,17 +365,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
       l_run *= alpha;
       m_run = m_cand;
     }
-    uint32_t pb[4];
-    float psum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pw = z[i] == -INFINITY ? 0.0f : exp2f(z[i] - m_run);
-      pb[i] = bf16_rne(pw);
-      psum += __uint_as_float(pb[i] << 16);
-    }
-    l_run += psum;
-    const s4 pv = {static_cast<short>(pb[0]), static_cast<short>(pb[1]), static_cast<short>(pb[2]),
-                   static_cast<short>(pb[3])};
+    // m_run is finite here (every tile holds a valid entry): z = -inf gives
+    // weight 0 through the hardware exponential
+    const bf2 w01 = __builtin_convertvector(
+        (f2{__builtin_amdgcn_exp2f(z[0] - m_run), __builtin_amdgcn_exp2f(z[1] - m_run)}), bf2);
+    const bf2 w23 = __builtin_convertvector(
+        (f2{__builtin_amdgcn_exp2f(z[2] - m_run), __builtin_amdgcn_exp2f(z[3] - m_run)}), bf2);
+    const uint32_t u01 = __builtin_bit_cast(uint32_t, w01), u23 = __builtin_bit_cast(uint32_t, w23);
+    l_run += (__uint_as_float(u01 << 16) + __uint_as_float(u01 & 0xFFFF0000u)) +
+             (__uint_as_float(u23 << 16) + __uint_as_float(u23 & 0xFFFF0000u));
+    const s4 pv = __builtin_bit_cast(s4, i2{static_cast<int>(u01), static_cast<int>(u23)});
     const int r0 = 4 * (ln >> 4);
 #pragma unroll
     for (int mg = 0; mg < kOT; mg += 8) {  // eight output tiles per group
@@ -431,7 +421,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
   }
 
   // 3. the pairs' states meet in LDS (over the tile buffers)
-  l_run = wave_sum_heads(l_run);
+  l_run = wave_sum_heads_swap(l_run);
   __syncthreads();  // every wave is done with the tile buffers
   float* mo = reinterpret_cast<float*>(lds);  // [pair][head][D]
   float* ml = reinterpret_cast<float*>(lds + kMiscOff + 256);  // [pair][head]: m, then l
